@@ -1,0 +1,162 @@
+// api.hip -- the extern "C" entry points declared in include/moe.h.
+//
+// Host side only: argument validation (before anything is enqueued), the
+// workspace layout, and dispatch to the kernels of route.hip, permute.hip,
+// expert_ffn.hip and combine_stats.hip.
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_problem(const moe_problem *p) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (p->T < 0 || p->d <= 0 || p->n_shared < 0 || p->n_routed < 0 || p->top_k < 0 || p->inter <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (p->d % 64 != 0 || p->inter % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    if (p->n_routed == 0) {
+        if (p->top_k != 0) return MOE_ERR_INVALID_ARG;
+    } else if (p->top_k < 1 || p->top_k > p->n_routed) {
+        return MOE_ERR_INVALID_ARG;
+    }
+    if (p->n_routed > kPermuteMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)p->T * p->top_k > INT32_MAX || (int64_t)p->n_shared * p->inter > INT32_MAX / 64 ||
+        (int64_t)p->T * p->top_k * p->inter > (int64_t)1 << 40)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_ws(const moe_problem *p, const void *ws, size_t ws_bytes, WsLayout *L) {
+    *L = ws_layout(*p);
+    if (L->total > 0 && (!ws || ws_bytes < L->total)) return MOE_ERR_WORKSPACE;
+    if (ws && ((uintptr_t)ws & 255u) != 0) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+uint8_t *at(void *ws, size_t off) { return (uint8_t *)ws + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer, misaligned pointer or bad shape";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside the supported envelope";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch or runtime error";
+        default: return "unknown moe status";
+    }
+}
+
+const char *moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+int moe_workspace_size(const moe_problem *p, size_t *bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    const int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    *bytes = ws_layout(*p).total;
+    return MOE_OK;
+}
+
+int moe_route(const moe_problem *p, const void *x, const float *centroids, const float *bias,
+              int32_t *idx, float *gate, float *probs, int32_t *counts, float *prob_sum, void *ws,
+              size_t ws_bytes, void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (p->n_routed < 1) return MOE_ERR_INVALID_ARG;
+    if (p->n_routed > kRouteMaxExperts || p->top_k > kRouteMaxTopK) return MOE_ERR_UNSUPPORTED;
+    if (!centroids || !counts || !prob_sum) return MOE_ERR_INVALID_ARG;
+    if (p->T > 0 && (!x || !idx || !gate)) return MOE_ERR_INVALID_ARG;
+    if ((x && !aligned16(x)) || !aligned16(centroids)) return MOE_ERR_INVALID_ARG;
+    WsLayout L;
+    if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
+    return hip_status(launch_route(*p, x, centroids, bias, idx, gate, probs,
+                                   (int32_t *)at(ws, L.route_counts), (double *)at(ws, L.route_psum),
+                                   counts, prob_sum, (hipStream_t)stream));
+}
+
+int moe_permute(const moe_problem *p, const int32_t *idx, int32_t *offsets, int32_t *sorted_token,
+                int32_t *slot_of, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (!offsets) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)p->T * p->top_k > 0 && (!idx || !sorted_token || !slot_of)) return MOE_ERR_INVALID_ARG;
+    WsLayout L;
+    if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
+    return hip_status(launch_permute(*p, idx, offsets, sorted_token, slot_of, (int32_t *)at(ws, L.perm_hist),
+                                     (int32_t *)at(ws, L.perm_base), (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets, const int32_t *sorted_token,
+                   const void *w1_routed, const void *w3_routed, const void *w2_routed, const void *w1_shared,
+                   const void *w3_shared, const void *w2_shared, void *y_routed, float *y_shared, void *ws,
+                   size_t ws_bytes, void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    const bool routed = p->n_routed > 0 && (int64_t)p->T * p->top_k > 0;
+    const bool shared = p->n_shared > 0 && p->T > 0;
+    if (routed) {
+        if (!x || !offsets || !sorted_token || !w1_routed || !w3_routed || !w2_routed || !y_routed)
+            return MOE_ERR_INVALID_ARG;
+        if (!aligned16(w1_routed) || !aligned16(w3_routed) || !aligned16(w2_routed) || !aligned16(y_routed))
+            return MOE_ERR_INVALID_ARG;
+    }
+    if (shared) {
+        if (!x || !w1_shared || !w3_shared || !w2_shared || !y_shared) return MOE_ERR_INVALID_ARG;
+        if (!aligned16(w1_shared) || !aligned16(w3_shared) || !aligned16(w2_shared) || !aligned16(y_shared))
+            return MOE_ERR_INVALID_ARG;
+    }
+    if (x && !aligned16(x)) return MOE_ERR_INVALID_ARG;
+    WsLayout L;
+    if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
+    if (!routed && !shared) return MOE_OK;
+    FfnArgs a{};
+    a.x = x;
+    a.offsets = offsets;
+    a.sorted_token = sorted_token;
+    a.w1_r = w1_routed; a.w3_r = w3_routed; a.w2_r = w2_routed;
+    a.w1_s = w1_shared; a.w3_s = w3_shared; a.w2_s = w2_shared;
+    a.act_shared = at(ws, L.act_shared);
+    a.act_routed = at(ws, L.act_routed);
+    a.y_routed = y_routed;
+    a.y_shared = y_shared;
+    moe_problem q = *p;
+    if (!routed) q.n_routed = 0, q.top_k = 0;
+    if (!shared) q.n_shared = 0;
+    return hip_status(launch_expert_ffn(q, a, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_problem *p, const void *x, const void *y_routed, const float *y_shared,
+                const float *gate, const int32_t *slot_of, void *h, void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (p->T == 0) return MOE_OK;
+    if (!x || !h) return MOE_ERR_INVALID_ARG;
+    if (p->top_k > 0 && (!y_routed || !gate || !slot_of)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(h) || (y_routed && !aligned16(y_routed)) ||
+        (y_shared && !aligned16(y_shared)))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_combine(*p, x, y_routed, y_shared, gate, slot_of, h, (hipStream_t)stream));
+}
+
+int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *counts, const float *prob_sum,
+                      float *f, float *P, float *f_dev, float *P_dev, float *exp_bal, float *dev_bal,
+                      void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (p->n_routed < 1 || groups < 1 || p->n_routed % groups != 0) return MOE_ERR_INVALID_ARG;
+    if (!counts || !prob_sum || !f || !P || !f_dev || !P_dev || !exp_bal || !dev_bal) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_balance_stats(*p, groups, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, dev_bal,
+                                           (hipStream_t)stream));
+}
+
+}  // extern "C"

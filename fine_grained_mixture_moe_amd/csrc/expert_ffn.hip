@@ -1,0 +1,326 @@
+// expert_ffn.hip -- the expert FFNs of the DeepSeekMoE layer on gfx950 MFMA.
+//
+// "[ACL 2024] DeepSeekMoE: 混合专家语言模型中的极致专家特化", section "Two core
+// strategies": mN fine-grained experts whose intermediate width is 1/m of a
+// standard FFN, and K_s shared experts that every token uses.  Each expert is
+// a SwiGLU FFN (no biases): FFN(u) = W2 (SiLU(W1 u) * (W3 u)).
+//
+// Two grouped GEMM launches:
+//   up   : for every group, act = SiLU(X W1^T) * (X W3^T), the SwiGLU fused into
+//          the epilogue (W1 and W3 rows of the same unit sit in one tile);
+//   down : y = act W2^T, written per grouped row.
+// Groups: the K_s shared experts form ONE dense group of width K_s*w over all
+// T rows (their W1/W3 stacks [K_s, w, d] are already one [K_s*w, d] matrix;
+// W2 is read segment by segment), then one group per routed expert whose rows
+// are its tokens in grouped order (gathered through sorted_token in the up
+// GEMM, contiguous in the down GEMM).
+//
+// Tiles: 128 weight rows x 128 tokens x 128 bytes of K per step, 256 threads
+// (4 wave64, 2x2), each wave 64x64 = 2x2 MFMA 32x32 blocks.  The MFMA A
+// operand is the weight tile, B the token tile, so each lane owns one token
+// column and 4 consecutive output columns per register quad (8/16-byte
+// stores).  bf16 uses v_mfma_f32_32x32x16_bf16; fp32 uses 8 x
+// v_mfma_f32_32x32x2_f32 per 16-wide k step over the same LDS fragments.
+// Every workgroup derives its (group, row-tile, column-tile) from the
+// device-side offsets, so no host round trip sizes the grid: the grid is an
+// upper bound and surplus workgroups exit at once.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 128;        // tokens per tile
+constexpr int BN = 128;        // weight rows per tile
+constexpr int KB = 128;        // bytes of K per tile step (64 bf16 / 32 fp32)
+constexpr int PITCH = KB + 16; // padded LDS row pitch (bytes)
+constexpr int MAXG = 1 + kPermuteMaxExperts;
+
+template <typename DT> struct Elt;
+template <> struct Elt<uint16_t> { static constexpr int size = 2; };
+template <> struct Elt<float> { static constexpr int size = 4; };
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ void store4(uint16_t *dst, const float v[4]) {
+    uint2 q;
+    q.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    q.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *(uint2 *)dst = q;
+}
+__device__ __forceinline__ void store4(float *dst, const float v[4]) {
+    *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// One 16-wide k step of a 32x32 block: a = weight fragment, b = token fragment.
+__device__ __forceinline__ void mfma_k16(f32x16 &acc, const uint8_t *a, const uint8_t *b, uint16_t) {
+    const bf16x8 av = *(const bf16x8 *)a;
+    const bf16x8 bv = *(const bf16x8 *)b;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_k16(f32x16 &acc, const uint8_t *a, const uint8_t *b, float) {
+    const float4 a0 = *(const float4 *)a, a1 = *(const float4 *)(a + 16);
+    const float4 b0 = *(const float4 *)b, b1 = *(const float4 *)(b + 16);
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
+}
+
+struct GemmParams {
+    int T, d, Ks, Nr, w;
+    const int32_t *offsets;
+    const int32_t *sorted_token;
+    const uint8_t *x;            // up: [T, d]
+    const uint8_t *act_shared;   // down: [T, Ks*w]
+    const uint8_t *act_routed;   // down: [T*K', w]
+    const uint8_t *wa_r, *wb_r;  // up: W1_r, W3_r  | down: W2_r
+    const uint8_t *wa_s, *wb_s;  // up: W1_s, W3_s  | down: W2_s
+    uint8_t *out_shared;         // up: act_shared  | down: y_shared (fp32)
+    uint8_t *out_routed;         // up: act_routed  | down: y_routed
+};
+
+// UP: true for the gate/up projection with SwiGLU epilogue, false for the down projection.
+template <typename DT, bool UP>
+__global__ __launch_bounds__(256) void grouped_ffn_kernel(GemmParams P) {
+    constexpr int ES = Elt<DT>::size;
+    constexpr int KSTEP = 16 * ES;          // bytes of one 16-wide k step
+    __shared__ int s_pref[MAXG + 1];
+    __shared__ int s_src[BM];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[BN * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[BM * PITCH];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = (P.Ks > 0 ? 1 : 0) + P.Nr;
+    const int ntn_s = UP ? P.Ks * P.w / 64 : cdiv(P.d, BN);
+    const int ntn_r = UP ? P.w / 64 : cdiv(P.d, BN);
+
+    // ---- tile prefix over groups (wave 0), then locate this workgroup's tile ----
+    if (wave == 0) {
+        int carry = 0;
+        if (lane == 0) s_pref[0] = 0;
+        for (int g0 = 0; g0 < G; g0 += 64) {
+            const int g = g0 + lane;
+            int tiles = 0;
+            if (g < G) {
+                const bool sh = P.Ks > 0 && g == 0;
+                const int r = g - (P.Ks > 0 ? 1 : 0);
+                const int rows = sh ? P.T : P.offsets[r + 1] - P.offsets[r];
+                tiles = cdiv(rows, BM) * (sh ? ntn_s : ntn_r);
+            }
+            int incl = tiles;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += v;
+            }
+            if (g < G) s_pref[g + 1] = carry + incl;
+            carry += __shfl(incl, 63, 64);
+        }
+    }
+    __syncthreads();
+    const int bid = blockIdx.x;
+    if (bid >= s_pref[G]) return;
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= bid) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const bool shared = P.Ks > 0 && g == 0;
+    const int r = g - (P.Ks > 0 ? 1 : 0);
+    const int row_off = shared ? 0 : P.offsets[r];
+    const int rows = shared ? P.T : P.offsets[r + 1] - row_off;
+    const int mt = cdiv(rows, BM);
+    const int lt = bid - s_pref[g];
+    const int m_tile = lt % mt, n_tile = lt / mt;
+    const int m0 = m_tile * BM;
+
+    // K extent and operand geometry of this group
+    const int K = UP ? P.d : (shared ? P.Ks * P.w : P.w);
+    const size_t a_pitch = (size_t)K * ES;               // token-side row pitch (bytes)
+    const uint8_t *a_base;
+    if (UP) a_base = P.x;
+    else a_base = shared ? P.act_shared : P.act_routed;
+    if (tid < BM) {
+        const int row = m0 + tid;
+        int src = -1;
+        if (row < rows) {
+            if (UP) src = shared ? row : P.sorted_token[row_off + row];
+            else src = row_off + row;
+        }
+        s_src[tid] = src;
+    }
+    __syncthreads();
+
+    // weight-side rows handled by this thread's 4 load chunks
+    const uint8_t *wsrc[4];
+    bool wvalid[4];
+    int wrow[4];
+    const uint8_t *xsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i;
+        const int row = c >> 3, part = c & 7;
+        wrow[i] = row;
+        if (UP) {
+            const uint8_t *base = (row < 64) ? (shared ? P.wa_s : P.wa_r + (size_t)r * P.w * P.d * ES)
+                                             : (shared ? P.wb_s : P.wb_r + (size_t)r * P.w * P.d * ES);
+            const int wr = n_tile * 64 + (row & 63);
+            wsrc[i] = base + (size_t)wr * P.d * ES + part * 16;
+            wvalid[i] = true;
+        } else {
+            const int col = n_tile * BN + row;
+            wvalid[i] = col < P.d;
+            // W2 row `col` of expert r (routed) or of shared segment 0 (advanced per k tile)
+            const uint8_t *base = shared ? P.wa_s : P.wa_r + (size_t)r * P.d * P.w * ES;
+            wsrc[i] = base + (size_t)(wvalid[i] ? col : 0) * P.w * ES + part * 16;
+        }
+        const int src = s_src[row];
+        xsrc[i] = src >= 0 ? a_base + (size_t)src * a_pitch + part * 16 : nullptr;
+    }
+
+    uint4 rw[4], rx[4];
+    auto load_tile = [&](int kt) {
+        const size_t kbyte = (size_t)kt * KB;
+        size_t wk = kbyte;
+        if (!UP && shared) {
+            // shared down projection: k runs over K_s segments of width w
+            const int k_el = kt * (KB / ES);
+            const int seg = k_el / P.w;
+            wk = ((size_t)seg * P.d * P.w + (k_el - seg * P.w)) * ES;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rw[i] = wvalid[i] ? *(const uint4 *)(wsrc[i] + wk) : make_uint4(0, 0, 0, 0);
+            rx[i] = xsrc[i] ? *(const uint4 *)(xsrc[i] + kbyte) : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    // LDS byte offsets of this lane's fragments (k step 0)
+    int wfrag[2], xfrag[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int wr = UP ? (ni * 64 + wn * 32 + l32) : (wn * 64 + ni * 32 + l32);
+        wfrag[ni] = wr * PITCH + lhi * (8 * ES);
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) xfrag[mi] = (wm * 64 + mi * 32 + l32) * PITCH + lhi * (8 * ES);
+
+    const int nk = K * ES / KB;
+    load_tile(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;
+            const int off = (c >> 3) * PITCH + (c & 7) * 16;
+            *(uint4 *)(s_w + off) = rw[i];
+            *(uint4 *)(s_x + off) = rx[i];
+        }
+        __syncthreads();
+        if (kt + 1 < nk) load_tile(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < KB / KSTEP; ++ks) {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+                    mfma_k16(acc[ni][mi], s_w + wfrag[ni] + ks * KSTEP, s_x + xfrag[mi] + ks * KSTEP, DT{});
+        }
+    }
+
+    // ---- epilogue: lane owns token column l32; register quad q holds 4 consecutive
+    //      weight rows 8q + 4*lhi + {0..3} of each 32x32 block ----
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int row = m0 + wm * 64 + mi * 32 + l32;
+        if (row >= rows) continue;
+        if (UP) {
+            const int ld = shared ? P.Ks * P.w : P.w;
+            DT *dst = (DT *)(shared ? P.out_shared : P.out_routed) + (size_t)(row_off + row) * ld;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = acc[0][mi][4 * q + e];
+                    const float u = acc[1][mi][4 * q + e];
+                    v[e] = p / (1.0f + __expf(-p)) * u;
+                }
+                store4(dst + n_tile * 64 + wn * 32 + 8 * q + 4 * lhi, v);
+            }
+        } else {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = n_tile * BN + wn * 64 + ni * 32 + 8 * q + 4 * lhi;
+                    if (col >= P.d) continue;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[ni][mi][4 * q + e];
+                    if (shared) store4((float *)P.out_shared + (size_t)row * P.d + col, v);
+                    else store4((DT *)P.out_routed + (size_t)(row_off + row) * P.d + col, v);
+                }
+        }
+    }
+}
+
+template <typename DT>
+hipError_t launch_typed(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
+    const int T = p.T, Ks = p.n_shared, Nr = p.n_routed, w = p.inter, d = p.d;
+    const int rt_bound = (int)(((int64_t)T * p.top_k) / BM) + Nr;  // >= sum_r ceil(c_r / BM)
+    const int mts = Ks > 0 ? cdiv(T, BM) : 0;
+
+    GemmParams P{};
+    P.T = T; P.d = d; P.Ks = Ks; P.Nr = Nr; P.w = w;
+    P.offsets = a.offsets;
+    P.sorted_token = a.sorted_token;
+    P.x = (const uint8_t *)a.x;
+    P.act_shared = (const uint8_t *)a.act_shared;
+    P.act_routed = (const uint8_t *)a.act_routed;
+
+    // up projection + SwiGLU
+    P.wa_r = (const uint8_t *)a.w1_r; P.wb_r = (const uint8_t *)a.w3_r;
+    P.wa_s = (const uint8_t *)a.w1_s; P.wb_s = (const uint8_t *)a.w3_s;
+    P.out_shared = (uint8_t *)a.act_shared; P.out_routed = (uint8_t *)a.act_routed;
+    const int up_tiles = mts * (Ks * w / 64) + (Nr > 0 ? rt_bound * (w / 64) : 0);
+    if (up_tiles > 0) {
+        grouped_ffn_kernel<DT, true><<<up_tiles, 256, 0, s>>>(P);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // down projection
+    P.wa_r = (const uint8_t *)a.w2_r; P.wb_r = nullptr;
+    P.wa_s = (const uint8_t *)a.w2_s; P.wb_s = nullptr;
+    P.out_shared = (uint8_t *)a.y_shared; P.out_routed = (uint8_t *)a.y_routed;
+    const int dn_tiles = mts * cdiv(d, BN) + (Nr > 0 ? rt_bound * cdiv(d, BN) : 0);
+    if (dn_tiles > 0) {
+        grouped_ffn_kernel<DT, false><<<dn_tiles, 256, 0, s>>>(P);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
+    if (p.dtype == MOE_BF16) return launch_typed<uint16_t>(p, a, s);
+    return launch_typed<float>(p, a, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,93 @@
+// moe_internal.h -- private declarations shared by the HIP sources of libmoe.
+// Not installed, not part of the C ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Tokens handled by one routing workgroup.
+constexpr int kRouteTokens = 64;
+// Tokens handled by one grouping (permute) workgroup.
+constexpr int kPermuteTokens = 256;
+// Largest N' the routing kernel supports, and K' bound.
+constexpr int kRouteMaxExperts = 256;
+constexpr int kRouteMaxTopK = 16;
+// Largest N' the grouping kernels support.
+constexpr int kPermuteMaxExperts = 1024;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+__host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+inline size_t dtype_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+// Byte offsets of each call's scratch inside the caller's workspace.  The
+// regions are disjoint, so one workspace serves a whole layer pass.
+struct WsLayout {
+    size_t route_counts;   // int32  [route_blocks, N']  per-block expert counts
+    size_t route_psum;     // double [route_blocks, N']  per-block affinity sums
+    size_t perm_hist;      // int32  [perm_blocks, N']   per-block histogram
+    size_t perm_base;      // int32  [perm_blocks, N']   first slot of each (block, expert)
+    size_t act_shared;     // dtype  [T, K_s*w]          SwiGLU activations, shared experts
+    size_t act_routed;     // dtype  [T*K', w]           SwiGLU activations, grouped order
+    size_t total;
+};
+
+inline WsLayout ws_layout(const moe_problem &p) {
+    WsLayout L{};
+    const size_t nr = (size_t)p.n_routed;
+    const size_t rb = (size_t)cdiv(p.T, kRouteTokens);
+    const size_t pb = (size_t)cdiv(p.T, kPermuteTokens);
+    const size_t es = dtype_bytes(p.dtype);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes, 256); return at; };
+    L.route_counts = take(rb * nr * sizeof(int32_t));
+    L.route_psum = take(rb * nr * sizeof(double));
+    L.perm_hist = take(pb * nr * sizeof(int32_t));
+    L.perm_base = take(pb * nr * sizeof(int32_t));
+    L.act_shared = take((size_t)p.T * p.n_shared * p.inter * es);
+    L.act_routed = take((size_t)p.T * p.top_k * p.inter * es);
+    L.total = off;
+    return L;
+}
+
+// ---- launchers (each returns hipSuccess or the launch error) -------------
+
+hipError_t launch_route(const moe_problem &p, const void *x, const float *centroids,
+                        const float *bias, int32_t *idx, float *gate, float *probs,
+                        int32_t *part_counts, double *part_psum, int32_t *counts,
+                        float *prob_sum, hipStream_t s);
+
+hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *offsets,
+                          int32_t *sorted_token, int32_t *slot_of, int32_t *hist,
+                          int32_t *base, hipStream_t s);
+
+struct FfnArgs {
+    const void *x;
+    const int32_t *offsets;
+    const int32_t *sorted_token;
+    const void *w1_r, *w3_r, *w2_r;
+    const void *w1_s, *w3_s, *w2_s;
+    void *act_shared, *act_routed;
+    void *y_routed;
+    float *y_shared;
+};
+
+hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, hipStream_t s);
+
+hipError_t launch_combine(const moe_problem &p, const void *x, const void *y_routed,
+                          const float *y_shared, const float *gate, const int32_t *slot_of,
+                          void *h, hipStream_t s);
+
+hipError_t launch_balance_stats(const moe_problem &p, int groups, const int32_t *counts,
+                                const float *prob_sum, float *f, float *P, float *f_dev,
+                                float *P_dev, float *exp_bal, float *dev_bal, hipStream_t s);
+
+}  // namespace moe

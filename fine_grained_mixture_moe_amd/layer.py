@@ -1,0 +1,152 @@
+"""Device buffers for one DeepSeekMoE layer pass and the five-call sequence.
+
+torch is used only to allocate device memory, upload inputs and read results
+back; every step of the layer runs in libmoe's HIP kernels through the C ABI
+(moe_route -> moe_permute -> moe_expert_ffn -> moe_combine ->
+moe_balance_stats).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import moe as M
+from .workloads import LayerInputs
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(a: np.ndarray, dtype: str, device):
+    """Upload an fp32 array (dtype "f32") or bf16 bit patterns (dtype "bf16")."""
+    torch = _torch()
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        assert a.dtype == np.uint16
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.int32:
+        return torch.from_numpy(a).to(device)
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to(device)
+
+
+def to_numpy_f32(t) -> np.ndarray:
+    """Device tensor (bf16 or fp32) -> fp32 NumPy array (exact upcast for bf16)."""
+    torch = _torch()
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+class DeviceLayer:
+    """Inputs resident in HBM plus every output buffer of one layer pass."""
+
+    def __init__(self, inp: LayerInputs, device="cuda", want_probs: bool = False, groups: Optional[int] = None,
+                 top_k: Optional[int] = None):
+        torch = _torch()
+        wl = inp.wl
+        self.inp = inp
+        self.device = torch.device(device)
+        self.dtype = wl.dtype
+        self.groups = groups if groups is not None else wl.groups
+        T, d, Ks, Nr, w = wl.T, wl.d, wl.n_shared, wl.n_routed, wl.inter
+        K = wl.top_k if top_k is None else top_k
+        self.prob = M.moe_problem.make(T, d, Ks, Nr, K, w, wl.dtype)
+        dev = self.device
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+        self.x = to_device(inp.x.device_bits(wl.dtype), wl.dtype, dev)
+        self.centroids = to_device(inp.centroids, "f32", dev) if Nr else None
+        self.bias = None if inp.bias is None else to_device(inp.bias, "f32", dev)
+        sh, ro = inp.shared, inp.routed
+        self.w1_s = to_device(sh(inp.w1).device_bits(wl.dtype), wl.dtype, dev) if Ks else None
+        self.w3_s = to_device(sh(inp.w3).device_bits(wl.dtype), wl.dtype, dev) if Ks else None
+        self.w2_s = to_device(sh(inp.w2).device_bits(wl.dtype), wl.dtype, dev) if Ks else None
+        self.w1_r = to_device(ro(inp.w1).device_bits(wl.dtype), wl.dtype, dev) if Nr else None
+        self.w3_r = to_device(ro(inp.w3).device_bits(wl.dtype), wl.dtype, dev) if Nr else None
+        self.w2_r = to_device(ro(inp.w2).device_bits(wl.dtype), wl.dtype, dev) if Nr else None
+
+        i32, f32 = torch.int32, torch.float32
+        TK = T * K
+        self.idx = torch.empty((T, K), dtype=i32, device=dev)
+        self.gate = torch.empty((T, K), dtype=f32, device=dev)
+        self.probs = torch.empty((T, Nr), dtype=f32, device=dev) if want_probs else None
+        self.counts = torch.empty(max(Nr, 1), dtype=i32, device=dev)
+        self.prob_sum = torch.empty(max(Nr, 1), dtype=f32, device=dev)
+        self.offsets = torch.empty(Nr + 1, dtype=i32, device=dev)
+        self.sorted_token = torch.empty(max(TK, 1), dtype=i32, device=dev)
+        self.slot_of = torch.empty((T, K), dtype=i32, device=dev)
+        self.y_routed = torch.empty((max(TK, 1), d), dtype=tdt, device=dev)
+        self.y_shared = torch.empty((T, d), dtype=f32, device=dev) if Ks else None
+        self.h = torch.empty((T, d), dtype=tdt, device=dev)
+        D = max(self.groups, 1)
+        self.f = torch.empty(max(Nr, 1), dtype=f32, device=dev)
+        self.P = torch.empty(max(Nr, 1), dtype=f32, device=dev)
+        self.f_dev = torch.empty(D, dtype=f32, device=dev)
+        self.P_dev = torch.empty(D, dtype=f32, device=dev)
+        self.exp_bal = torch.empty(1, dtype=f32, device=dev)
+        self.dev_bal = torch.empty(1, dtype=f32, device=dev)
+        self.ws_bytes = M.moe_workspace_size(self.prob)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    # -- the five calls ----------------------------------------------------
+    def route(self, stream=None):
+        M.moe_route(self.prob, self.x, self.centroids, self.bias, self.idx, self.gate, self.probs, self.counts,
+                    self.prob_sum, self.ws, self.ws_bytes, stream)
+
+    def permute(self, stream=None):
+        M.moe_permute(self.prob, self.idx, self.offsets, self.sorted_token, self.slot_of, self.ws, self.ws_bytes,
+                      stream)
+
+    def expert_ffn(self, stream=None):
+        M.moe_expert_ffn(self.prob, self.x, self.offsets, self.sorted_token, self.w1_r, self.w3_r, self.w2_r,
+                         self.w1_s, self.w3_s, self.w2_s, self.y_routed, self.y_shared, self.ws, self.ws_bytes,
+                         stream)
+
+    def combine(self, stream=None):
+        M.moe_combine(self.prob, self.x, self.y_routed, self.y_shared, self.gate, self.slot_of, self.h, stream)
+
+    def balance_stats(self, stream=None):
+        M.moe_balance_stats(self.prob, self.groups, self.counts, self.prob_sum, self.f, self.P, self.f_dev,
+                            self.P_dev, self.exp_bal, self.dev_bal, stream)
+
+    def forward(self, stream=None, stats: bool = True):
+        """One whole layer pass on the stream."""
+        if self.prob.n_routed:
+            self.route(stream)
+        self.permute(stream)
+        self.expert_ffn(stream)
+        self.combine(stream)
+        if stats and self.prob.n_routed:
+            self.balance_stats(stream)
+
+    def forward_with_routing(self, idx: np.ndarray, gate: np.ndarray, stream=None):
+        """Layer pass with an externally supplied routing (e.g. every expert at gate 1)."""
+        torch = _torch()
+        self.idx.copy_(torch.from_numpy(np.ascontiguousarray(idx, np.int32)))
+        self.gate.copy_(torch.from_numpy(np.ascontiguousarray(gate, np.float32)))
+        self.permute(stream)
+        self.expert_ffn(stream)
+        self.combine(stream)
+
+    # -- readback ----------------------------------------------------------
+    def results(self) -> dict:
+        torch = _torch()
+        torch.cuda.synchronize(self.device)
+        Nr = self.prob.n_routed
+        TK = self.prob.T * self.prob.top_k
+        out = dict(
+            idx=self.idx.cpu().numpy(), gate=self.gate.cpu().numpy(),
+            counts=self.counts.cpu().numpy()[:Nr], prob_sum=self.prob_sum.cpu().numpy()[:Nr],
+            offsets=self.offsets.cpu().numpy(), sorted_token=self.sorted_token.cpu().numpy()[:TK],
+            slot_of=self.slot_of.cpu().numpy(),
+            y_routed=to_numpy_f32(self.y_routed)[:TK],
+            y_shared=None if self.y_shared is None else self.y_shared.cpu().numpy(),
+            h=to_numpy_f32(self.h),
+            f=self.f.cpu().numpy()[:Nr], P=self.P.cpu().numpy()[:Nr],
+            f_dev=self.f_dev.cpu().numpy(), P_dev=self.P_dev.cpu().numpy(),
+            exp_bal=float(self.exp_bal.cpu()[0]), dev_bal=float(self.dev_bal.cpu()[0]),
+        )
+        if self.probs is not None:
+            out["probs"] = self.probs.cpu().numpy()
+        return out

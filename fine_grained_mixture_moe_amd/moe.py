@@ -1,0 +1,133 @@
+"""Thin ctypes binding of libmoe.so (include/moe.h) -- argument marshalling only.
+
+Each function has the name of the C entry point it wraps and takes torch
+tensors on the GPU (or None for nullable pointers); it passes their device
+pointers and the current HIP stream, and raises MoEError on a non-zero
+status.  No layer arithmetic happens here: every step runs in the HIP
+kernels.  There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {moe_status_str(status)} ({status})")
+        self.status = status
+
+
+class moe_problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("n_routed", ctypes.c_int32), ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+    @classmethod
+    def make(cls, T, d, n_shared, n_routed, top_k, inter, dtype) -> "moe_problem":
+        dt = dtype if isinstance(dtype, int) else {"f32": MOE_F32, "bf16": MOE_BF16}[dtype]
+        return cls(T, d, n_shared, n_routed, top_k, inter, dt)
+
+    def __repr__(self):
+        return (f"moe_problem(T={self.T}, d={self.d}, n_shared={self.n_shared}, n_routed={self.n_routed}, "
+                f"top_k={self.top_k}, inter={self.inter}, dtype={self.dtype})")
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_pp = ctypes.POINTER(moe_problem)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is missing: run __graft_entry__.build() (hipcc, gfx950) first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [ctypes.c_int]
+        L.moe_version.restype = ctypes.c_char_p
+        L.moe_workspace_size.argtypes = [_pp, ctypes.POINTER(_sz)]
+        L.moe_route.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_permute.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_expert_ffn.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_combine.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_balance_stats.argtypes = [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
+                   "moe_balance_stats"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+def moe_status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()
+
+
+def moe_workspace_size(p: moe_problem) -> int:
+    n = _sz(0)
+    _check("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def moe_route(p, x, centroids, bias, idx, gate, probs, counts, prob_sum, ws, ws_bytes, stream=None):
+    _check("moe_route", lib().moe_route(ctypes.byref(p), _ptr(x), _ptr(centroids), _ptr(bias), _ptr(idx),
+                                        _ptr(gate), _ptr(probs), _ptr(counts), _ptr(prob_sum), _ptr(ws),
+                                        ws_bytes, _stream(stream)))
+
+
+def moe_permute(p, idx, offsets, sorted_token, slot_of, ws, ws_bytes, stream=None):
+    _check("moe_permute", lib().moe_permute(ctypes.byref(p), _ptr(idx), _ptr(offsets), _ptr(sorted_token),
+                                            _ptr(slot_of), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_expert_ffn(p, x, offsets, sorted_token, w1_routed, w3_routed, w2_routed, w1_shared, w3_shared,
+                   w2_shared, y_routed, y_shared, ws, ws_bytes, stream=None):
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        ctypes.byref(p), _ptr(x), _ptr(offsets), _ptr(sorted_token), _ptr(w1_routed), _ptr(w3_routed),
+        _ptr(w2_routed), _ptr(w1_shared), _ptr(w3_shared), _ptr(w2_shared), _ptr(y_routed), _ptr(y_shared),
+        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_combine(p, x, y_routed, y_shared, gate, slot_of, h, stream=None):
+    _check("moe_combine", lib().moe_combine(ctypes.byref(p), _ptr(x), _ptr(y_routed), _ptr(y_shared),
+                                            _ptr(gate), _ptr(slot_of), _ptr(h), _stream(stream)))
+
+
+def moe_balance_stats(p, groups, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, dev_bal, stream=None):
+    _check("moe_balance_stats", lib().moe_balance_stats(
+        ctypes.byref(p), int(groups), _ptr(counts), _ptr(prob_sum), _ptr(f), _ptr(P), _ptr(f_dev),
+        _ptr(P_dev), _ptr(exp_bal), _ptr(dev_bal), _stream(stream)))

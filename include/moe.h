@@ -1,0 +1,200 @@
+/*
+ * moe.h -- C ABI of the DeepSeekMoE layer forward on one MI355X (gfx950).
+ *
+ * The layer (source: "[ACL 2024] DeepSeekMoE: 混合专家语言模型中的极致专家特化",
+ * section "Method details: formulas and load balance"):
+ *
+ *   s_{r,t} = softmax_r(u_t . e_r)                over the N' routed experts
+ *   g_{r,t} = s_{r,t} if r in Topk(s_t, K') else 0
+ *   h_t     = sum_{i < K_s} FFN_i(u_t) + sum_r g_{r,t} FFN_{K_s + r}(u_t) + u_t
+ *
+ * with the first K_s experts shared (always active), the remaining N' routed,
+ * each expert a SwiGLU FFN  FFN(u) = W2 (SiLU(W1 u) * (W3 u))  of intermediate
+ * width w (1/m of a standard FFN, section "Two core strategies"), and the
+ * balance terms of the same section and of "【论文总结】MoE" sections 2.3-2.4:
+ *
+ *   f_r  = N'/(K'T) * #{t : t selects r},     P_r = mean_t s_{r,t}
+ *   f'_g = mean of f over device group g,      P'_g = sum of P over group g
+ *   ExpBal = sum_r f_r P_r,                    DevBal = sum_g f'_g P'_g
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is device memory owned by the caller (contiguous,
+ *    row-major, 16-byte aligned).  The library allocates nothing and keeps no
+ *    mutable global state; calls on different streams with different
+ *    workspaces are independent.
+ *  - Every call validates its arguments on the host first.  On an error it
+ *    returns a negative status, enqueues nothing and leaves outputs untouched.
+ *    Launch failures return MOE_ERR_HIP.  Faults inside kernels surface at
+ *    the caller's next synchronisation.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Outputs are overwritten, never accumulated into.
+ *  - dtype (moe_problem.dtype) applies to x, the expert weights, y_routed and
+ *    h.  Centroids, bias, gates, probabilities and statistics are fp32;
+ *    indices and counts are int32.
+ *  - Shapes: d % 64 == 0, w % 64 == 0, T >= 0, K_s >= 0, N' >= 0;
+ *    N' == 0 (a dense, shared-only layer) requires K' == 0, otherwise
+ *    1 <= K' <= N'.  T*K' and T*K_s*w must fit in int32.
+ *  - Routing inputs must be finite.  Expert indices handed to moe_permute
+ *    must lie in [0, N') and be distinct within a token; entries that are
+ *    not are skipped (memory stays safe, results for that token are
+ *    undefined).
+ *  - Expert weights, per expert, "out x in": W1 and W3 are [w, d], W2 is
+ *    [d, w].  Shared experts are stacked [K_s, ...], routed [N', ...].
+ *  - The workspace `ws` (size from moe_workspace_size) holds the per-block
+ *    partial statistics, the grouping scratch and the SwiGLU activations.
+ *    The calls use disjoint parts of it, so one workspace serves a whole
+ *    layer pass on one stream.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG (-1)  /* null pointer, bad shape, bad group count     */
+#define MOE_ERR_UNSUPPORTED (-2)  /* outside the supported envelope (see each call) */
+#define MOE_ERR_WORKSPACE   (-3)  /* workspace missing or smaller than required    */
+#define MOE_ERR_HIP         (-4)  /* a HIP launch or runtime call failed           */
+
+/* element types of x, weights, y_routed and h */
+#define MOE_F32  0
+#define MOE_BF16 1
+
+typedef struct moe_problem {
+    int32_t T;         /* tokens in the batch                                  */
+    int32_t d;         /* hidden size                                          */
+    int32_t n_shared;  /* K_s: shared experts, always active                   */
+    int32_t n_routed;  /* N': routed experts                                   */
+    int32_t top_k;     /* K': routed experts selected per token                */
+    int32_t inter;     /* w: expert intermediate width                         */
+    int32_t dtype;     /* MOE_F32 or MOE_BF16                                  */
+} moe_problem;
+
+/* Human-readable text of a status code (static storage). */
+const char *moe_status_str(int status);
+
+/* Library build/version tag (static storage). */
+const char *moe_version(void);
+
+/* Bytes of workspace one layer pass needs for `p` (written to *bytes).
+ * Returns MOE_ERR_INVALID_ARG on a bad problem or null pointers. */
+int moe_workspace_size(const moe_problem *p, size_t *bytes);
+
+/*
+ * moe_route -- gating: token-to-centroid affinities, softmax, Top-K'.
+ * Source: "[ACL 2024] DeepSeekMoE ..." section "Method details" (gates from
+ * Top-k of the affinities; only routed experts are selected), "【论文总结】MoE"
+ * section 2.2 (centroids e_i).
+ *
+ *   x        [T, d]   dtype      token activations u_t
+ *   centroids[N', d]  fp32       e_r
+ *   bias     [N']     fp32       optional additive logit bias (NULL = none)
+ *   idx      [T, K']  int32  out selected routed experts, order (z desc, r asc)
+ *   gate     [T, K']  fp32   out s_{idx[t,k], t}
+ *   probs    [T, N']  fp32   out all affinities s (NULL = not written)
+ *   counts   [N']     int32  out tokens per routed expert
+ *   prob_sum [N']     fp32   out sum_t s_{r,t}
+ *
+ * Logits z_{t,r} are accumulated in fp32 as one fused multiply-add chain over
+ * k = 0..d-1 in ascending order starting from +0, then the bias is added in
+ * one fp32 add; selection compares z (ties go to the lower index), so the
+ * selected experts do not depend on how exp is evaluated.  Deterministic:
+ * counts and prob_sum are reduced in a fixed order without atomics.
+ * Envelope: 1 <= K' <= min(N', 16), 1 <= N' <= 256 (MOE_ERR_UNSUPPORTED).
+ */
+int moe_route(const moe_problem *p, const void *x, const float *centroids,
+              const float *bias, int32_t *idx, float *gate, float *probs,
+              int32_t *counts, float *prob_sum, void *ws, size_t ws_bytes,
+              void *stream);
+
+/*
+ * moe_permute -- group (token, expert) pairs by routed expert: histogram,
+ * exclusive scan, stable scatter (tokens ascending within an expert).  This
+ * is the bookkeeping behind "token t selects expert i" ("【论文总结】MoE"
+ * section 2.3).  It recounts from idx, so any routing can be supplied.
+ *
+ *   idx          [T, K']   int32 in   routed expert of each (t, k)
+ *   offsets      [N'+1]    int32 out  offsets[r] = pairs of experts < r
+ *   sorted_token [T*K']    int32 out  tokens of expert 0, then expert 1, ...
+ *   slot_of      [T, K']   int32 out  position of (t, idx[t,k]) in sorted_token
+ *
+ * Envelope: N' <= 1024; 1 <= K' <= N' (any K', e.g. every expert active).
+ */
+int moe_permute(const moe_problem *p, const int32_t *idx, int32_t *offsets,
+                int32_t *sorted_token, int32_t *slot_of, void *ws,
+                size_t ws_bytes, void *stream);
+
+/*
+ * moe_expert_ffn -- the expert FFNs (SwiGLU, no biases) on MFMA.
+ * Source: "[ACL 2024] DeepSeekMoE ..." sections "Two core strategies" (m
+ * fine-grained experts of width 1/m; K_s shared experts always active) and
+ * "Method details" (FFN_i terms of the layer output).
+ *
+ *   x            [T, d]         dtype in
+ *   offsets      [N'+1]         int32 in   from moe_permute
+ *   sorted_token [T*K']         int32 in   from moe_permute
+ *   w1_routed, w3_routed [N', w, d]  dtype;  w2_routed [N', d, w]  dtype
+ *   w1_shared, w3_shared [K_s, w, d] dtype;  w2_shared [K_s, d, w] dtype
+ *   y_routed     [T*K', d]      dtype out  y_routed[j] = FFN_{e(j)}(u_{sorted_token[j]})
+ *                                          (unweighted, in grouped order)
+ *   y_shared     [T, d]         fp32  out  sum_{i < K_s} FFN_i(u_t)
+ *                                          (may be NULL when K_s == 0)
+ *
+ * The K_s shared experts run as one dense expert of width K_s*w over all T
+ * rows.  Accumulation is fp32; the SwiGLU activation is rounded to dtype
+ * before the down projection.  Routed pointers may be NULL when N' == 0 and
+ * shared pointers when K_s == 0.
+ */
+int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets,
+                   const int32_t *sorted_token, const void *w1_routed,
+                   const void *w3_routed, const void *w2_routed,
+                   const void *w1_shared, const void *w3_shared,
+                   const void *w2_shared, void *y_routed, float *y_shared,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine -- layer output, "[ACL 2024] DeepSeekMoE ..." section "Method
+ * details" (output formula):
+ *   h_t = u_t + y_shared_t + sum_{k < K'} gate[t,k] * y_routed[slot_of[t,k]]
+ * summed in k order in fp32 (deterministic), written as dtype.
+ *
+ *   x [T, d] dtype, y_routed [T*K', d] dtype, y_shared [T, d] fp32 (NULL =
+ *   zero), gate [T, K'] fp32, slot_of [T, K'] int32, h [T, d] dtype out.
+ */
+int moe_combine(const moe_problem *p, const void *x, const void *y_routed,
+                const float *y_shared, const float *gate, const int32_t *slot_of,
+                void *h, void *stream);
+
+/*
+ * moe_balance_stats -- expert-level and device-level balance terms.
+ * Source: "[ACL 2024] DeepSeekMoE ..." section "Method details" (expert-level
+ * and device-level balance losses), "【论文总结】MoE" sections 2.3 (symbols T,
+ * N', K', indicator, factor N'/K') and 2.4 (f'_i, P'_i of a device).
+ *
+ *   groups D: routed experts are split into D contiguous equal groups
+ *   counts [N'] int32, prob_sum [N'] fp32       in (from moe_route)
+ *   f [N'], P [N'], f_dev [D], P_dev [D]        fp32 out
+ *   exp_bal [1], dev_bal [1]                    fp32 out (alpha_1, alpha_2 not applied)
+ *
+ *   f_r = RN_fp32((double)N' * counts[r] / ((double)K' * T))
+ *   P_r = prob_sum[r] / T
+ *   f'_g = RN_fp32((double)N' * C_g / ((double)K' * T * (N'/D))), C_g = sum of counts in g
+ *   P'_g = sum of P over g;  ExpBal = sum f P;  DevBal = sum f' P'  (fp64, then fp32)
+ * T == 0 gives f = P = 0.  Requires N' >= 1, 1 <= K' <= N', D >= 1, D | N'.
+ */
+int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *counts,
+                      const float *prob_sum, float *f, float *P, float *f_dev,
+                      float *P_dev, float *exp_bal, float *dev_bal, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,104 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and rejects bad arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fine_grained_mixture_moe_amd import moe as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
+               "moe_workspace_size", "moe_status_str"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = M.lib()
+    for fn in declared_functions():
+        assert hasattr(L, fn), fn
+        assert ctypes.cast(getattr(L, fn), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    assert M.moe_status_str(0) == "MOE_OK"
+    for code in (-1, -2, -3, -4):
+        assert M.moe_status_str(code).startswith("MOE_ERR")
+    assert "gfx950" in M.moe_version()
+
+
+def test_workspace_size_and_shape_validation():
+    p = M.moe_problem.make(4096, 1280, 0, 64, 8, 512, "bf16")
+    n = M.moe_workspace_size(p)
+    # at least the routed SwiGLU activations T*K'*w in bf16
+    assert n >= 4096 * 8 * 512 * 2
+    bad = [
+        M.moe_problem.make(16, 100, 0, 8, 2, 64, "f32"),    # d % 64
+        M.moe_problem.make(16, 128, 0, 8, 2, 96, "f32"),    # w % 64
+        M.moe_problem.make(16, 128, 0, 8, 9, 64, "f32"),    # K' > N'
+        M.moe_problem.make(16, 128, 0, 0, 1, 64, "f32"),    # N' = 0 needs K' = 0
+        M.moe_problem.make(-1, 128, 0, 8, 2, 64, "f32"),    # T < 0
+        M.moe_problem.make(16, 128, 0, 8, 2, 64, 7),        # dtype
+    ]
+    for q in bad:
+        with pytest.raises(M.MoEError):
+            M.moe_workspace_size(q)
+    # shared-only (dense) problem is valid
+    assert M.moe_workspace_size(M.moe_problem.make(16, 128, 1, 0, 0, 64, "f32")) > 0
+
+
+FAKE = 1 << 20  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def test_route_rejects_bad_arguments_before_launch():
+    p = M.moe_problem.make(64, 128, 1, 8, 2, 64, "f32")
+    ws = M.moe_workspace_size(p)
+    with pytest.raises(M.MoEError) as e:   # null centroids
+        M.moe_route(p, FAKE, None, None, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:   # workspace too small
+        M.moe_route(p, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws - 1, 0)
+    assert e.value.status == M.MOE_ERR_WORKSPACE
+    with pytest.raises(M.MoEError) as e:   # misaligned x
+        M.moe_route(p, FAKE + 4, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    q = M.moe_problem.make(64, 128, 0, 300, 2, 64, "f32")   # N' beyond the routing envelope
+    with pytest.raises(M.MoEError) as e:
+        M.moe_route(q, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, 0)
+    assert e.value.status == M.MOE_ERR_UNSUPPORTED
+    q = M.moe_problem.make(64, 128, 0, 64, 17, 64, "f32")   # K' beyond 16
+    with pytest.raises(M.MoEError) as e:
+        M.moe_route(q, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, 0)
+    assert e.value.status == M.MOE_ERR_UNSUPPORTED
+
+
+def test_other_calls_reject_bad_arguments_before_launch():
+    p = M.moe_problem.make(64, 128, 1, 8, 2, 64, "bf16")
+    ws = M.moe_workspace_size(p)
+    with pytest.raises(M.MoEError) as e:
+        M.moe_permute(p, None, FAKE, FAKE, FAKE, FAKE, ws, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:   # shared experts present but y_shared missing
+        M.moe_expert_ffn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:
+        M.moe_expert_ffn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0)
+    assert e.value.status == M.MOE_ERR_WORKSPACE
+    with pytest.raises(M.MoEError) as e:
+        M.moe_combine(p, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:   # D does not divide N'
+        M.moe_balance_stats(p, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
