@@ -1,0 +1,301 @@
+"""Benchmark of the DeepSeekMoE layer forward on one MI355X.
+
+One step = one whole layer pass through the C ABI on synthetic seeded inputs
+already resident in HBM: moe_route -> moe_permute -> moe_expert_up ->
+moe_expert_down -> moe_combine -> moe_balance_stats.  Prints ONE JSON line.
+
+Default workload: the fine-grained half of the granularity-equivalence pair
+(T=4096, d=1280, 64 routed experts of width 512, top-8, bf16); the
+coarse GShard-style half (16 experts of width 2048, top-2, same weights) is
+timed alongside for the fine/coarse ratio.  Other workloads: --config.
+
+Extra modes (used to produce the committed profile summaries):
+  --copy-probe       also run a plain device copy of known size (counter calibration)
+  --ingest-pmc DIR   read rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs under DIR
+                     and write profiles/traffic_<kernel>_<workload>.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + active TFLOP/s (% MFMA/HBM peak) on 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+UP_KERNEL = "grouped_ffn_kernel<bf16, up>"
+KERNEL_SOURCES = ["fine_grained_mixture_moe_amd/csrc/expert_ffn.hip",
+                  "fine_grained_mixture_moe_amd/csrc/moe_internal.h"]
+COPY_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def up_algorithmic(wl, counts) -> dict:
+    """Algorithmic work of one up-projection launch (gate+up GEMMs with SwiGLU).
+
+    Per (token, expert) pair: 4*d*w FLOPs (two d x w products).  Bytes: W1 and
+    W3 of every touched expert (all shared + routed experts with tokens), the
+    token rows read once, the SwiGLU activations written once.
+    """
+    es = 2 if wl.dtype == "bf16" else 4
+    pairs = wl.T * (wl.top_k + wl.n_shared)
+    flops = 4.0 * wl.d * wl.inter * pairs
+    touched = wl.n_shared + int((counts > 0).sum())
+    byts = 2.0 * wl.inter * wl.d * es * touched + wl.T * wl.d * es + pairs * wl.inter * es
+    return dict(flops=flops, bytes=byts, pairs=pairs, touched=touched)
+
+
+def layer_bytes(wl, counts) -> float:
+    """Algorithmic bytes of one layer pass: touched expert weights, x in, h out, centroids, routing table."""
+    es = 2 if wl.dtype == "bf16" else 4
+    touched = wl.n_shared + int((counts > 0).sum())
+    return (3.0 * wl.inter * wl.d * es * touched + 2.0 * wl.T * wl.d * es + wl.n_routed * wl.d * 4
+            + wl.T * wl.top_k * 8)
+
+
+def load_traffic(kernel_tag: str, workload: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        log(f"[bench] {path} was measured on other kernel sources: traffic reported as null")
+        return None
+    return rec
+
+
+def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
+    """The oracle (plain C, fp64 FFN, OpenMP over tokens) on a bounded sample of the workload."""
+    from oracle import oracle as O
+    wl = inp.wl
+    sh, ro = inp.shared, inp.routed
+    args = (inp.x.f32, inp.centroids, inp.bias, wl.top_k, max(wl.groups, 1), sh(inp.w1).f32, sh(inp.w3).f32,
+            sh(inp.w2).f32, ro(inp.w1).f32, ro(inp.w3).f32, ro(inp.w2).f32)
+    n0 = min(wl.T, 64)
+    t0 = time.perf_counter()
+    O.forward(n0, *args)
+    dt0 = time.perf_counter() - t0
+    n = int(min(wl.T, max(n0, n0 * budget_s / max(dt0, 1e-6))))
+    n = max(n0, n - n % 64) if n >= 64 else n
+    t0 = time.perf_counter()
+    O.forward(n, *args)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {wl.T} tokens of the same workload, whole layer pass "
+                      f"(route, group, fp64 expert FFNs, combine, stats); {dt:.1f} s",
+            "tflops": wl.flops() * n / wl.T / dt / 1e12}
+
+
+def run(args) -> dict:
+    import numpy as np
+    import torch
+    from fine_grained_mixture_moe_amd import workloads as W
+    from fine_grained_mixture_moe_amd.layer import DeviceLayer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    name = args.config
+    t_gen = time.perf_counter()
+    coarse = None
+    if name in ("c2b", "c2a"):
+        coarse = W.make_c2_coarse()
+        inp = coarse if name == "c2a" else W.make_c2_fine(independent_centroids=True, coarse=coarse)
+    else:
+        inp = W.make_inputs(W.WORKLOADS[name])
+    wl = inp.wl
+    log(f"[bench] {name}: {wl.description} (inputs in {time.perf_counter() - t_gen:.1f}s)")
+    dl = DeviceLayer(inp, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        dl.route()
+        dl.permute()
+        if ev is not None:
+            ev[0].record(stream)
+        dl.expert_up()
+        if ev is not None:
+            ev[1].record(stream)
+        dl.expert_down()
+        dl.combine()
+        dl.balance_stats()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    up_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms = elapsed * 1e3 / args.steps
+    counts = dl.counts.cpu().numpy()[:wl.n_routed]
+
+    # per-stage breakdown (separate, untimed-for-value loop)
+    stages = ["route", "permute", "expert_up", "expert_down", "combine", "balance_stats"]
+    n_b = min(args.steps, 10)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_b)]
+    for i in range(n_b):
+        marks[i][0].record(stream)
+        for j, s in enumerate(stages):
+            getattr(dl, s)()
+            marks[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    breakdown = {s: round(sum(m[j].elapsed_time(m[j + 1]) for m in marks) / n_b, 4) for j, s in enumerate(stages)}
+
+    if args.copy_probe:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)   # an elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 x {COPY_BYTES} bytes")
+
+    up = up_algorithmic(wl, counts)
+    tflops = wl.flops() / (ms * 1e-3) / 1e12
+    ai = up["flops"] / up["bytes"]
+    mfma_peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        achieved = up["flops"] / (up_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(achieved / mfma_peak, 4)}
+    else:
+        achieved = up["bytes"] / (up_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    tr = load_traffic("up", name)
+    roof["traffic"] = None if tr is None else tr["bytes_per_launch"]
+    roof["kernel"] = UP_KERNEL if wl.dtype == "bf16" else "grouped_ffn_kernel<f32, up>"
+    roof["kernel_ms"] = round(up_ms, 4)
+    roof["algorithmic"] = {"flops": up["flops"], "bytes": up["bytes"], "pairs": up["pairs"],
+                           "touched_experts": up["touched"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(wl.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {wl.description}", "T": wl.T, "d": wl.d, "n_shared": wl.n_shared,
+                   "n_routed": wl.n_routed, "top_k": wl.top_k, "inter": wl.inter, "parallelism": "none (1 GPU)"},
+        "active_tflops": round(tflops, 2),
+        "active_mfma_frac": round(tflops / mfma_peak, 4),
+        "layer_hbm_gbs": round(layer_bytes(wl, counts) / (ms * 1e-3) / 1e9, 1),
+        "stage_ms": breakdown,
+        "roofline": roof,
+    }
+    if coarse is not None and name == "c2b" and not args.no_pair:
+        dc = DeviceLayer(coarse, device="cuda:0")
+        for _ in range(args.warmup):
+            dc.forward()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dc.forward()
+        torch.cuda.synchronize()
+        ms_a = (time.perf_counter() - t0) * 1e3 / args.steps
+        out["pair"] = {"c2a_gshard_ms_per_step": round(ms_a, 4), "fine_over_coarse_time": round(ms / ms_a, 3)}
+        del dc
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    return out
+
+
+def ingest_pmc(pmc_dir: str, workload: str) -> None:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the up kernel, scaled by the copy probe's readings."""
+    rows = []
+    for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    per = {}
+    for r in rows:
+        kname = r.get("Kernel_Name", "")
+        cname = r.get("Counter_Name", "")
+        if "grouped_ffn_kernel" in kname and ("true>" in kname or "Lb1E" in kname):
+            key = "up"
+        elif "grouped_ffn_kernel" in kname:
+            key = "down"
+        elif "elementwise" in kname.lower():
+            key = "copy"
+        else:
+            continue
+        per.setdefault((key, cname), []).append(float(r["Counter_Value"]))
+    rec = {"workload": workload, "source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = per.get(("copy", cname))
+        up = per.get(("up", cname))
+        if not cp or not up:
+            continue
+        # copy reads COPY_BYTES and writes COPY_BYTES: bytes per counter unit
+        copy_kib = max(cp)
+        scale = COPY_BYTES / copy_kib
+        rec[cname] = {"up_kib_per_dispatch": sum(up) / len(up), "copy_kib": copy_kib, "bytes_per_unit": scale,
+                      "up_bytes": sum(up) / len(up) * scale}
+    if "FETCH_SIZE" in rec and "WRITE_SIZE" in rec:
+        rec["bytes_per_launch"] = rec["FETCH_SIZE"]["up_bytes"] + rec["WRITE_SIZE"]["up_bytes"]
+    out = os.path.join(ROOT, "profiles", f"traffic_up_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2b", help="c1 c2a c2b c3 c4 c5a c5b c5c")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-pair", action="store_true", help="skip timing the coarse c2a half")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--ingest-pmc", default=None)
+    args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc, args.config)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this layer pass has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    out = run(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

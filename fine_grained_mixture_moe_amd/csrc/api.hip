@@ -96,29 +96,42 @@ int moe_permute(const moe_problem *p, const int32_t *idx, int32_t *offsets, int3
                                      (int32_t *)at(ws, L.perm_base), (hipStream_t)stream));
 }
 
-int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets, const int32_t *sorted_token,
-                   const void *w1_routed, const void *w3_routed, const void *w2_routed, const void *w1_shared,
-                   const void *w3_shared, const void *w2_shared, void *y_routed, float *y_shared, void *ws,
-                   size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the expert-FFN calls.  `up` / `down` select which
+// weights and outputs the call touches.
+int check_ffn(const moe_problem *p, bool up, bool down, const void *x, const int32_t *offsets,
+              const int32_t *sorted_token, const void *w1_routed, const void *w3_routed, const void *w2_routed,
+              const void *w1_shared, const void *w3_shared, const void *w2_shared, const void *y_routed,
+              const float *y_shared, const void *ws, size_t ws_bytes, WsLayout *L, bool *routed, bool *shared) {
     int rc = check_problem(p);
     if (rc != MOE_OK) return rc;
-    const bool routed = p->n_routed > 0 && (int64_t)p->T * p->top_k > 0;
-    const bool shared = p->n_shared > 0 && p->T > 0;
-    if (routed) {
-        if (!x || !offsets || !sorted_token || !w1_routed || !w3_routed || !w2_routed || !y_routed)
-            return MOE_ERR_INVALID_ARG;
-        if (!aligned16(w1_routed) || !aligned16(w3_routed) || !aligned16(w2_routed) || !aligned16(y_routed))
+    *routed = p->n_routed > 0 && (int64_t)p->T * p->top_k > 0;
+    *shared = p->n_shared > 0 && p->T > 0;
+    if (*routed) {
+        if (!offsets) return MOE_ERR_INVALID_ARG;
+        if (up && (!x || !sorted_token || !w1_routed || !w3_routed)) return MOE_ERR_INVALID_ARG;
+        if (down && (!w2_routed || !y_routed)) return MOE_ERR_INVALID_ARG;
+        if ((w1_routed && !aligned16(w1_routed)) || (w3_routed && !aligned16(w3_routed)) ||
+            (w2_routed && !aligned16(w2_routed)) || (y_routed && !aligned16(y_routed)))
             return MOE_ERR_INVALID_ARG;
     }
-    if (shared) {
-        if (!x || !w1_shared || !w3_shared || !w2_shared || !y_shared) return MOE_ERR_INVALID_ARG;
-        if (!aligned16(w1_shared) || !aligned16(w3_shared) || !aligned16(w2_shared) || !aligned16(y_shared))
+    if (*shared) {
+        if (up && (!x || !w1_shared || !w3_shared)) return MOE_ERR_INVALID_ARG;
+        if (down && (!w2_shared || !y_shared)) return MOE_ERR_INVALID_ARG;
+        if ((w1_shared && !aligned16(w1_shared)) || (w3_shared && !aligned16(w3_shared)) ||
+            (w2_shared && !aligned16(w2_shared)) || (y_shared && !aligned16(y_shared)))
             return MOE_ERR_INVALID_ARG;
     }
     if (x && !aligned16(x)) return MOE_ERR_INVALID_ARG;
-    WsLayout L;
-    if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
-    if (!routed && !shared) return MOE_OK;
+    return check_ws(p, ws, ws_bytes, L);
+}
+
+FfnArgs ffn_args(const void *x, const int32_t *offsets, const int32_t *sorted_token, const void *w1_routed,
+                 const void *w3_routed, const void *w2_routed, const void *w1_shared, const void *w3_shared,
+                 const void *w2_shared, void *y_routed, float *y_shared, void *ws, const WsLayout &L) {
     FfnArgs a{};
     a.x = x;
     a.offsets = offsets;
@@ -129,10 +142,63 @@ int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets, 
     a.act_routed = at(ws, L.act_routed);
     a.y_routed = y_routed;
     a.y_shared = y_shared;
-    moe_problem q = *p;
+    return a;
+}
+
+moe_problem active_part(const moe_problem &p, bool routed, bool shared) {
+    moe_problem q = p;
     if (!routed) q.n_routed = 0, q.top_k = 0;
     if (!shared) q.n_shared = 0;
-    return hip_status(launch_expert_ffn(q, a, (hipStream_t)stream));
+    return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_up(const moe_problem *p, const void *x, const int32_t *offsets, const int32_t *sorted_token,
+                  const void *w1_routed, const void *w3_routed, const void *w1_shared, const void *w3_shared,
+                  void *ws, size_t ws_bytes, void *stream) {
+    WsLayout L;
+    bool routed, shared;
+    int rc = check_ffn(p, true, false, x, offsets, sorted_token, w1_routed, w3_routed, nullptr, w1_shared,
+                       w3_shared, nullptr, nullptr, nullptr, ws, ws_bytes, &L, &routed, &shared);
+    if (rc != MOE_OK) return rc;
+    if (!routed && !shared) return MOE_OK;
+    const FfnArgs a = ffn_args(x, offsets, sorted_token, w1_routed, w3_routed, nullptr, w1_shared, w3_shared,
+                               nullptr, nullptr, nullptr, ws, L);
+    return hip_status(launch_expert_up(active_part(*p, routed, shared), a, (hipStream_t)stream));
+}
+
+int moe_expert_down(const moe_problem *p, const int32_t *offsets, const void *w2_routed, const void *w2_shared,
+                    void *y_routed, float *y_shared, void *ws, size_t ws_bytes, void *stream) {
+    WsLayout L;
+    bool routed, shared;
+    int rc = check_ffn(p, false, true, nullptr, offsets, nullptr, nullptr, nullptr, w2_routed, nullptr, nullptr,
+                       w2_shared, y_routed, y_shared, ws, ws_bytes, &L, &routed, &shared);
+    if (rc != MOE_OK) return rc;
+    if (!routed && !shared) return MOE_OK;
+    const FfnArgs a = ffn_args(nullptr, offsets, nullptr, nullptr, nullptr, w2_routed, nullptr, nullptr, w2_shared,
+                               y_routed, y_shared, ws, L);
+    return hip_status(launch_expert_down(active_part(*p, routed, shared), a, (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets, const int32_t *sorted_token,
+                   const void *w1_routed, const void *w3_routed, const void *w2_routed, const void *w1_shared,
+                   const void *w3_shared, const void *w2_shared, void *y_routed, float *y_shared, void *ws,
+                   size_t ws_bytes, void *stream) {
+    WsLayout L;
+    bool routed, shared;
+    int rc = check_ffn(p, true, true, x, offsets, sorted_token, w1_routed, w3_routed, w2_routed, w1_shared,
+                       w3_shared, w2_shared, y_routed, y_shared, ws, ws_bytes, &L, &routed, &shared);
+    if (rc != MOE_OK) return rc;
+    if (!routed && !shared) return MOE_OK;
+    const FfnArgs a = ffn_args(x, offsets, sorted_token, w1_routed, w3_routed, w2_routed, w1_shared, w3_shared,
+                               w2_shared, y_routed, y_shared, ws, L);
+    const moe_problem q = active_part(*p, routed, shared);
+    hipError_t e = launch_expert_up(q, a, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_expert_down(q, a, (hipStream_t)stream);
+    return hip_status(e);
 }
 
 int moe_combine(const moe_problem *p, const void *x, const void *y_routed, const float *y_shared,

@@ -279,48 +279,52 @@ __global__ __launch_bounds__(256) void grouped_ffn_kernel(GemmParams P) {
     }
 }
 
-template <typename DT>
-hipError_t launch_typed(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
-    const int T = p.T, Ks = p.n_shared, Nr = p.n_routed, w = p.inter, d = p.d;
-    const int rt_bound = (int)(((int64_t)T * p.top_k) / BM) + Nr;  // >= sum_r ceil(c_r / BM)
-    const int mts = Ks > 0 ? cdiv(T, BM) : 0;
-
+GemmParams make_params(const moe_problem &p, const FfnArgs &a, bool up) {
     GemmParams P{};
-    P.T = T; P.d = d; P.Ks = Ks; P.Nr = Nr; P.w = w;
+    P.T = p.T; P.d = p.d; P.Ks = p.n_shared; P.Nr = p.n_routed; P.w = p.inter;
     P.offsets = a.offsets;
     P.sorted_token = a.sorted_token;
     P.x = (const uint8_t *)a.x;
     P.act_shared = (const uint8_t *)a.act_shared;
     P.act_routed = (const uint8_t *)a.act_routed;
+    if (up) {
+        P.wa_r = (const uint8_t *)a.w1_r; P.wb_r = (const uint8_t *)a.w3_r;
+        P.wa_s = (const uint8_t *)a.w1_s; P.wb_s = (const uint8_t *)a.w3_s;
+        P.out_shared = (uint8_t *)a.act_shared; P.out_routed = (uint8_t *)a.act_routed;
+    } else {
+        P.wa_r = (const uint8_t *)a.w2_r; P.wb_r = nullptr;
+        P.wa_s = (const uint8_t *)a.w2_s; P.wb_s = nullptr;
+        P.out_shared = (uint8_t *)a.y_shared; P.out_routed = (uint8_t *)a.y_routed;
+    }
+    return P;
+}
 
-    // up projection + SwiGLU
-    P.wa_r = (const uint8_t *)a.w1_r; P.wb_r = (const uint8_t *)a.w3_r;
-    P.wa_s = (const uint8_t *)a.w1_s; P.wb_s = (const uint8_t *)a.w3_s;
-    P.out_shared = (uint8_t *)a.act_shared; P.out_routed = (uint8_t *)a.act_routed;
-    const int up_tiles = mts * (Ks * w / 64) + (Nr > 0 ? rt_bound * (w / 64) : 0);
-    if (up_tiles > 0) {
-        grouped_ffn_kernel<DT, true><<<up_tiles, 256, 0, s>>>(P);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    // down projection
-    P.wa_r = (const uint8_t *)a.w2_r; P.wb_r = nullptr;
-    P.wa_s = (const uint8_t *)a.w2_s; P.wb_s = nullptr;
-    P.out_shared = (uint8_t *)a.y_shared; P.out_routed = (uint8_t *)a.y_routed;
-    const int dn_tiles = mts * cdiv(d, BN) + (Nr > 0 ? rt_bound * cdiv(d, BN) : 0);
-    if (dn_tiles > 0) {
-        grouped_ffn_kernel<DT, false><<<dn_tiles, 256, 0, s>>>(P);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+// Upper bound of the tile count: sum_r ceil(c_r / BM) <= floor(T K' / BM) + N'.
+int tile_bound(const moe_problem &p, bool up) {
+    const int rt_bound = (int)(((int64_t)p.T * p.top_k) / BM) + p.n_routed;
+    const int mts = p.n_shared > 0 ? cdiv(p.T, BM) : 0;
+    if (up) return mts * (p.n_shared * p.inter / 64) + (p.n_routed > 0 ? rt_bound * (p.inter / 64) : 0);
+    return mts * cdiv(p.d, BN) + (p.n_routed > 0 ? rt_bound * cdiv(p.d, BN) : 0);
+}
+
+template <typename DT, bool UP>
+hipError_t launch_typed(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
+    const int tiles = tile_bound(p, UP);
+    if (tiles == 0) return hipSuccess;
+    grouped_ffn_kernel<DT, UP><<<tiles, 256, 0, s>>>(make_params(p, a, UP));
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
-    if (p.dtype == MOE_BF16) return launch_typed<uint16_t>(p, a, s);
-    return launch_typed<float>(p, a, s);
+hipError_t launch_expert_up(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
+    if (p.dtype == MOE_BF16) return launch_typed<uint16_t, true>(p, a, s);
+    return launch_typed<float, true>(p, a, s);
+}
+
+hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
+    if (p.dtype == MOE_BF16) return launch_typed<uint16_t, false>(p, a, s);
+    return launch_typed<float, false>(p, a, s);
 }
 
 }  // namespace moe

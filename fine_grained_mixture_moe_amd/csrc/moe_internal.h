@@ -80,7 +80,9 @@ struct FfnArgs {
     float *y_shared;
 };
 
-hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, hipStream_t s);
+// up: act = SiLU(X W1^T) * (X W3^T) into the workspace; down: y = act W2^T.
+hipError_t launch_expert_up(const moe_problem &p, const FfnArgs &a, hipStream_t s);
+hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_t s);
 
 hipError_t launch_combine(const moe_problem &p, const void *x, const void *y_routed,
                           const float *y_shared, const float *gate, const int32_t *slot_of,

@@ -103,6 +103,14 @@ class DeviceLayer:
                          self.w1_s, self.w3_s, self.w2_s, self.y_routed, self.y_shared, self.ws, self.ws_bytes,
                          stream)
 
+    def expert_up(self, stream=None):
+        M.moe_expert_up(self.prob, self.x, self.offsets, self.sorted_token, self.w1_r, self.w3_r, self.w1_s,
+                        self.w3_s, self.ws, self.ws_bytes, stream)
+
+    def expert_down(self, stream=None):
+        M.moe_expert_down(self.prob, self.offsets, self.w2_r, self.w2_s, self.y_routed, self.y_shared, self.ws,
+                          self.ws_bytes, stream)
+
     def combine(self, stream=None):
         M.moe_combine(self.prob, self.x, self.y_routed, self.y_shared, self.gate, self.slot_of, self.h, stream)
 

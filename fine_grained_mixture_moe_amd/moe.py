@@ -60,10 +60,12 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_permute.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_expert_ffn.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_expert_up.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_expert_down.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_combine.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_balance_stats.argtypes = [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-        for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-                   "moe_balance_stats"):
+        for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up",
+                   "moe_expert_down", "moe_combine", "moe_balance_stats"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -119,6 +121,19 @@ def moe_expert_ffn(p, x, offsets, sorted_token, w1_routed, w3_routed, w2_routed,
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         ctypes.byref(p), _ptr(x), _ptr(offsets), _ptr(sorted_token), _ptr(w1_routed), _ptr(w3_routed),
         _ptr(w2_routed), _ptr(w1_shared), _ptr(w3_shared), _ptr(w2_shared), _ptr(y_routed), _ptr(y_shared),
+        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_expert_up(p, x, offsets, sorted_token, w1_routed, w3_routed, w1_shared, w3_shared, ws, ws_bytes,
+                  stream=None):
+    _check("moe_expert_up", lib().moe_expert_up(
+        ctypes.byref(p), _ptr(x), _ptr(offsets), _ptr(sorted_token), _ptr(w1_routed), _ptr(w3_routed),
+        _ptr(w1_shared), _ptr(w3_shared), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_expert_down(p, offsets, w2_routed, w2_shared, y_routed, y_shared, ws, ws_bytes, stream=None):
+    _check("moe_expert_down", lib().moe_expert_down(
+        ctypes.byref(p), _ptr(offsets), _ptr(w2_routed), _ptr(w2_shared), _ptr(y_routed), _ptr(y_shared),
         _ptr(ws), ws_bytes, _stream(stream)))
 
 

@@ -160,6 +160,24 @@ int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets,
                    void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_expert_up / moe_expert_down -- the two halves of moe_expert_ffn, for
+ * callers that schedule or time them separately.  moe_expert_up computes the
+ * SwiGLU activations act = SiLU(W1 u) * (W3 u) (rounded to dtype) of every
+ * shared row and grouped routed row into the workspace; moe_expert_down
+ * reads them from the same workspace (same problem, same ws, same stream, in
+ * that order) and writes y_routed and y_shared exactly as moe_expert_ffn
+ * does.  Arguments have the meanings given above.
+ */
+int moe_expert_up(const moe_problem *p, const void *x, const int32_t *offsets,
+                  const int32_t *sorted_token, const void *w1_routed,
+                  const void *w3_routed, const void *w1_shared,
+                  const void *w3_shared, void *ws, size_t ws_bytes, void *stream);
+
+int moe_expert_down(const moe_problem *p, const int32_t *offsets,
+                    const void *w2_routed, const void *w2_shared, void *y_routed,
+                    float *y_shared, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * moe_combine -- layer output, "[ACL 2024] DeepSeekMoE ..." section "Method
  * details" (output formula):
  *   h_t = u_t + y_shared_t + sum_{k < K'} gate[t,k] * y_routed[slot_of[t,k]]
