@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int K, const
 }
 
 // One workgroup.  f and f' are exact functions of integer counts (fp64
-// quotient rounded once to fp32); the sums run in fp64 in index order.
+// quotient rounded once to fp32); ExpBal and DevBal are fp64 sums over a
+// fixed tree (deterministic).
 __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K, int D,
                                                             const int32_t *__restrict__ counts,
                                                             const float *__restrict__ prob_sum,
@@ -114,13 +115,20 @@ __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K
         P_dev[g] = pf;
         s_gp[g] = (double)ff * (double)pf;
     }
+    for (int r = Nr + threadIdx.x; r < kPermuteMaxExperts; r += 256) s_fp[r] = 0.0;
+    for (int g = D + threadIdx.x; g < kPermuteMaxExperts; g += 256) s_gp[g] = 0.0;
     __syncthreads();
+    // fixed-order tree sums over the (zero-padded) 1024 slots
+    for (int o = kPermuteMaxExperts / 2; o > 0; o >>= 1) {
+        for (int i = threadIdx.x; i < o; i += 256) {
+            s_fp[i] += s_fp[i + o];
+            s_gp[i] += s_gp[i + o];
+        }
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
-        double eb = 0.0, db = 0.0;
-        for (int r = 0; r < Nr; ++r) eb += s_fp[r];
-        for (int g = 0; g < D; ++g) db += s_gp[g];
-        *exp_bal = (float)eb;
-        *dev_bal = (float)db;
+        *exp_bal = (float)s_fp[0];
+        *dev_bal = (float)s_gp[0];
     }
 }
 

@@ -24,6 +24,8 @@
 // Every workgroup derives its (group, row-tile, column-tile) from the
 // device-side offsets, so no host round trip sizes the grid: the grid is an
 // upper bound and surplus workgroups exit at once.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -279,6 +281,301 @@ __global__ __launch_bounds__(256) void grouped_ffn_kernel(GemmParams P) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path: 256 weight rows x BM tokens per tile, 64 k per step.
+//
+// LDS rows are 128 bytes (64 bf16) with no padding; the 16-byte chunk c of
+// row r lives at chunk c ^ (r & 7), so the 32 rows a fragment read touches
+// spread over all banks.  Two LDS stages: while the MFMAs consume stage s,
+// the registers already hold the next k step (issued one step earlier) and
+// are written to stage s^1 afterwards; one barrier per k step.  Global reads
+// are raw buffer loads: per-thread 32-bit row offsets are fixed for the
+// whole k loop and the k position is a scalar offset; rows outside the
+// group read as zero (range-checked loads), so no masking is needed.
+// 8 waves (2 per SIMD, so one wave's LDS and memory latency hides behind
+// the other's MFMAs), laid out 2 (tokens) x 4 (weights): a wave owns 64
+// weight rows (2 blocks of 32) x BM/2 tokens (BM/64 blocks of 32).  In the
+// up projection the wave's two weight blocks are the W1 rows and the W3 rows
+// of the same 32 intermediate units, so the SwiGLU pairs up in registers.
+// ---------------------------------------------------------------------------
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;   // offset beyond any buffer: reads as zero
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int BM, bool UP>
+__global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
+    constexpr int NT = 512;          // threads: 8 waves, 2 per SIMD
+    constexpr int BN = 256;          // weight rows per tile
+    constexpr int RB = 128;          // LDS row bytes
+    constexpr int MB = BM / 64;      // 32-token blocks per wave
+    constexpr int NB = 2;            // 32-row weight blocks per wave
+    constexpr int CW = BN * 8 / NT;  // weight chunks per thread (4)
+    constexpr int CX = BM * 8 / NT;  // token chunks per thread (4 or 2)
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[2][BN * RB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * RB];
+    __shared__ int s_pref[MAXG + 1];
+    __shared__ int s_src[BM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = (P.Ks > 0 ? 1 : 0) + P.Nr;
+    const int ntn_s = UP ? cdiv(P.Ks * P.w, 128) : cdiv(P.d, BN);
+    const int ntn_r = UP ? cdiv(P.w, 128) : cdiv(P.d, BN);
+
+    if (wave == 0) {
+        int carry = 0;
+        if (lane == 0) s_pref[0] = 0;
+        for (int g0 = 0; g0 < G; g0 += 64) {
+            const int g = g0 + lane;
+            int tiles = 0;
+            if (g < G) {
+                const bool sh = P.Ks > 0 && g == 0;
+                const int r = g - (P.Ks > 0 ? 1 : 0);
+                const int rows = sh ? P.T : P.offsets[r + 1] - P.offsets[r];
+                tiles = cdiv(rows, BM) * (sh ? ntn_s : ntn_r);
+            }
+            int incl = tiles;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += v;
+            }
+            if (g < G) s_pref[g + 1] = carry + incl;
+            carry += __shfl(incl, 63, 64);
+        }
+    }
+    __syncthreads();
+    const int total = s_pref[G];
+    const int bid = blockIdx.x;
+    if (bid >= total) return;
+    // Renumbering: workgroups reach the 8 XCDs round-robin, so within each run
+    // of 256 workgroups XCD x gets the 32 consecutive tiles [32x, 32x+32) of
+    // that run (they are co-resident there and share operands in its L2);
+    // runs follow each other in tile order, which keeps the XCDs balanced.
+    // The tail run (< 256 tiles) keeps the identity order.
+    const int L = (bid < (total & ~255)) ? ((bid & ~255) + (bid & 7) * 32 + ((bid >> 3) & 31)) : bid;
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= L) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const bool shared = P.Ks > 0 && g == 0;
+    const int r = g - (P.Ks > 0 ? 1 : 0);
+    const int row_off = shared ? 0 : P.offsets[r];
+    const int rows = shared ? P.T : P.offsets[r + 1] - row_off;
+    const int mt = cdiv(rows, BM);
+    const int lt = L - s_pref[g];
+    const int m_tile = lt % mt, n_tile = lt / mt;
+    const int m0 = m_tile * BM;
+
+    const int K = UP ? P.d : (shared ? P.Ks * P.w : P.w);
+    const uint32_t xpitch = (uint32_t)K * 2u;   // token-side row bytes
+    if (tid < BM) {
+        const int row = m0 + tid;
+        int src = -1;
+        if (row < rows) {
+            if (UP) src = shared ? row : P.sorted_token[row_off + row];
+            else src = row_off + row;
+        }
+        s_src[tid] = src;
+    }
+    __syncthreads();
+
+    // ---- buffer resources and fixed per-thread offsets ----
+    const int part = tid & 7;               // logical 16-byte chunk of the row
+    const int rsub = tid >> 3;              // row within a group of 64
+    __amdgpu_buffer_rsrc_t rw_a, rw_b, rx;
+    uint32_t ow[CW], ox[CX];
+    int n_valid;                            // weight-side rows of this group
+    uint32_t wpitch;
+    if (UP) {
+        const size_t ebytes = (size_t)P.w * P.d * 2;
+        const uint8_t *b1 = shared ? P.wa_s : P.wa_r + (size_t)r * ebytes;
+        const uint8_t *b3 = shared ? P.wb_s : P.wb_r + (size_t)r * ebytes;
+        n_valid = shared ? P.Ks * P.w : P.w;
+        wpitch = (uint32_t)P.d * 2u;
+        rw_a = make_rsrc(b1, (uint32_t)((size_t)n_valid * wpitch));
+        rw_b = make_rsrc(b3, (uint32_t)((size_t)n_valid * wpitch));
+        rx = make_rsrc(P.x, (uint32_t)((size_t)P.T * P.d * 2));
+    } else {
+        const size_t ebytes = (size_t)P.d * P.w * 2;
+        const uint8_t *b2 = shared ? P.wa_s : P.wa_r + (size_t)r * ebytes;
+        n_valid = P.d;
+        wpitch = (uint32_t)P.w * 2u;
+        rw_a = make_rsrc(b2, (uint32_t)(shared ? (size_t)P.Ks * ebytes : ebytes));
+        rw_b = rw_a;
+        const uint8_t *xb = shared ? P.act_shared : P.act_routed;
+        const size_t xrows = shared ? (size_t)P.T : (size_t)(P.offsets[P.Nr]);
+        rx = make_rsrc(xb, (uint32_t)(xrows * xpitch));
+    }
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+        const int j = rsub + 64 * i;                     // tile row 0..255
+        int wr;
+        if (UP) wr = n_tile * 128 + (j & 127);           // W1 (j < 128) or W3 row
+        else wr = n_tile * BN + j;                       // W2 row = output column
+        ow[i] = wr < n_valid ? (uint32_t)wr * wpitch + part * 16 : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < CX; ++i) {
+        const int src = s_src[rsub + 64 * i];
+        ox[i] = src >= 0 ? (uint32_t)src * xpitch + part * 16 : kOOB;
+    }
+    // physical chunk of logical chunk c in row r: c ^ (r & 7) ^ ((r >> 3) & 1).
+    // Any 8 consecutive rows, and any 16 consecutive rows split by parity,
+    // land on distinct 16-byte bank groups.
+    const int swz = part ^ (rsub & 7) ^ ((rsub >> 3) & 1);
+
+    uint4 sw[CW], sx[CX];
+    auto kw_of = [&](int kt) -> uint32_t {
+        if (!UP && shared) {
+            // W2 of the shared experts: k runs over K_s segments [d, w]
+            const int k_el = kt * 64;
+            const int seg = k_el / P.w;
+            return (uint32_t)(((size_t)seg * P.d * P.w + (k_el - seg * P.w)) * 2);
+        }
+        return (uint32_t)kt * RB;
+    };
+    // part ph (0..3) of a k step: weight chunks [ph*CW/4, (ph+1)*CW/4), token chunks likewise
+    auto gload_part = [&](int kt, int ph) {
+        const uint32_t kw = kw_of(kt), kx = (uint32_t)kt * RB;
+#pragma unroll
+        for (int i = 0; i < CW; ++i)
+            if (i * 4 / CW == ph) sw[i] = bload((UP && i >= CW / 2) ? rw_b : rw_a, ow[i], kw);
+#pragma unroll
+        for (int i = 0; i < CX; ++i)
+            if (i * 4 / CX == ph) sx[i] = bload(rx, ox[i], kx);
+    };
+    auto sstore_part = [&](int stg, int ph) {
+#pragma unroll
+        for (int i = 0; i < CW; ++i)
+            if (i * 4 / CW == ph) *(uint4 *)(s_w[stg] + (rsub + 64 * i) * RB + swz * 16) = sw[i];
+#pragma unroll
+        for (int i = 0; i < CX; ++i)
+            if (i * 4 / CX == ph) *(uint4 *)(s_x[stg] + (rsub + 64 * i) * RB + swz * 16) = sx[i];
+    };
+
+    f32x16 acc[NB][MB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    int wrow[NB], xrow[MB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        wrow[nb] = UP ? (nb * 128 + wn * 32 + l32) : (wn * 64 + nb * 32 + l32);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) xrow[mb] = wm * (BM / 2) + mb * 32 + l32;
+    const int lsw = (l32 & 7) ^ ((l32 >> 3) & 1);   // swizzle of every fragment row of this lane
+
+    auto frags = [&](int stg, int ks, bf16x8 (&fa)[NB], bf16x8 (&fb)[MB]) {
+        const int ch = ((2 * ks + lhi) ^ lsw) * 16;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) fa[nb] = *(const bf16x8 *)(s_w[stg] + wrow[nb] * RB + ch);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) fb[mb] = *(const bf16x8 *)(s_x[stg] + xrow[mb] * RB + ch);
+    };
+    auto mma = [&](const bf16x8 (&fa)[NB], const bf16x8 (&fb)[MB]) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[nb], fb[mb], acc[nb][mb], 0, 0, 0);
+    };
+
+    // Pipeline: stage kt&1 holds k step kt; the registers hold step kt+1.
+    // During the 4 sub-steps of step kt, quarter ph of the registers is
+    // written to the other stage and refilled with step kt+2, between MFMAs.
+    const int nk = K / 64;
+#pragma unroll
+    for (int ph = 0; ph < 4; ++ph) gload_part(0, ph);
+#pragma unroll
+    for (int ph = 0; ph < 4; ++ph) sstore_part(0, ph);
+    __syncthreads();
+    if (nk > 1)
+#pragma unroll
+        for (int ph = 0; ph < 4; ++ph) gload_part(1, ph);
+    // one k step; MORE: step kt+1 exists (store it), MORE2: step kt+2 exists (load it)
+    auto kstep = [&](int kt, auto more_t, auto more2_t) {
+        constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
+        const int st = kt & 1;
+        bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
+        frags(st, 0, fa0, fb0);
+        frags(st, 1, fa1, fb1);
+        if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kt + 2, 0); }
+        __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
+        mma(fa0, fb0);
+        frags(st, 2, fa0, fb0);
+        if (MORE) { sstore_part(st ^ 1, 1); if (MORE2) gload_part(kt + 2, 1); }
+        __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
+        mma(fa1, fb1);
+        frags(st, 3, fa1, fb1);
+        if (MORE) { sstore_part(st ^ 1, 2); if (MORE2) gload_part(kt + 2, 2); }
+        __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
+        mma(fa0, fb0);
+        if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kt + 2, 3); }
+        __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
+        mma(fa1, fb1);
+        __syncthreads();
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) kstep(kt, yes{}, yes{});
+    if (kt + 1 < nk) kstep(kt++, yes{}, no{});
+    kstep(kt, no{}, no{});
+
+    // ---- epilogue: lane owns token column l32 of each block; register quad q
+    //      holds weight rows 8q + 4*lhi + {0..3} of the block ----
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int row = m0 + xrow[mb];
+        if (row >= rows) continue;
+        if (UP) {
+            const int ld = shared ? P.Ks * P.w : P.w;
+            uint16_t *dst = (uint16_t *)(shared ? P.out_shared : P.out_routed) + (size_t)(row_off + row) * ld;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n_tile * 128 + wn * 32 + 8 * q + 4 * lhi;
+                if (col >= ld) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pg = acc[0][mb][4 * q + e];
+                    const float pu = acc[1][mb][4 * q + e];
+                    v[e] = pg / (1.0f + __expf(-pg)) * pu;
+                }
+                store4(dst + col, v);
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = n_tile * BN + wn * 64 + nb * 32 + 8 * q + 4 * lhi;
+                    if (col >= P.d) continue;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][4 * q + e];
+                    if (shared) store4((float *)P.out_shared + (size_t)row * P.d + col, v);
+                    else store4((uint16_t *)P.out_routed + (size_t)(row_off + row) * P.d + col, v);
+                }
+        }
+    }
+}
+
 GemmParams make_params(const moe_problem &p, const FfnArgs &a, bool up) {
     GemmParams P{};
     P.T = p.T; P.d = p.d; P.Ks = p.n_shared; P.Nr = p.n_routed; P.w = p.inter;
@@ -299,31 +596,50 @@ GemmParams make_params(const moe_problem &p, const FfnArgs &a, bool up) {
     return P;
 }
 
-// Upper bound of the tile count: sum_r ceil(c_r / BM) <= floor(T K' / BM) + N'.
-int tile_bound(const moe_problem &p, bool up) {
-    const int rt_bound = (int)(((int64_t)p.T * p.top_k) / BM) + p.n_routed;
-    const int mts = p.n_shared > 0 ? cdiv(p.T, BM) : 0;
-    if (up) return mts * (p.n_shared * p.inter / 64) + (p.n_routed > 0 ? rt_bound * (p.inter / 64) : 0);
-    return mts * cdiv(p.d, BN) + (p.n_routed > 0 ? rt_bound * cdiv(p.d, BN) : 0);
+// Upper bound of the tile count for token tiles of bm rows and weight
+// tiles of `wn` rows (act columns in the up projection):
+// sum_r ceil(c_r / bm) <= floor(T K' / bm) + N'.
+int tile_bound(const moe_problem &p, bool up, int bm, int wn_up, int wn_down) {
+    const int rt_bound = (int)(((int64_t)p.T * p.top_k) / bm) + p.n_routed;
+    const int mts = p.n_shared > 0 ? cdiv(p.T, bm) : 0;
+    if (up) return mts * cdiv(p.n_shared * p.inter, wn_up) + (p.n_routed > 0 ? rt_bound * cdiv(p.inter, wn_up) : 0);
+    return mts * cdiv(p.d, wn_down) + (p.n_routed > 0 ? rt_bound * cdiv(p.d, wn_down) : 0);
 }
 
 template <typename DT, bool UP>
 hipError_t launch_typed(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
-    const int tiles = tile_bound(p, UP);
+    const int tiles = tile_bound(p, UP, BM, 64, BN);
     if (tiles == 0) return hipSuccess;
     grouped_ffn_kernel<DT, UP><<<tiles, 256, 0, s>>>(make_params(p, a, UP));
+    return hipGetLastError();
+}
+
+// Token tile of the bf16 path: 256 rows when the routed experts average at
+// least 768 rows (edge waste <= 1/6), else 128.
+template <bool UP>
+hipError_t launch_bf16(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
+    const int64_t avg = p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / p.n_routed : (int64_t)p.T;
+    if (avg >= 768) {
+        const int tiles = tile_bound(p, UP, 256, 128, 256);
+        if (tiles == 0) return hipSuccess;
+        grouped_ffn_bf16_kernel<256, UP><<<tiles, 512, 0, s>>>(make_params(p, a, UP));
+    } else {
+        const int tiles = tile_bound(p, UP, 128, 128, 256);
+        if (tiles == 0) return hipSuccess;
+        grouped_ffn_bf16_kernel<128, UP><<<tiles, 512, 0, s>>>(make_params(p, a, UP));
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_expert_up(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
-    if (p.dtype == MOE_BF16) return launch_typed<uint16_t, true>(p, a, s);
+    if (p.dtype == MOE_BF16) return launch_bf16<true>(p, a, s);
     return launch_typed<float, true>(p, a, s);
 }
 
 hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
-    if (p.dtype == MOE_BF16) return launch_typed<uint16_t, false>(p, a, s);
+    if (p.dtype == MOE_BF16) return launch_bf16<false>(p, a, s);
     return launch_typed<float, false>(p, a, s);
 }
 

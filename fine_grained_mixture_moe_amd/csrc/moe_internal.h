@@ -14,8 +14,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Tokens handled by one routing workgroup.
-constexpr int kRouteTokens = 64;
 // Tokens handled by one grouping (permute) workgroup.
 constexpr int kPermuteTokens = 256;
 // Largest N' the routing kernel supports, and K' bound.
@@ -40,10 +38,13 @@ struct WsLayout {
     size_t total;
 };
 
+// Routing workgroups for T tokens (route.hip).
+int route_blocks(int T);
+
 inline WsLayout ws_layout(const moe_problem &p) {
     WsLayout L{};
     const size_t nr = (size_t)p.n_routed;
-    const size_t rb = (size_t)cdiv(p.T, kRouteTokens);
+    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T) : 0;
     const size_t pb = (size_t)cdiv(p.T, kPermuteTokens);
     const size_t es = dtype_bytes(p.dtype);
     size_t off = 0;

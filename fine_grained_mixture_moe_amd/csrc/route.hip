@@ -57,137 +57,160 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
-// NRP: N' padded to a multiple of 64 (64, 128 or 256).
-template <int NRP>
+// One wave owns RT tokens and all N' experts: lane l holds experts l + 64 j
+// (j < NJ).  Every (token, expert) logit is one fma chain over k ascending.
+// The four waves of a workgroup share each KC-wide chunk of the centroids and
+// of their 4*RT token rows through LDS (fp32, double-buffered, one barrier
+// per chunk; row pitch KC+4 floats keeps the 16-byte centroid reads of 16
+// consecutive lanes on distinct banks; token reads are wave-uniform
+// broadcasts).  After the chain the wave holds every logit of its tokens in
+// registers: softmax and Top-K' need no LDS round trip.
+template <int RT, int NJ, int KC>
 __global__ __launch_bounds__(256) void route_kernel(
     int T, int d, int Nr, int K, const void *__restrict__ x, int x_bf16,
     const float *__restrict__ E, const float *__restrict__ bias, int32_t *__restrict__ idx,
     float *__restrict__ gate, float *__restrict__ probs, int32_t *__restrict__ part_counts,
     double *__restrict__ part_psum) {
-    constexpr int TB = kRouteTokens;      // 64 tokens
-    constexpr int EG = NRP / 4;           // expert groups of 4 consecutive experts
-    constexpr int TG = 256 / EG;          // token groups
-    constexpr int RT = TB / TG;           // tokens per thread
-    constexpr int NJ = NRP / 64;          // experts per lane in the selection phase
-
-    __shared__ float xs[KC][TB];
-    __shared__ __attribute__((aligned(16))) float es[KC][NRP];
-    __shared__ float zs[TB][NRP + 1];
-    __shared__ int cnt[NRP];
+    constexpr int NE = NJ * 64;            // expert rows covered by a wave
+    constexpr int TB = 4 * RT;             // tokens of the workgroup
+    constexpr int PITCH = KC + 4;          // LDS row pitch (floats)
+    constexpr int NL = NE * KC / 4 / 256;  // centroid float4 staged per thread per chunk
+    constexpr int NX = TB * KC / 8;        // threads staging 8 token values each
+    static_assert(NL >= 1 && NX <= 256, "chunk shape");
+    __shared__ __attribute__((aligned(16))) float s_e[2][NE * PITCH];
+    __shared__ __attribute__((aligned(16))) float s_x[2][TB * PITCH];
+    __shared__ double s_ps[4][NE];
+    __shared__ int s_cnt[4][NE];
 
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * TB;
-    const int eg = tid % EG, tg = tid / EG;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int tb0 = blockIdx.x * TB;
+    const int t0 = tb0 + wave * RT;
 
-    float acc[RT][4];
+    bool ev[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) ev[j] = lane + 64 * j < Nr;
+
+    float acc[RT][NJ];
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+        for (int j = 0; j < NJ; ++j) acc[i][j] = 0.0f;
 
-    for (int k0 = 0; k0 < d; k0 += KC) {
-        // x chunk [TB x KC] -> xs[k][t]; 8 consecutive k of one token per thread
-        {
-            const int tt = tid >> 2, kk = (tid & 3) * 8;
-            const int t = t0 + tt;
-            float v[8];
-            if (t >= T) {
+    // staging registers: centroid float4s, and 8 token values (thread < NX)
+    float4 stage[NL];
+    float xst[8];
+    const int xt = tid / (KC / 8), xk = (tid % (KC / 8)) * 8;   // token row / k offset staged by this thread
+    const size_t xrow = (size_t)min(tb0 + xt, T - 1) * d;
+    auto gload = [&](int k0) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-            } else if (x_bf16) {
-                const uint4 q = *(const uint4 *)((const uint16_t *)x + (size_t)t * d + k0 + kk);
-                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        for (int q = 0; q < NL; ++q) {
+            const int c = tid + 256 * q;
+            const int row = c / (KC / 4), c4 = c % (KC / 4);
+            stage[q] = row < Nr ? *(const float4 *)(E + (size_t)row * d + k0 + 4 * c4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (tid < NX) {
+            if (x_bf16) {
+                const uint4 w = *(const uint4 *)((const uint16_t *)x + xrow + k0 + xk);
+                const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[2 * j] = __uint_as_float(w[j] << 16);
-                    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                for (int h = 0; h < 4; ++h) {
+                    xst[2 * h] = __uint_as_float(wv[h] << 16);
+                    xst[2 * h + 1] = __uint_as_float(wv[h] & 0xffff0000u);
                 }
             } else {
-                const float4 a = *(const float4 *)((const float *)x + (size_t)t * d + k0 + kk);
-                const float4 b = *(const float4 *)((const float *)x + (size_t)t * d + k0 + kk + 4);
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xs[kk + j][tt] = v[j];
-        }
-        // E chunk [NRP x KC] -> es[k][r]
-        for (int c = tid; c < NRP * (KC / 4); c += 256) {
-            const int r = c / (KC / 4), kq = (c % (KC / 4)) * 4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r < Nr) v = *(const float4 *)(E + (size_t)r * d + k0 + kq);
-            es[kq + 0][r] = v.x;
-            es[kq + 1][r] = v.y;
-            es[kq + 2][r] = v.z;
-            es[kq + 3][r] = v.w;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int k = 0; k < KC; ++k) {
-            const float4 ev = *(const float4 *)&es[k][eg * 4];
-#pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                const float xv = xs[k][tg + i * TG];
-                acc[i][0] = __builtin_fmaf(xv, ev.x, acc[i][0]);
-                acc[i][1] = __builtin_fmaf(xv, ev.y, acc[i][1]);
-                acc[i][2] = __builtin_fmaf(xv, ev.z, acc[i][2]);
-                acc[i][3] = __builtin_fmaf(xv, ev.w, acc[i][3]);
+                const float4 a = *(const float4 *)((const float *)x + xrow + k0 + xk);
+                const float4 b = *(const float4 *)((const float *)x + xrow + k0 + xk + 4);
+                xst[0] = a.x; xst[1] = a.y; xst[2] = a.z; xst[3] = a.w;
+                xst[4] = b.x; xst[5] = b.y; xst[6] = b.z; xst[7] = b.w;
             }
         }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < NL; ++q) {
+            const int c = tid + 256 * q;
+            const int row = c / (KC / 4), c4 = c % (KC / 4);
+            *(float4 *)&s_e[buf][row * PITCH + 4 * c4] = stage[q];
+        }
+        if (tid < NX) {
+            *(float4 *)&s_x[buf][xt * PITCH + xk] = make_float4(xst[0], xst[1], xst[2], xst[3]);
+            *(float4 *)&s_x[buf][xt * PITCH + xk + 4] = make_float4(xst[4], xst[5], xst[6], xst[7]);
+        }
+    };
+
+    const int nchunk = d / KC;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kc = 0; kc < nchunk; ++kc) {
+        const int buf = kc & 1;
+        if (kc + 1 < nchunk) gload((kc + 1) * KC);
+        if (t0 < T) {
+#pragma unroll
+            for (int v = 0; v < KC / 4; ++v) {
+                float4 e4[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) e4[j] = *(const float4 *)&s_e[buf][(lane + 64 * j) * PITCH + 4 * v];
+#pragma unroll
+                for (int i = 0; i < RT; ++i) {
+                    const float4 x4 = *(const float4 *)&s_x[buf][(wave * RT + i) * PITCH + 4 * v];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        acc[i][j] = __builtin_fmaf(x4.x, e4[j].x, acc[i][j]);
+                        acc[i][j] = __builtin_fmaf(x4.y, e4[j].y, acc[i][j]);
+                        acc[i][j] = __builtin_fmaf(x4.z, e4[j].z, acc[i][j]);
+                        acc[i][j] = __builtin_fmaf(x4.w, e4[j].w, acc[i][j]);
+                    }
+                }
+            }
+        }
+        if (kc + 1 < nchunk) sstore(buf ^ 1);
         __syncthreads();
     }
 
+    double ps[NJ];
+    int cnt[NJ];
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = eg * 4 + j;
-            float z = acc[i][j];
-            if (bias && r < Nr) z = z + bias[r];
-            zs[tg + i * TG][r] = z;
-        }
-    for (int r = tid; r < NRP; r += 256) cnt[r] = 0;
-    __syncthreads();
+    for (int j = 0; j < NJ; ++j) { ps[j] = 0.0; cnt[j] = 0; }
 
-    // ---- per-token softmax + Top-K' (one wave per token) ----
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int tt = wave; tt < TB; tt += 4) {
-        const int t = t0 + tt;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const int t = t0 + i;
         if (t >= T) break;
-        float z[NJ], e[NJ];
-        bool valid[NJ];
+        float z[NJ], e[NJ], s[NJ];
         float m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int r = lane + 64 * j;
-            valid[j] = r < Nr;
-            z[j] = zs[tt][r];
-            if (valid[j]) m = fmaxf(m, z[j]);
+            z[j] = acc[i][j];
+            if (bias && ev[j]) z[j] = z[j] + bias[lane + 64 * j];
+            if (ev[j]) m = fmaxf(m, z[j]);
         }
         m = wave_max(m);
         float sum = 0.0f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            e[j] = valid[j] ? expf(z[j] - m) : 0.0f;
+            e[j] = ev[j] ? expf(z[j] - m) : 0.0f;
             sum += e[j];
         }
         sum = wave_sum(sum);
         const float inv = 1.0f / sum;
-        float s[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             s[j] = e[j] * inv;
-            const int r = lane + 64 * j;
-            if (valid[j] && probs) probs[(size_t)t * Nr + r] = s[j];
+            ps[j] += (double)s[j];
+            if (ev[j] && probs) probs[(size_t)t * Nr + lane + 64 * j] = s[j];
         }
-        // Top-K' by repeated wave argmax.  key = (ordered z) << 32 | ~r.
+        // Top-K' by repeated wave argmax on key = (ordered z) << 32 | ~r
         uint32_t taken = 0;
         for (int k = 0; k < K; ++k) {
             uint64_t best = 0;  // below every real key (ordered keys of finite z are > 0)
             float best_s = 0.0f;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                if (!valid[j] || (taken >> j & 1u)) continue;
+                if (!ev[j] || (taken >> j & 1u)) continue;
                 const uint32_t r = (uint32_t)(lane + 64 * j);
                 const uint64_t key = ((uint64_t)ordered_key(z[j]) << 32) | (uint32_t)(~r);
                 if (key > best) { best = key; best_s = s[j]; }
@@ -196,68 +219,106 @@ __global__ __launch_bounds__(256) void route_kernel(
             const int r = (int)(~(uint32_t)win);
             const int owner = r & 63;
             const float g = __shfl(best_s, owner, 64);
-            if (lane == owner) taken |= 1u << (r >> 6);
+            if (lane == owner) {
+                taken |= 1u << (r >> 6);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) cnt[j] += (j == (r >> 6)) ? 1 : 0;
+            }
             if (lane == 0) {
                 idx[(size_t)t * K + k] = r;
                 gate[(size_t)t * K + k] = g;
-                atomicAdd(&cnt[r], 1);  // integer: order-independent result
             }
         }
-        // keep s for the per-block affinity sums
+    }
+
+    // per-workgroup partial statistics, waves combined in order
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) zs[tt][lane + 64 * j] = s[j];
+    for (int j = 0; j < NJ; ++j) {
+        s_ps[wave][lane + 64 * j] = ps[j];
+        s_cnt[wave][lane + 64 * j] = cnt[j];
     }
     __syncthreads();
-
-    // ---- per-block partial statistics (tokens in order, fp64) ----
-    const int nt = min(TB, T - t0);
-    for (int r = tid; r < Nr; r += 256) {
-        double ps = 0.0;
-        for (int tt = 0; tt < nt; ++tt) ps += (double)zs[tt][r];
-        part_psum[(size_t)blockIdx.x * Nr + r] = ps;
-        part_counts[(size_t)blockIdx.x * Nr + r] = cnt[r];
+    for (int r = threadIdx.x; r < Nr; r += 256) {
+        double a = 0.0;
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) { a += s_ps[w][r]; c += s_cnt[w][r]; }
+        part_psum[(size_t)blockIdx.x * Nr + r] = a;
+        part_counts[(size_t)blockIdx.x * Nr + r] = c;
     }
 }
 
-// counts[r] = sum_b part_counts[b, r]; prob_sum[r] = sum_b part_psum[b, r] (fp64, b ascending)
+// One workgroup per expert: counts[r] = sum_b part_counts[b, r],
+// prob_sum[r] = sum_b part_psum[b, r] in fp64 over a fixed tree.
 __global__ __launch_bounds__(256) void route_reduce_kernel(
     int nblk, int Nr, const int32_t *__restrict__ part_counts, const double *__restrict__ part_psum,
     int32_t *__restrict__ counts, float *__restrict__ prob_sum) {
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= Nr) return;
-    int64_t c = 0;
-    double ps = 0.0;
-    for (int b = 0; b < nblk; ++b) {
+    __shared__ double s_p[256];
+    __shared__ long long s_c[256];
+    const int r = blockIdx.x;
+    double a = 0.0;
+    long long c = 0;
+    for (int b = threadIdx.x; b < nblk; b += 256) {
+        a += part_psum[(size_t)b * Nr + r];
         c += part_counts[(size_t)b * Nr + r];
-        ps += part_psum[(size_t)b * Nr + r];
     }
-    counts[r] = (int32_t)c;
-    prob_sum[r] = (float)ps;
+    s_p[threadIdx.x] = a;
+    s_c[threadIdx.x] = c;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) {
+            s_p[threadIdx.x] += s_p[threadIdx.x + o];
+            s_c[threadIdx.x] += s_c[threadIdx.x + o];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        counts[r] = (int32_t)s_c[0];
+        prob_sum[r] = (float)s_p[0];
+    }
 }
 
 }  // namespace
+
+// Tokens per wave: as many (up to 4) as keep at least 256 workgroups of
+// 4 waves, so the centroid chunks are reused across up to 16 tokens.
+int route_tokens_per_wave(int T) { return T >= 4096 ? 4 : (T >= 2048 ? 2 : 1); }
+
+int route_blocks(int T) {
+    const int rt = route_tokens_per_wave(T);
+    return cdiv(T, 4 * rt);
+}
 
 hipError_t launch_route(const moe_problem &p, const void *x, const float *centroids,
                         const float *bias, int32_t *idx, float *gate, float *probs,
                         int32_t *part_counts, double *part_psum, int32_t *counts,
                         float *prob_sum, hipStream_t s) {
-    const int nblk = cdiv(p.T, kRouteTokens);
+    const int nblk = p.T > 0 ? route_blocks(p.T) : 0;
     const int xb = p.dtype == MOE_BF16;
+    const int nj = cdiv(p.n_routed, 64);
+    const int rt = route_tokens_per_wave(p.T);
     if (nblk > 0) {
-        if (p.n_routed <= 64)
-            route_kernel<64><<<nblk, 256, 0, s>>>(p.T, p.d, p.n_routed, p.top_k, x, xb, centroids, bias,
-                                                  idx, gate, probs, part_counts, part_psum);
-        else if (p.n_routed <= 128)
-            route_kernel<128><<<nblk, 256, 0, s>>>(p.T, p.d, p.n_routed, p.top_k, x, xb, centroids, bias,
-                                                   idx, gate, probs, part_counts, part_psum);
-        else
-            route_kernel<256><<<nblk, 256, 0, s>>>(p.T, p.d, p.n_routed, p.top_k, x, xb, centroids, bias,
-                                                   idx, gate, probs, part_counts, part_psum);
+#define MOE_ROUTE_LAUNCH(RT, NJ, KC)                                                                      \
+    route_kernel<RT, NJ, KC><<<nblk, 256, 0, s>>>(p.T, p.d, p.n_routed, p.top_k, x, xb, centroids, bias, idx, \
+                                                  gate, probs, part_counts, part_psum)
+        if (rt == 4) {
+            if (nj == 1) MOE_ROUTE_LAUNCH(4, 1, 32);
+            else if (nj == 2) MOE_ROUTE_LAUNCH(4, 2, 32);
+            else MOE_ROUTE_LAUNCH(4, 4, 16);
+        } else if (rt == 2) {
+            if (nj == 1) MOE_ROUTE_LAUNCH(2, 1, 32);
+            else if (nj == 2) MOE_ROUTE_LAUNCH(2, 2, 32);
+            else MOE_ROUTE_LAUNCH(2, 4, 16);
+        } else {
+            if (nj == 1) MOE_ROUTE_LAUNCH(1, 1, 32);
+            else if (nj == 2) MOE_ROUTE_LAUNCH(1, 2, 32);
+            else MOE_ROUTE_LAUNCH(1, 4, 16);
+        }
+#undef MOE_ROUTE_LAUNCH
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    route_reduce_kernel<<<cdiv(p.n_routed, 256), 256, 0, s>>>(nblk, p.n_routed, part_counts, part_psum,
-                                                              counts, prob_sum);
+    route_reduce_kernel<<<p.n_routed, 256, 0, s>>>(nblk, p.n_routed, part_counts, part_psum, counts, prob_sum);
     return hipGetLastError();
 }
 
