@@ -32,7 +32,6 @@ METRIC = "MoE-layer tokens/s + active TFLOP/s (% MFMA/HBM peak) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-UP_KERNEL = "grouped_ffn_kernel<bf16, up>"
 KERNEL_SOURCES = ["fine_grained_mixture_moe_amd/csrc/expert_ffn.hip",
                   "fine_grained_mixture_moe_amd/csrc/moe_internal.h"]
 COPY_BYTES = 1 << 30
@@ -191,7 +190,9 @@ def run(args) -> dict:
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     tr = load_traffic("up", name)
     roof["traffic"] = None if tr is None else tr["bytes_per_launch"]
-    roof["kernel"] = UP_KERNEL if wl.dtype == "bf16" else "grouped_ffn_kernel<f32, up>"
+    avg_rows = wl.T * wl.top_k / wl.n_routed if wl.n_routed else wl.T
+    roof["kernel"] = (f"grouped_ffn_bf16_kernel<{256 if avg_rows >= 768 else 128}, up>" if wl.dtype == "bf16"
+                      else "grouped_ffn_kernel<f32, up>")
     roof["kernel_ms"] = round(up_ms, 4)
     roof["algorithmic"] = {"flops": up["flops"], "bytes": up["bytes"], "pairs": up["pairs"],
                            "touched_experts": up["touched"]}
@@ -246,9 +247,9 @@ def ingest_pmc(pmc_dir: str, workload: str) -> None:
     for r in rows:
         kname = r.get("Kernel_Name", "")
         cname = r.get("Counter_Name", "")
-        if "grouped_ffn_kernel" in kname and ("true>" in kname or "Lb1E" in kname):
+        if "grouped_ffn" in kname and ("true>" in kname or "Lb1E" in kname):
             key = "up"
-        elif "grouped_ffn_kernel" in kname:
+        elif "grouped_ffn" in kname:
             key = "down"
         elif "elementwise" in kname.lower():
             key = "copy"
@@ -274,6 +275,22 @@ def ingest_pmc(pmc_dir: str, workload: str) -> None:
     print(json.dumps(rec, indent=1))
 
 
+def summarize_trace(trace_dir: str, command: str) -> None:
+    """Text summary of a rocprofv3 --kernel-trace --stats run (kernel_stats.csv)."""
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(paths[0])))
+    print(f"# rocprofv3 kernel statistics")
+    print(f"# command: {command}")
+    print(f"# {'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_%':>8s}")
+    for r in rows:
+        name = r["Name"].replace("moe::(anonymous namespace)::", "").replace("void ", "")
+        name = name.split("(")[0][:70]
+        print(f"  {name:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+              f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,9 +302,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--ingest-pmc", default=None)
+    ap.add_argument("--summarize-trace", default=None, help="rocprofv3 output dir to summarize")
+    ap.add_argument("--trace-command", default="", help="command that produced --summarize-trace")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc, args.config)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.trace_command)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this layer pass has no multi-GPU path (asked for --gpus {args.gpus})",

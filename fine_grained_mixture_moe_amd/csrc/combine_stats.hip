@@ -80,9 +80,18 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int K, const
     store8(h + (size_t)t * d + c, acc);
 }
 
-// One workgroup.  f and f' are exact functions of integer counts (fp64
-// quotient rounded once to fp32); ExpBal and DevBal are fp64 sums over a
-// fixed tree (deterministic).
+// One workgroup of 256 threads.  f and f' are exact functions of integer
+// counts (fp64 quotient rounded once to fp32); ExpBal and DevBal are fp64
+// sums: strided per-thread sums, a butterfly within each wave, then the four
+// wave sums in order (a fixed order, so deterministic).
+__device__ __forceinline__ double block_sum4(double v, double *s_w) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+}
+
 __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K, int D,
                                                             const int32_t *__restrict__ counts,
                                                             const float *__restrict__ prob_sum,
@@ -91,16 +100,16 @@ __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K
                                                             float *__restrict__ P_dev,
                                                             float *__restrict__ exp_bal,
                                                             float *__restrict__ dev_bal) {
-    __shared__ double s_fp[kPermuteMaxExperts];
-    __shared__ double s_gp[kPermuteMaxExperts];
+    __shared__ double s_a[4], s_b[4];
     const int gsz = Nr / D;
+    double eb = 0.0, db = 0.0;
     for (int r = threadIdx.x; r < Nr; r += 256) {
         const double fr = T > 0 ? ((double)Nr * (double)counts[r]) / ((double)K * (double)T) : 0.0;
         const double pr = T > 0 ? (double)prob_sum[r] / (double)T : 0.0;
         const float ff = (float)fr, pf = (float)pr;
         f[r] = ff;
         P[r] = pf;
-        s_fp[r] = (double)ff * (double)pf;
+        eb += (double)ff * (double)pf;
     }
     for (int g = threadIdx.x; g < D; g += 256) {
         int64_t C = 0;
@@ -113,22 +122,13 @@ __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K
         const float ff = (float)fg, pf = (float)ps;
         f_dev[g] = ff;
         P_dev[g] = pf;
-        s_gp[g] = (double)ff * (double)pf;
+        db += (double)ff * (double)pf;
     }
-    for (int r = Nr + threadIdx.x; r < kPermuteMaxExperts; r += 256) s_fp[r] = 0.0;
-    for (int g = D + threadIdx.x; g < kPermuteMaxExperts; g += 256) s_gp[g] = 0.0;
-    __syncthreads();
-    // fixed-order tree sums over the (zero-padded) 1024 slots
-    for (int o = kPermuteMaxExperts / 2; o > 0; o >>= 1) {
-        for (int i = threadIdx.x; i < o; i += 256) {
-            s_fp[i] += s_fp[i + o];
-            s_gp[i] += s_gp[i + o];
-        }
-        __syncthreads();
-    }
+    const double e_all = block_sum4(eb, s_a);
+    const double d_all = block_sum4(db, s_b);
     if (threadIdx.x == 0) {
-        *exp_bal = (float)s_fp[0];
-        *dev_bal = (float)s_gp[0];
+        *exp_bal = (float)e_all;
+        *dev_bal = (float)d_all;
     }
 }
 

@@ -31,8 +31,8 @@ inline size_t dtype_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 struct WsLayout {
     size_t route_counts;   // int32  [route_blocks, N']  per-block expert counts
     size_t route_psum;     // double [route_blocks, N']  per-block affinity sums
-    size_t perm_hist;      // int32  [perm_blocks, N']   per-block histogram
-    size_t perm_base;      // int32  [perm_blocks, N']   first slot of each (block, expert)
+    size_t perm_hist;      // int32  [N', perm_blocks]   per-block histogram (expert-major)
+    size_t perm_base;      // int32  [N', perm_blocks]   first slot of each (expert, block)
     size_t act_shared;     // dtype  [T, K_s*w]          SwiGLU activations, shared experts
     size_t act_routed;     // dtype  [T*K', w]           SwiGLU activations, grouped order
     size_t total;

@@ -4,9 +4,12 @@
 // 2.3): a stable counting sort of the T*K' pairs by expert, so each expert's
 // tokens sit contiguously (tokens ascending) for the grouped expert GEMMs.
 //
-//   hist     <<<ceil(T/256), 256>>>  per-block expert histogram (LDS int atomics)
-//   scan     <<<1, 1024>>>           expert totals -> offsets; per (block, expert)
-//                                    first slot = offsets[r] + earlier blocks' counts
+//   hist     <<<ceil(T/256), 256>>>  per-block expert histogram (LDS int atomics),
+//                                    stored expert-major: hist[r][b]
+//   scan     <<<1, 1024>>>           expert totals (contiguous rows) -> exclusive scan
+//                                    over experts (wave scans + one cross-wave step)
+//                                    -> offsets; first slot of (expert, block) =
+//                                    offsets[r] + earlier blocks' counts
 //   scatter  <<<ceil(T/256), 256>>>  each wave builds, per expert, the 64-bit mask of
 //                                    its lanes (tokens) that chose it; a pair's rank
 //                                    inside the expert is popcount of the masks of
@@ -31,37 +34,45 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(int T, int Nr, int K,
         }
     }
     __syncthreads();
-    for (int r = threadIdx.x; r < Nr; r += 256) hist[(size_t)blockIdx.x * Nr + r] = cnt[r];
+    for (int r = threadIdx.x; r < Nr; r += 256) hist[(size_t)r * gridDim.x + blockIdx.x] = cnt[r];
 }
 
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int nblk, int Nr,
                                                          const int32_t *__restrict__ hist,
                                                          int32_t *__restrict__ base,
                                                          int32_t *__restrict__ offsets) {
-    __shared__ int tot[kPermuteMaxExperts];
-    const int r = threadIdx.x;
+    __shared__ int wsum[16];
+    const int r = threadIdx.x, lane = r & 63, wave = r >> 6;
+    const int32_t *row = hist + (size_t)r * nblk;
     int total = 0;
     if (r < Nr)
-        for (int b = 0; b < nblk; ++b) total += hist[(size_t)b * Nr + r];
-    tot[r] = total;
-    __syncthreads();
-    // inclusive Hillis-Steele scan over the (<= 1024) expert totals
-    for (int o = 1; o < 1024; o <<= 1) {
-        const int v = r >= o ? tot[r - o] : 0;
-        __syncthreads();
-        tot[r] += v;
-        __syncthreads();
+        for (int b = 0; b < nblk; ++b) total += row[b];
+    // inclusive scan within the wave, then across the 16 wave totals
+    int incl = total;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
     }
-    const int excl = tot[r] - total;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int excl = before + incl - total;
     if (r < Nr) {
         offsets[r] = excl;
         int run = excl;
+        int32_t *brow = base + (size_t)r * nblk;
         for (int b = 0; b < nblk; ++b) {
-            base[(size_t)b * Nr + r] = run;
-            run += hist[(size_t)b * Nr + r];
+            brow[b] = run;
+            run += row[b];
         }
     }
-    if (r == 0) offsets[Nr] = tot[1023];
+    if (r == 0) {
+        int all = 0;
+        for (int w = 0; w < 16; ++w) all += wsum[w];
+        offsets[Nr] = all;
+    }
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int Nr, int K,
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int Nr, int K,
         }
         int rank = __popcll(mask[wave][r] & below);
         for (int w = 0; w < wave; ++w) rank += __popcll(mask[w][r]);
-        const int pos = base[(size_t)blockIdx.x * Nr + r] + rank;
+        const int pos = base[(size_t)r * gridDim.x + blockIdx.x] + rank;
         sorted_token[pos] = t;
         slot_of[(size_t)t * K + k] = pos;
     }

@@ -57,6 +57,88 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
+// Softmax over the routed experts and Top-K' selection for one token whose
+// logits (before bias) the wave holds: lane l has experts l + 64 j.  Writes
+// idx/gate (and probs), and adds the token's affinities and selections to
+// the lane's running per-expert sums ps / cnt.
+template <int NJ>
+__device__ __forceinline__ void finish_token(int t, int Nr, int K, int lane, float (&z)[NJ], const bool (&ev)[NJ],
+                                             const float *__restrict__ bias, int32_t *__restrict__ idx,
+                                             float *__restrict__ gate, float *__restrict__ probs,
+                                             double (&ps)[NJ], int (&cnt)[NJ]) {
+    float e[NJ], s[NJ];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if (bias && ev[j]) z[j] = z[j] + bias[lane + 64 * j];
+        if (ev[j]) m = fmaxf(m, z[j]);
+    }
+    m = wave_max(m);
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        e[j] = ev[j] ? expf(z[j] - m) : 0.0f;
+        sum += e[j];
+    }
+    sum = wave_sum(sum);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        s[j] = e[j] * inv;
+        ps[j] += (double)s[j];
+        if (ev[j] && probs) probs[(size_t)t * Nr + lane + 64 * j] = s[j];
+    }
+    // Top-K' by repeated wave argmax on key = (ordered z) << 32 | ~r
+    uint32_t taken = 0;
+    for (int k = 0; k < K; ++k) {
+        uint64_t best = 0;  // below every real key (ordered keys of finite z are > 0)
+        float best_s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (!ev[j] || (taken >> j & 1u)) continue;
+            const uint32_t r = (uint32_t)(lane + 64 * j);
+            const uint64_t key = ((uint64_t)ordered_key(z[j]) << 32) | (uint32_t)(~r);
+            if (key > best) { best = key; best_s = s[j]; }
+        }
+        const uint64_t win = wave_max_u64(best);
+        const int r = (int)(~(uint32_t)win);
+        const int owner = r & 63;
+        const float g = __shfl(best_s, owner, 64);
+        if (lane == owner) {
+            taken |= 1u << (r >> 6);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) cnt[j] += (j == (r >> 6)) ? 1 : 0;
+        }
+        if (lane == 0) {
+            idx[(size_t)t * K + k] = r;
+            gate[(size_t)t * K + k] = g;
+        }
+    }
+}
+
+// Per-workgroup partial statistics: the 4 waves' per-expert sums combined in
+// wave order (fixed), written to part_* at row blockIdx.x.
+template <int NJ>
+__device__ __forceinline__ void write_partials(int Nr, int wave, int lane, const double (&ps)[NJ],
+                                               const int (&cnt)[NJ], double (*s_ps)[NJ * 64],
+                                               int (*s_cnt)[NJ * 64], int32_t *__restrict__ part_counts,
+                                               double *__restrict__ part_psum) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        s_ps[wave][lane + 64 * j] = ps[j];
+        s_cnt[wave][lane + 64 * j] = cnt[j];
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < Nr; r += blockDim.x) {
+        double a = 0.0;
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) { a += s_ps[w][r]; c += s_cnt[w][r]; }
+        part_psum[(size_t)blockIdx.x * Nr + r] = a;
+        part_counts[(size_t)blockIdx.x * Nr + r] = c;
+    }
+}
+
 // One wave owns RT tokens and all N' experts: lane l holds experts l + 64 j
 // (j < NJ).  Every (token, expert) logit is one fma chain over k ascending.
 // The four waves of a workgroup share each KC-wide chunk of the centroids and
@@ -180,114 +262,50 @@ __global__ __launch_bounds__(256) void route_kernel(
     for (int i = 0; i < RT; ++i) {
         const int t = t0 + i;
         if (t >= T) break;
-        float z[NJ], e[NJ], s[NJ];
-        float m = -INFINITY;
+        float z[NJ];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            z[j] = acc[i][j];
-            if (bias && ev[j]) z[j] = z[j] + bias[lane + 64 * j];
-            if (ev[j]) m = fmaxf(m, z[j]);
-        }
-        m = wave_max(m);
-        float sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            e[j] = ev[j] ? expf(z[j] - m) : 0.0f;
-            sum += e[j];
-        }
-        sum = wave_sum(sum);
-        const float inv = 1.0f / sum;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            s[j] = e[j] * inv;
-            ps[j] += (double)s[j];
-            if (ev[j] && probs) probs[(size_t)t * Nr + lane + 64 * j] = s[j];
-        }
-        // Top-K' by repeated wave argmax on key = (ordered z) << 32 | ~r
-        uint32_t taken = 0;
-        for (int k = 0; k < K; ++k) {
-            uint64_t best = 0;  // below every real key (ordered keys of finite z are > 0)
-            float best_s = 0.0f;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                if (!ev[j] || (taken >> j & 1u)) continue;
-                const uint32_t r = (uint32_t)(lane + 64 * j);
-                const uint64_t key = ((uint64_t)ordered_key(z[j]) << 32) | (uint32_t)(~r);
-                if (key > best) { best = key; best_s = s[j]; }
-            }
-            const uint64_t win = wave_max_u64(best);
-            const int r = (int)(~(uint32_t)win);
-            const int owner = r & 63;
-            const float g = __shfl(best_s, owner, 64);
-            if (lane == owner) {
-                taken |= 1u << (r >> 6);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) cnt[j] += (j == (r >> 6)) ? 1 : 0;
-            }
-            if (lane == 0) {
-                idx[(size_t)t * K + k] = r;
-                gate[(size_t)t * K + k] = g;
-            }
-        }
+        for (int j = 0; j < NJ; ++j) z[j] = acc[i][j];
+        finish_token<NJ>(t, Nr, K, lane, z, ev, bias, idx, gate, probs, ps, cnt);
     }
 
-    // per-workgroup partial statistics, waves combined in order
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        s_ps[wave][lane + 64 * j] = ps[j];
-        s_cnt[wave][lane + 64 * j] = cnt[j];
-    }
-    __syncthreads();
-    for (int r = threadIdx.x; r < Nr; r += 256) {
-        double a = 0.0;
-        int c = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) { a += s_ps[w][r]; c += s_cnt[w][r]; }
-        part_psum[(size_t)blockIdx.x * Nr + r] = a;
-        part_counts[(size_t)blockIdx.x * Nr + r] = c;
-    }
+    write_partials<NJ>(Nr, wave, lane, ps, cnt, s_ps, s_cnt, part_counts, part_psum);
 }
 
 // One workgroup per expert: counts[r] = sum_b part_counts[b, r],
-// prob_sum[r] = sum_b part_psum[b, r] in fp64 over a fixed tree.
+// prob_sum[r] = sum_b part_psum[b, r] in fp64: strided per-thread sums, a
+// butterfly within each wave, then the 4 wave sums in order (fixed order).
 __global__ __launch_bounds__(256) void route_reduce_kernel(
     int nblk, int Nr, const int32_t *__restrict__ part_counts, const double *__restrict__ part_psum,
     int32_t *__restrict__ counts, float *__restrict__ prob_sum) {
-    __shared__ double s_p[256];
-    __shared__ long long s_c[256];
-    const int r = blockIdx.x;
+    __shared__ double s_p[4];
+    __shared__ long long s_c[4];
+    const int r = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     double a = 0.0;
     long long c = 0;
     for (int b = threadIdx.x; b < nblk; b += 256) {
         a += part_psum[(size_t)b * Nr + r];
         c += part_counts[(size_t)b * Nr + r];
     }
-    s_p[threadIdx.x] = a;
-    s_c[threadIdx.x] = c;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (threadIdx.x < o) {
-            s_p[threadIdx.x] += s_p[threadIdx.x + o];
-            s_c[threadIdx.x] += s_c[threadIdx.x + o];
-        }
-        __syncthreads();
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a += __shfl_xor(a, o, 64);
+        c += __shfl_xor(c, o, 64);
     }
+    if (lane == 0) { s_p[wave] = a; s_c[wave] = c; }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        counts[r] = (int32_t)s_c[0];
-        prob_sum[r] = (float)s_p[0];
+        counts[r] = (int32_t)(s_c[0] + s_c[1] + s_c[2] + s_c[3]);
+        prob_sum[r] = (float)(((s_p[0] + s_p[1]) + s_p[2]) + s_p[3]);
     }
 }
 
 }  // namespace
 
-// Tokens per wave: as many (up to 4) as keep at least 256 workgroups of
-// 4 waves, so the centroid chunks are reused across up to 16 tokens.
-int route_tokens_per_wave(int T) { return T >= 4096 ? 4 : (T >= 2048 ? 2 : 1); }
+// Tokens per wave: 4 for large batches (centroid chunks reused by 16 tokens
+// of a workgroup), 1 otherwise (more workgroups to overlap chunk latency).
+int route_tokens_per_wave(int T) { return T >= 8192 ? 4 : 1; }
 
-int route_blocks(int T) {
-    const int rt = route_tokens_per_wave(T);
-    return cdiv(T, 4 * rt);
-}
+int route_blocks(int T) { return cdiv(T, 4 * route_tokens_per_wave(T)); }
 
 hipError_t launch_route(const moe_problem &p, const void *x, const float *centroids,
                         const float *bias, int32_t *idx, float *gate, float *probs,
@@ -296,25 +314,18 @@ hipError_t launch_route(const moe_problem &p, const void *x, const float *centro
     const int nblk = p.T > 0 ? route_blocks(p.T) : 0;
     const int xb = p.dtype == MOE_BF16;
     const int nj = cdiv(p.n_routed, 64);
-    const int rt = route_tokens_per_wave(p.T);
     if (nblk > 0) {
-#define MOE_ROUTE_LAUNCH(RT, NJ, KC)                                                                      \
-    route_kernel<RT, NJ, KC><<<nblk, 256, 0, s>>>(p.T, p.d, p.n_routed, p.top_k, x, xb, centroids, bias, idx, \
-                                                  gate, probs, part_counts, part_psum)
-        if (rt == 4) {
-            if (nj == 1) MOE_ROUTE_LAUNCH(4, 1, 32);
-            else if (nj == 2) MOE_ROUTE_LAUNCH(4, 2, 32);
-            else MOE_ROUTE_LAUNCH(4, 4, 16);
-        } else if (rt == 2) {
-            if (nj == 1) MOE_ROUTE_LAUNCH(2, 1, 32);
-            else if (nj == 2) MOE_ROUTE_LAUNCH(2, 2, 32);
-            else MOE_ROUTE_LAUNCH(2, 4, 16);
+#define MOE_ARGS p.T, p.d, p.n_routed, p.top_k, x, xb, centroids, bias, idx, gate, probs, part_counts, part_psum
+        if (route_tokens_per_wave(p.T) == 4) {
+            if (nj == 1) route_kernel<4, 1, 32><<<nblk, 256, 0, s>>>(MOE_ARGS);
+            else if (nj == 2) route_kernel<4, 2, 32><<<nblk, 256, 0, s>>>(MOE_ARGS);
+            else route_kernel<4, 4, 16><<<nblk, 256, 0, s>>>(MOE_ARGS);
         } else {
-            if (nj == 1) MOE_ROUTE_LAUNCH(1, 1, 32);
-            else if (nj == 2) MOE_ROUTE_LAUNCH(1, 2, 32);
-            else MOE_ROUTE_LAUNCH(1, 4, 16);
+            if (nj == 1) route_kernel<1, 1, 64><<<nblk, 256, 0, s>>>(MOE_ARGS);
+            else if (nj == 2) route_kernel<1, 2, 64><<<nblk, 256, 0, s>>>(MOE_ARGS);
+            else route_kernel<1, 4, 32><<<nblk, 256, 0, s>>>(MOE_ARGS);
         }
-#undef MOE_ROUTE_LAUNCH
+#undef MOE_ARGS
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
