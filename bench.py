@@ -191,7 +191,7 @@ def run(args) -> dict:
     tr = load_traffic("up", name)
     roof["traffic"] = None if tr is None else tr["bytes_per_launch"]
     avg_rows = wl.T * wl.top_k / wl.n_routed if wl.n_routed else wl.T
-    roof["kernel"] = (f"grouped_ffn_bf16_kernel<{256 if avg_rows >= 768 else 128}, up>" if wl.dtype == "bf16"
+    roof["kernel"] = (f"grouped_ffn_bf16_kernel<{256 if avg_rows >= 256 else 128}, up>" if wl.dtype == "bf16"
                       else "grouped_ffn_kernel<f32, up>")
     roof["kernel_ms"] = round(up_ms, 4)
     roof["algorithmic"] = {"flops": up["flops"], "bytes": up["bytes"], "pairs": up["pairs"],

@@ -101,22 +101,28 @@ __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K
                                                             float *__restrict__ exp_bal,
                                                             float *__restrict__ dev_bal) {
     __shared__ double s_a[4], s_b[4];
+    __shared__ double s_P[kPermuteMaxExperts];
+    __shared__ int s_c[kPermuteMaxExperts];
     const int gsz = Nr / D;
     double eb = 0.0, db = 0.0;
     for (int r = threadIdx.x; r < Nr; r += 256) {
-        const double fr = T > 0 ? ((double)Nr * (double)counts[r]) / ((double)K * (double)T) : 0.0;
+        const int c = counts[r];
+        const double fr = T > 0 ? ((double)Nr * (double)c) / ((double)K * (double)T) : 0.0;
         const double pr = T > 0 ? (double)prob_sum[r] / (double)T : 0.0;
         const float ff = (float)fr, pf = (float)pr;
         f[r] = ff;
         P[r] = pf;
+        s_P[r] = pr;
+        s_c[r] = c;
         eb += (double)ff * (double)pf;
     }
+    __syncthreads();
     for (int g = threadIdx.x; g < D; g += 256) {
         int64_t C = 0;
         double ps = 0.0;
         for (int r = g * gsz; r < (g + 1) * gsz; ++r) {
-            C += counts[r];
-            ps += T > 0 ? (double)prob_sum[r] / (double)T : 0.0;
+            C += s_c[r];
+            ps += s_P[r];
         }
         const double fg = T > 0 ? ((double)Nr * (double)C) / ((double)K * (double)T * (double)gsz) : 0.0;
         const float ff = (float)fg, pf = (float)ps;

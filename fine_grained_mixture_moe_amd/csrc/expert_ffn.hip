@@ -495,47 +495,49 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
                 acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[nb], fb[mb], acc[nb][mb], 0, 0, 0);
     };
 
-    // Pipeline: stage kt&1 holds k step kt; the registers hold step kt+1.
-    // During the 4 sub-steps of step kt, quarter ph of the registers is
-    // written to the other stage and refilled with step kt+2, between MFMAs.
-    const int nk = K / 64;
-#pragma unroll
-    for (int ph = 0; ph < 4; ++ph) gload_part(0, ph);
-#pragma unroll
-    for (int ph = 0; ph < 4; ++ph) sstore_part(0, ph);
-    __syncthreads();
-    if (nk > 1)
-#pragma unroll
-        for (int ph = 0; ph < 4; ++ph) gload_part(1, ph);
-    // one k step; MORE: step kt+1 exists (store it), MORE2: step kt+2 exists (load it)
-    auto kstep = [&](int kt, auto more_t, auto more2_t) {
-        constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
-        const int st = kt & 1;
-        bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
-        frags(st, 0, fa0, fb0);
-        frags(st, 1, fa1, fb1);
-        if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kt + 2, 0); }
-        __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
-        mma(fa0, fb0);
-        frags(st, 2, fa0, fb0);
-        if (MORE) { sstore_part(st ^ 1, 1); if (MORE2) gload_part(kt + 2, 1); }
-        __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
-        mma(fa1, fb1);
-        frags(st, 3, fa1, fb1);
-        if (MORE) { sstore_part(st ^ 1, 2); if (MORE2) gload_part(kt + 2, 2); }
-        __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
-        mma(fa0, fb0);
-        if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kt + 2, 3); }
-        __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
-        mma(fa1, fb1);
-        __syncthreads();
-    };
     using yes = std::true_type;
     using no = std::false_type;
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) kstep(kt, yes{}, yes{});
-    if (kt + 1 < nk) kstep(kt++, yes{}, no{});
-    kstep(kt, no{}, no{});
+    const int nk = K / 64;
+    {
+        // Stage kt&1 holds k step kt; the registers hold step kt+1.  During
+        // the 4 sub-steps of step kt, quarter ph of the registers is written
+        // to the other stage and refilled with step kt+2, between MFMAs.
+#pragma unroll
+        for (int ph = 0; ph < 4; ++ph) gload_part(0, ph);
+#pragma unroll
+        for (int ph = 0; ph < 4; ++ph) sstore_part(0, ph);
+        __syncthreads();
+        if (nk > 1)
+#pragma unroll
+            for (int ph = 0; ph < 4; ++ph) gload_part(1, ph);
+        // MORE: step kt+1 exists (store it), MORE2: step kt+2 exists (load it)
+        auto kstep = [&](int kt, auto more_t, auto more2_t) {
+            constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
+            const int st = kt & 1;
+            bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
+            frags(st, 0, fa0, fb0);
+            frags(st, 1, fa1, fb1);
+            if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kt + 2, 0); }
+            __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
+            mma(fa0, fb0);
+            frags(st, 2, fa0, fb0);
+            if (MORE) { sstore_part(st ^ 1, 1); if (MORE2) gload_part(kt + 2, 1); }
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fa1, fb1);
+            frags(st, 3, fa1, fb1);
+            if (MORE) { sstore_part(st ^ 1, 2); if (MORE2) gload_part(kt + 2, 2); }
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fa0, fb0);
+            if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kt + 2, 3); }
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fa1, fb1);
+            __syncthreads();
+        };
+        int kt = 0;
+        for (; kt + 2 < nk; ++kt) kstep(kt, yes{}, yes{});
+        if (kt + 1 < nk) kstep(kt++, yes{}, no{});
+        kstep(kt, no{}, no{});
+    }
 
     // ---- epilogue: lane owns token column l32 of each block; register quad q
     //      holds weight rows 8q + 4*lhi + {0..3} of the block ----
@@ -615,11 +617,12 @@ hipError_t launch_typed(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
 }
 
 // Token tile of the bf16 path: 256 rows when the routed experts average at
-// least 768 rows (edge waste <= 1/6), else 128.
+// least 256 rows (measured: the larger tile's lower LDS traffic per MFMA
+// outweighs its edge waste down to ~2 tiles per expert), else 128.
 template <bool UP>
 hipError_t launch_bf16(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
     const int64_t avg = p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / p.n_routed : (int64_t)p.T;
-    if (avg >= 768) {
+    if (avg >= 256) {
         const int tiles = tile_bound(p, UP, 256, 128, 256);
         if (tiles == 0) return hipSuccess;
         grouped_ffn_bf16_kernel<256, UP><<<tiles, 512, 0, s>>>(make_params(p, a, UP));

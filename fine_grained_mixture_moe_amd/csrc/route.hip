@@ -6,20 +6,23 @@
 // "【论文总结】MoE" section 2.2: the affinity is computed against a learnable
 // centroid e_i per expert.
 //
-// One workgroup (256 threads, 4 wave64) owns 64 tokens and all N' experts:
-//   1. logits z[64 x N'] as a register-tiled SIMT GEMM in fp32.  Every
-//      z_{t,r} is ONE fused multiply-add chain over k = 0..d-1 in ascending
-//      order starting from +0 (then + bias_r), so the value - and therefore
-//      the selected experts - is reproducible bit for bit on any IEEE host.
-//      No MFMA and no split-K: both would change the summation order.
-//   2. per token, one wave computes softmax over the routed experts
-//      (max/sum butterflies) and selects the Top-K' by repeated wave argmax
-//      on a 64-bit key (ordered logit bits, then inverted expert index), so
-//      equal logits go to the lower index and -0.0 ties +0.0.
-//   3. the workgroup writes its per-expert token counts and affinity sums
-//      (fp64, tokens in order); a second one-block kernel reduces the
-//      partials over workgroups in a fixed order (only integer LDS atomics,
-//      whose result does not depend on order).
+// Large batches: one launch (route_kernel) computes logits, softmax, Top-K'
+// and partial statistics per 16 tokens.  Small batches: three launches:
+//   1. logits: z[T x N'] in fp32 as a register-tiled SIMT GEMM (lane = token,
+//      a wave's experts read as LDS broadcasts).  Every z_{t,r} is ONE fused
+//      multiply-add chain over k = 0..d-1 in ascending order starting from +0,
+//      so the value - and therefore the selected experts - is reproducible
+//      bit for bit on any IEEE host.  No MFMA and no split-K: both would
+//      change the summation order.
+//   2. select: one wave per token adds the bias, computes softmax over the
+//      routed experts (max/sum butterflies) and selects the Top-K' by repeated
+//      wave argmax on a 64-bit key (ordered logit bits, then inverted expert
+//      index), so equal logits go to the lower index and -0.0 ties +0.0; each
+//      workgroup writes its per-expert token counts and fp64 affinity sums
+//      (tokens in order).
+//   3. reduce (both shapes): one workgroup per expert sums the partials in a
+//      fixed order.
+// No atomics: results are identical on every run.
 #include "moe_internal.h"
 
 namespace moe {
@@ -271,6 +274,141 @@ __global__ __launch_bounds__(256) void route_kernel(
     write_partials<NJ>(Nr, wave, lane, ps, cnt, s_ps, s_cnt, part_counts, part_psum);
 }
 
+// Logits.  A workgroup owns 64 tokens x 4*EW experts: lane = token, wave w
+// the experts 4*EW*blockIdx.y + EW*w + (0..EW-1).  Every z_{t,r} is one fp32
+// fma chain over k = 0..d-1 in ascending order from +0 (the bias is added
+// by the select kernel).  The workgroup streams KC-wide chunks of its 64
+// token rows (converted to fp32, shared by the 4 waves; row pitch KC+4 keeps
+// the 16-byte per-lane reads on distinct banks) and of its experts' centroid
+// rows (read as wave-uniform broadcasts) through double-buffered LDS.
+template <int EW, int KC>
+__global__ __launch_bounds__(256) void route_logits_kernel(int T, int d, int Nr, const void *__restrict__ x,
+                                                           int x_bf16, const float *__restrict__ E,
+                                                           float *__restrict__ z) {
+    constexpr int NE = 4 * EW;           // experts of the workgroup
+    constexpr int XP = KC + 4;           // token row pitch (floats)
+    constexpr int XV = 64 * KC / 8 / 256;  // 8-value token pieces per thread
+    constexpr int EV = (NE * KC / 4 + 255) / 256;  // centroid float4 per thread
+    static_assert(XV >= 1, "chunk shape");
+    __shared__ __attribute__((aligned(16))) float s_x[2][64 * XP];
+    __shared__ __attribute__((aligned(16))) float s_e[2][NE * KC];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t0 = blockIdx.x * 64, r0 = blockIdx.y * NE;
+
+    float xs[XV][8];
+    float4 es[EV];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int v = 0; v < XV; ++v) {
+            const int c = tid + 256 * v;                // piece: token c / (KC/8), k offset 8*(c % (KC/8))
+            const int tt = c / (KC / 8), kk = (c % (KC / 8)) * 8;
+            const int t = t0 + tt;
+            if (t >= T) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) xs[v][j] = 0.0f;
+            } else if (x_bf16) {
+                const uint4 w = *(const uint4 *)((const uint16_t *)x + (size_t)t * d + k0 + kk);
+                const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    xs[v][2 * h] = __uint_as_float(wv[h] << 16);
+                    xs[v][2 * h + 1] = __uint_as_float(wv[h] & 0xffff0000u);
+                }
+            } else {
+                const float4 a = *(const float4 *)((const float *)x + (size_t)t * d + k0 + kk);
+                const float4 b = *(const float4 *)((const float *)x + (size_t)t * d + k0 + kk + 4);
+                xs[v][0] = a.x; xs[v][1] = a.y; xs[v][2] = a.z; xs[v][3] = a.w;
+                xs[v][4] = b.x; xs[v][5] = b.y; xs[v][6] = b.z; xs[v][7] = b.w;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < EV; ++q) {
+            const int c = tid + 256 * q;
+            es[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < NE * KC / 4) {
+                const int e = c / (KC / 4), c4 = c % (KC / 4);
+                if (r0 + e < Nr) es[q] = *(const float4 *)(E + (size_t)(r0 + e) * d + k0 + 4 * c4);
+            }
+        }
+    };
+    auto sstore = [&](int b) {
+#pragma unroll
+        for (int v = 0; v < XV; ++v) {
+            const int c = tid + 256 * v;
+            const int tt = c / (KC / 8), kk = (c % (KC / 8)) * 8;
+            *(float4 *)&s_x[b][tt * XP + kk] = make_float4(xs[v][0], xs[v][1], xs[v][2], xs[v][3]);
+            *(float4 *)&s_x[b][tt * XP + kk + 4] = make_float4(xs[v][4], xs[v][5], xs[v][6], xs[v][7]);
+        }
+#pragma unroll
+        for (int q = 0; q < EV; ++q)
+            if (tid + 256 * q < NE * KC / 4) *(float4 *)&s_e[b][(tid + 256 * q) * 4] = es[q];
+    };
+
+    float acc[EW];
+#pragma unroll
+    for (int e = 0; e < EW; ++e) acc[e] = 0.0f;
+    const int nchunk = d / KC;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kc = 0; kc < nchunk; ++kc) {
+        const int b = kc & 1;
+        if (kc + 1 < nchunk) gload((kc + 1) * KC);
+#pragma unroll 4
+        for (int v = 0; v < KC / 4; ++v) {
+            const float4 x4 = *(const float4 *)&s_x[b][lane * XP + 4 * v];
+#pragma unroll
+            for (int e = 0; e < EW; ++e) {
+                const float4 e4 = *(const float4 *)&s_e[b][(wave * EW + e) * KC + 4 * v];
+                acc[e] = __builtin_fmaf(x4.x, e4.x, acc[e]);
+                acc[e] = __builtin_fmaf(x4.y, e4.y, acc[e]);
+                acc[e] = __builtin_fmaf(x4.z, e4.z, acc[e]);
+                acc[e] = __builtin_fmaf(x4.w, e4.w, acc[e]);
+            }
+        }
+        if (kc + 1 < nchunk) sstore(b ^ 1);
+        __syncthreads();
+    }
+    const int t = t0 + lane;
+    if (t < T)
+#pragma unroll
+        for (int e = 0; e < EW; ++e) {
+            const int r = r0 + wave * EW + e;
+            if (r < Nr) z[(size_t)t * Nr + r] = acc[e];
+        }
+}
+
+// Select.  One wave per token (its shuffle chains are latency-bound, so
+// tokens run in parallel waves), 4 per workgroup: add the bias, softmax,
+// Top-K', and the per-workgroup partial statistics (waves in a fixed order).
+template <int NJ>
+__global__ __launch_bounds__(256) void route_select_kernel(int T, int Nr, int K, const float *__restrict__ z,
+                                                           const float *__restrict__ bias,
+                                                           int32_t *__restrict__ idx, float *__restrict__ gate,
+                                                           float *__restrict__ probs,
+                                                           int32_t *__restrict__ part_counts,
+                                                           double *__restrict__ part_psum) {
+    __shared__ double s_ps[4][NJ * 64];
+    __shared__ int s_cnt[4][NJ * 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    bool ev[NJ];
+    double ps[NJ];
+    int cnt[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) { ev[j] = lane + 64 * j < Nr; ps[j] = 0.0; cnt[j] = 0; }
+    const int t = blockIdx.x * 4 + wave;
+    if (t < T) {
+        float zz[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) zz[j] = ev[j] ? z[(size_t)t * Nr + lane + 64 * j] : 0.0f;
+        finish_token<NJ>(t, Nr, K, lane, zz, ev, bias, idx, gate, probs, ps, cnt);
+    }
+    write_partials<NJ>(Nr, wave, lane, ps, cnt, s_ps, s_cnt, part_counts, part_psum);
+}
+
 // One workgroup per expert: counts[r] = sum_b part_counts[b, r],
 // prob_sum[r] = sum_b part_psum[b, r] in fp64: strided per-thread sums, a
 // butterfly within each wave, then the 4 wave sums in order (fixed order).
@@ -301,31 +439,52 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(
 
 }  // namespace
 
-// Tokens per wave: 4 for large batches (centroid chunks reused by 16 tokens
-// of a workgroup), 1 otherwise (more workgroups to overlap chunk latency).
-int route_tokens_per_wave(int T) { return T >= 8192 ? 4 : 1; }
+// Two shapes of the same computation (identical fma chains, so identical
+// results):
+//   T >= 8192: route_kernel, lane = expert, 4 tokens per wave, centroid
+//     chunks staged once per 16 tokens (each LDS read feeds 4 token chains);
+//   T <  8192: route_logits_kernel + route_select_kernel, lane = token, so
+//     even a decode batch spreads over many workgroups (2 experts per wave
+//     from 2048 tokens, else 1), then one wave per token selects.
+constexpr int kRouteTiledT = 8192;
 
-int route_blocks(int T) { return cdiv(T, 4 * route_tokens_per_wave(T)); }
+int route_blocks(int T) { return T >= kRouteTiledT ? cdiv(T, 16) : cdiv(T, 4); }
 
 hipError_t launch_route(const moe_problem &p, const void *x, const float *centroids,
-                        const float *bias, int32_t *idx, float *gate, float *probs,
+                        const float *bias, int32_t *idx, float *gate, float *probs, float *z,
                         int32_t *part_counts, double *part_psum, int32_t *counts,
                         float *prob_sum, hipStream_t s) {
     const int nblk = p.T > 0 ? route_blocks(p.T) : 0;
     const int xb = p.dtype == MOE_BF16;
     const int nj = cdiv(p.n_routed, 64);
     if (nblk > 0) {
+        if (p.T >= kRouteTiledT) {
 #define MOE_ARGS p.T, p.d, p.n_routed, p.top_k, x, xb, centroids, bias, idx, gate, probs, part_counts, part_psum
-        if (route_tokens_per_wave(p.T) == 4) {
             if (nj == 1) route_kernel<4, 1, 32><<<nblk, 256, 0, s>>>(MOE_ARGS);
             else if (nj == 2) route_kernel<4, 2, 32><<<nblk, 256, 0, s>>>(MOE_ARGS);
             else route_kernel<4, 4, 16><<<nblk, 256, 0, s>>>(MOE_ARGS);
-        } else {
-            if (nj == 1) route_kernel<1, 1, 64><<<nblk, 256, 0, s>>>(MOE_ARGS);
-            else if (nj == 2) route_kernel<1, 2, 64><<<nblk, 256, 0, s>>>(MOE_ARGS);
-            else route_kernel<1, 4, 32><<<nblk, 256, 0, s>>>(MOE_ARGS);
-        }
 #undef MOE_ARGS
+        } else {
+            // chunk of 128 when it divides d (d is a multiple of 64), else 64
+            const bool k128 = p.d % 128 == 0;
+            if (p.T >= 2048) {
+                const dim3 grid(cdiv(p.T, 64), cdiv(p.n_routed, 8));
+                if (k128) route_logits_kernel<2, 128><<<grid, 256, 0, s>>>(p.T, p.d, p.n_routed, x, xb, centroids, z);
+                else route_logits_kernel<2, 64><<<grid, 256, 0, s>>>(p.T, p.d, p.n_routed, x, xb, centroids, z);
+            } else {
+                const dim3 grid(cdiv(p.T, 64), cdiv(p.n_routed, 4));
+                if (k128) route_logits_kernel<1, 128><<<grid, 256, 0, s>>>(p.T, p.d, p.n_routed, x, xb, centroids, z);
+                else route_logits_kernel<1, 64><<<grid, 256, 0, s>>>(p.T, p.d, p.n_routed, x, xb, centroids, z);
+            }
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+#define MOE_SEL(NJ) route_select_kernel<NJ><<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, z, bias, idx, gate, \
+                                                                 probs, part_counts, part_psum)
+            if (nj == 1) MOE_SEL(1);
+            else if (nj == 2) MOE_SEL(2);
+            else MOE_SEL(4);
+#undef MOE_SEL
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

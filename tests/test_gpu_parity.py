@@ -43,6 +43,8 @@ SMALL = [
     (257, 128, 1, 100, 3, 128, "f32", 6, None, 5),
     (700, 128, 3, 2, 2, 192, "bf16", 7, None, 2),
     (130, 64, 0, 1, 1, 64, "f32", 8, None, 1),
+    (2500, 192, 1, 40, 5, 128, "bf16", 15, 1.1, 4),    # routing: 2 experts per wave, 64-wide chunks
+    (8300, 128, 0, 70, 4, 64, "f32", 16, None, 7),     # routing: tiled kernel, 2 expert lanes, ragged T
 ]
 
 
