@@ -373,14 +373,20 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
     const int mt = cdiv(rows, BM);
     const int lt = L - s_pref[g];
     const int m_tile = lt % mt, n_tile = lt / mt;
-    const int m0 = m_tile * BM;
+    // The group's rows are cut into mt runs of equal length rounded up to 32
+    // (never above BM, never empty), so a group of 530 rows makes tiles of
+    // 192, 192 and 146 rows instead of 256, 256 and 18: the work of a tile
+    // follows its live 32-row blocks, which the waves skip when empty.
+    const int run = (cdiv(rows, mt) + 31) & ~31;
+    const int m0 = m_tile * run;
+    const int nr = min(run, rows - m0);
 
     const int K = UP ? P.d : (shared ? P.Ks * P.w : P.w);
     const uint32_t xpitch = (uint32_t)K * 2u;   // token-side row bytes
     if (tid < BM) {
         const int row = m0 + tid;
         int src = -1;
-        if (row < rows) {
+        if (tid < nr) {
             if (UP) src = shared ? row : P.sorted_token[row_off + row];
             else src = row_off + row;
         }
@@ -476,22 +482,33 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
         wrow[nb] = UP ? (nb * 128 + wn * 32 + l32) : (wn * 64 + nb * 32 + l32);
+    // token block j (tile rows 32j..32j+31) belongs to wave row j & 1 as its
+    // block j >> 1, so the live blocks of a short tile split evenly
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) xrow[mb] = wm * (BM / 2) + mb * 32 + l32;
+    for (int mb = 0; mb < MB; ++mb) xrow[mb] = (2 * mb + wm) * 32 + l32;
+    const int nblk = cdiv(nr, 32);
+    // live token blocks of this wave (the same in all its lanes)
+    const int ml = __builtin_amdgcn_readfirstlane(min(MB, (nblk - wm + 1) >> 1));
     const int lsw = (l32 & 7) ^ ((l32 >> 3) & 1);   // swizzle of every fragment row of this lane
 
-    auto frags = [&](int stg, int ks, bf16x8 (&fa)[NB], bf16x8 (&fb)[MB]) {
+    // ML: live token blocks of the wave, a compile-time count so that the
+    // k loop stays straight-line code
+    auto frags = [&](auto ml_t, int stg, int ks, bf16x8 (&fa)[NB], bf16x8 (&fb)[MB]) {
+        constexpr int ML = decltype(ml_t)::value;
         const int ch = ((2 * ks + lhi) ^ lsw) * 16;
+        if (ML > 0) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fa[nb] = *(const bf16x8 *)(s_w[stg] + wrow[nb] * RB + ch);
+            for (int nb = 0; nb < NB; ++nb) fa[nb] = *(const bf16x8 *)(s_w[stg] + wrow[nb] * RB + ch);
+        }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fb[mb] = *(const bf16x8 *)(s_x[stg] + xrow[mb] * RB + ch);
+        for (int mb = 0; mb < ML; ++mb) fb[mb] = *(const bf16x8 *)(s_x[stg] + xrow[mb] * RB + ch);
     };
-    auto mma = [&](const bf16x8 (&fa)[NB], const bf16x8 (&fb)[MB]) {
+    auto mma = [&](auto ml_t, const bf16x8 (&fa)[NB], const bf16x8 (&fb)[MB]) {
+        constexpr int ML = decltype(ml_t)::value;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < ML; ++mb)
                 acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[nb], fb[mb], acc[nb][mb], 0, 0, 0);
     };
 
@@ -511,40 +528,50 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
 #pragma unroll
             for (int ph = 0; ph < 4; ++ph) gload_part(1, ph);
         // MORE: step kt+1 exists (store it), MORE2: step kt+2 exists (load it)
-        auto kstep = [&](int kt, auto more_t, auto more2_t) {
-            constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
-            const int st = kt & 1;
-            bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
-            frags(st, 0, fa0, fb0);
-            frags(st, 1, fa1, fb1);
-            if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kt + 2, 0); }
-            __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
-            mma(fa0, fb0);
-            frags(st, 2, fa0, fb0);
-            if (MORE) { sstore_part(st ^ 1, 1); if (MORE2) gload_part(kt + 2, 1); }
-            __builtin_amdgcn_sched_barrier(0);
-            mma(fa1, fb1);
-            frags(st, 3, fa1, fb1);
-            if (MORE) { sstore_part(st ^ 1, 2); if (MORE2) gload_part(kt + 2, 2); }
-            __builtin_amdgcn_sched_barrier(0);
-            mma(fa0, fb0);
-            if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kt + 2, 3); }
-            __builtin_amdgcn_sched_barrier(0);
-            mma(fa1, fb1);
-            __syncthreads();
+        auto kloop = [&](auto ml_t) {
+            auto kstep = [&](int kt, auto more_t, auto more2_t) {
+                constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
+                const int st = kt & 1;
+                bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
+                frags(ml_t, st, 0, fa0, fb0);
+                frags(ml_t, st, 1, fa1, fb1);
+                if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kt + 2, 0); }
+                __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
+                mma(ml_t, fa0, fb0);
+                frags(ml_t, st, 2, fa0, fb0);
+                if (MORE) { sstore_part(st ^ 1, 1); if (MORE2) gload_part(kt + 2, 1); }
+                __builtin_amdgcn_sched_barrier(0);
+                mma(ml_t, fa1, fb1);
+                frags(ml_t, st, 3, fa1, fb1);
+                if (MORE) { sstore_part(st ^ 1, 2); if (MORE2) gload_part(kt + 2, 2); }
+                __builtin_amdgcn_sched_barrier(0);
+                mma(ml_t, fa0, fb0);
+                if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kt + 2, 3); }
+                __builtin_amdgcn_sched_barrier(0);
+                mma(ml_t, fa1, fb1);
+                __syncthreads();
+            };
+            int kt = 0;
+            for (; kt + 2 < nk; ++kt) kstep(kt, yes{}, yes{});
+            if (kt + 1 < nk) kstep(kt++, yes{}, no{});
+            kstep(kt, no{}, no{});
         };
-        int kt = 0;
-        for (; kt + 2 < nk; ++kt) kstep(kt, yes{}, yes{});
-        if (kt + 1 < nk) kstep(kt++, yes{}, no{});
-        kstep(kt, no{}, no{});
+        // every wave runs every k step (loads, LDS stores, barriers); only its
+        // fragment reads and MFMAs follow its live blocks
+        using std::integral_constant;
+        if (ml >= MB) kloop(integral_constant<int, MB>{});
+        else if (MB > 3 && ml == 3) kloop(integral_constant<int, (MB > 3 ? 3 : 0)>{});
+        else if (MB > 2 && ml == 2) kloop(integral_constant<int, (MB > 2 ? 2 : 0)>{});
+        else if (ml == 1) kloop(integral_constant<int, 1>{});
+        else kloop(integral_constant<int, 0>{});
     }
 
     // ---- epilogue: lane owns token column l32 of each block; register quad q
     //      holds weight rows 8q + 4*lhi + {0..3} of the block ----
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+        if (xrow[mb] >= nr) continue;
         const int row = m0 + xrow[mb];
-        if (row >= rows) continue;
         if (UP) {
             const int ld = shared ? P.Ks * P.w : P.w;
             uint16_t *dst = (uint16_t *)(shared ? P.out_shared : P.out_routed) + (size_t)(row_off + row) * ld;

@@ -6,14 +6,19 @@
 //
 //   hist     <<<ceil(T/256), 256>>>  per-block expert histogram (LDS int atomics),
 //                                    stored expert-major: hist[r][b]
-//   scan     <<<1, 1024>>>           expert totals (contiguous rows) -> exclusive scan
-//                                    over experts (wave scans + one cross-wave step)
-//                                    -> offsets; first slot of (expert, block) =
-//                                    offsets[r] + earlier blocks' counts
-//   scatter  <<<ceil(T/256), 256>>>  each wave builds, per expert, the 64-bit mask of
-//                                    its lanes (tokens) that chose it; a pair's rank
-//                                    inside the expert is popcount of the masks of
-//                                    earlier waves plus its lanes below -> stable.
+//   scatter  <<<ceil(T/256), 256>>>  each block first derives what it needs from the
+//                                    whole histogram: expert totals, their exclusive
+//                                    scan (= offsets; block 0 stores them) and the
+//                                    first slot of (expert, this block) = offsets[r]
+//                                    + earlier blocks' counts.  Then each wave builds,
+//                                    per expert, the 64-bit mask of its lanes (tokens)
+//                                    that chose it; a pair's rank inside the expert is
+//                                    popcount of the masks of earlier waves plus its
+//                                    lanes below -> stable.
+// When the histogram is large (blocks x experts above kFusedScanMax) every
+// scatter block re-reading it would cost more than one more launch, so a
+// separate scan kernel <<<1, 1024>>> computes offsets and the per-(expert,
+// block) first slots once.
 // Integer-only, so the result is identical on every run.
 #include "moe_internal.h"
 
@@ -75,16 +80,80 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int nblk, int Nr,
     }
 }
 
+constexpr int kFusedScanMax = 16384;   // histogram entries each scatter block may read
+
+// Exclusive scan over experts of tot[0..Nr) in place (Nr <= 1024), 256
+// threads: each takes a run of 4 consecutive experts.  Returns the total.
+__device__ int block_exscan_experts(int *tot, int Nr, int *s_w) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = tid * 4;
+    int loc[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        loc[i] = r0 + i < Nr ? tot[r0 + i] : 0;
+        sum += loc[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_w[w];
+    const int all = ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (r0 + i < Nr) tot[r0 + i] = run;
+        run += loc[i];
+    }
+    __syncthreads();
+    return all;
+}
+
+// FUSED: derive offsets and this block's first slots from hist (see above);
+// else read the first slots from base (written by perm_scan_kernel).
+template <bool FUSED>
 __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int Nr, int K,
                                                            const int32_t *__restrict__ idx,
+                                                           const int32_t *__restrict__ hist,
                                                            const int32_t *__restrict__ base,
+                                                           int32_t *__restrict__ offsets,
                                                            int32_t *__restrict__ sorted_token,
                                                            int32_t *__restrict__ slot_of) {
     __shared__ unsigned long long mask[4][kPermuteMaxExperts];
+    __shared__ int s_first[kPermuteMaxExperts];
+    __shared__ int s_tot[kPermuteMaxExperts];
+    __shared__ int s_w[4];
+    const int nblk = gridDim.x, b = blockIdx.x;
     for (int i = threadIdx.x; i < 4 * Nr; i += 256) mask[i / Nr][i % Nr] = 0ull;
+    if (FUSED) {
+        for (int r = threadIdx.x; r < Nr; r += 256) {
+            const int32_t *row = hist + (size_t)r * nblk;
+            int tot = 0, before = 0;
+            for (int j = 0; j < nblk; ++j) {
+                const int v = row[j];
+                tot += v;
+                before += j < b ? v : 0;
+            }
+            s_tot[r] = tot;
+            s_first[r] = before;
+        }
+        __syncthreads();
+        const int all = block_exscan_experts(s_tot, Nr, s_w);
+        for (int r = threadIdx.x; r < Nr; r += 256) {
+            s_first[r] += s_tot[r];
+            if (b == 0) offsets[r] = s_tot[r];
+        }
+        if (b == 0 && threadIdx.x == 0) offsets[Nr] = all;
+    } else {
+        for (int r = threadIdx.x; r < Nr; r += 256) s_first[r] = base[(size_t)r * nblk + b];
+    }
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * kPermuteTokens + threadIdx.x;
+    const int t = b * kPermuteTokens + threadIdx.x;
     const bool live = t < T;
     if (live)
         for (int k = 0; k < K; ++k) {
@@ -102,7 +171,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int Nr, int K,
         }
         int rank = __popcll(mask[wave][r] & below);
         for (int w = 0; w < wave; ++w) rank += __popcll(mask[w][r]);
-        const int pos = base[(size_t)r * gridDim.x + blockIdx.x] + rank;
+        const int pos = s_first[r] + rank;
         sorted_token[pos] = t;
         slot_of[(size_t)t * K + k] = pos;
     }
@@ -123,8 +192,14 @@ hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *off
         return hipGetLastError();
     }
     perm_hist_kernel<<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist);
-    perm_scan_kernel<<<1, 1024, 0, s>>>(nblk, p.n_routed, hist, base, offsets);
-    perm_scatter_kernel<<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, base, sorted_token, slot_of);
+    if ((int64_t)nblk * p.n_routed <= kFusedScanMax) {
+        perm_scatter_kernel<true><<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist, nullptr, offsets,
+                                                       sorted_token, slot_of);
+    } else {
+        perm_scan_kernel<<<1, 1024, 0, s>>>(nblk, p.n_routed, hist, base, offsets);
+        perm_scatter_kernel<false><<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist, base, offsets,
+                                                        sorted_token, slot_of);
+    }
     return hipGetLastError();
 }
 

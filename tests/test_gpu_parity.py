@@ -44,7 +44,10 @@ SMALL = [
     (700, 128, 3, 2, 2, 192, "bf16", 7, None, 2),
     (130, 64, 0, 1, 1, 64, "f32", 8, None, 1),
     (2500, 192, 1, 40, 5, 128, "bf16", 15, 1.1, 4),    # routing: 2 experts per wave, 64-wide chunks
-    (8300, 128, 0, 70, 4, 64, "f32", 16, None, 7),     # routing: tiled kernel, 2 expert lanes, ragged T
+    (8300, 128, 0, 70, 4, 64, "f32", 16, None, 7),     # routing: 4 tokens per wave, 2 expert lanes, ragged T
+    (16500, 64, 0, 130, 3, 64, "bf16", 17, None, 5),   # routing: 8 tokens per wave, 3 expert lanes
+    (5000, 64, 0, 256, 16, 64, "bf16", 18, 1.1, 8),    # routing: N'=256, K'=16, skewed
+    (9000, 2048, 1, 64, 6, 64, "bf16", 19, 1.1, 4),    # routing: large d, 4 tokens per wave
 ]
 
 
