@@ -568,27 +568,12 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
 
     // ---- epilogue: lane owns token column l32 of each block; register quad q
     //      holds weight rows 8q + 4*lhi + {0..3} of the block ----
+    if (!UP && shared) {
+        // fp32 output of the shared experts: stored straight from registers
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        if (xrow[mb] >= nr) continue;
-        const int row = m0 + xrow[mb];
-        if (UP) {
-            const int ld = shared ? P.Ks * P.w : P.w;
-            uint16_t *dst = (uint16_t *)(shared ? P.out_shared : P.out_routed) + (size_t)(row_off + row) * ld;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = n_tile * 128 + wn * 32 + 8 * q + 4 * lhi;
-                if (col >= ld) continue;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pg = acc[0][mb][4 * q + e];
-                    const float pu = acc[1][mb][4 * q + e];
-                    v[e] = pg / (1.0f + __expf(-pg)) * pu;
-                }
-                store4(dst + col, v);
-            }
-        } else {
+        for (int mb = 0; mb < MB; ++mb) {
+            if (xrow[mb] >= nr) continue;
+            const int row = m0 + xrow[mb];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -598,10 +583,61 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][4 * q + e];
-                    if (shared) store4((float *)P.out_shared + (size_t)row * P.d + col, v);
-                    else store4((uint16_t *)P.out_routed + (size_t)(row_off + row) * P.d + col, v);
+                    store4((float *)P.out_shared + (size_t)row * P.d + col, v);
                 }
         }
+        return;
+    }
+    // bf16 output tile (BM tokens x NC features) staged in the now idle LDS
+    // stages, then written row by row with 16-byte stores: a wave covers whole
+    // rows, where direct stores from the MFMA layout would touch 32 rows with
+    // 16 bytes each.  Row pitch NC*2 bytes (C16 chunks of 16 B); chunk c of
+    // row r sits at chunk c ^ (r % C16), so the 32 rows of a fragment write,
+    // and the consecutive chunks of a row read, hit distinct banks.
+    constexpr int NC = UP ? 128 : BN;           // features of the tile
+    constexpr int C16 = NC / 8;                 // 16-byte chunks per row
+    constexpr int ROWS_W = (2 * BN * RB) / (NC * 2);   // rows that fit in the weight stages
+    static_assert(BM <= ROWS_W || BM - ROWS_W <= (2 * BM * RB) / (NC * 2), "output tile fits in LDS");
+    auto slot = [&](int r, int c) -> uint8_t * {
+        const int pc = c ^ (r & (C16 - 1));
+        return r < ROWS_W ? &s_w[0][0] + r * (NC * 2) + pc * 16 : &s_x[0][0] + (r - ROWS_W) * (NC * 2) + pc * 16;
+    };
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int r = xrow[mb];
+        if (UP) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pg = acc[0][mb][4 * q + e];
+                    const float pu = acc[1][mb][4 * q + e];
+                    v[e] = pg / (1.0f + __expf(-pg)) * pu;
+                }
+                store4((uint16_t *)(slot(r, wn * 4 + q) + lhi * 8), v);
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][4 * q + e];
+                    store4((uint16_t *)(slot(r, wn * 8 + nb * 4 + q) + lhi * 8), v);
+                }
+        }
+    }
+    __syncthreads();
+    const int ld = UP ? (shared ? P.Ks * P.w : P.w) : P.d;   // features of an output row
+    const int col0 = n_tile * NC;
+    uint16_t *out = (uint16_t *)(UP && shared ? P.out_shared : P.out_routed);
+    for (int i = tid; i < BM * C16; i += NT) {
+        const int r = i / C16, c = i % C16;
+        if (r >= nr || col0 + c * 8 >= ld) continue;
+        const uint4 v = *(const uint4 *)slot(r, c);
+        *(uint4 *)(out + (size_t)(row_off + m0 + r) * ld + col0 + c * 8) = v;
     }
 }
 
