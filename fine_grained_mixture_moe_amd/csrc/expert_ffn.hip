@@ -383,17 +383,6 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
 
     const int K = UP ? P.d : (shared ? P.Ks * P.w : P.w);
     const uint32_t xpitch = (uint32_t)K * 2u;   // token-side row bytes
-    if (tid < BM) {
-        const int row = m0 + tid;
-        int src = -1;
-        if (tid < nr) {
-            if (UP) src = shared ? row : P.sorted_token[row_off + row];
-            else src = row_off + row;
-        }
-        s_src[tid] = src;
-    }
-    __syncthreads();
-
     // ---- buffer resources and fixed per-thread offsets ----
     const int part = tid & 7;               // logical 16-byte chunk of the row
     const int rsub = tid >> 3;              // row within a group of 64
@@ -429,11 +418,6 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
         else wr = n_tile * BN + j;                       // W2 row = output column
         ow[i] = wr < n_valid ? (uint32_t)wr * wpitch + part * 16 : kOOB;
     }
-#pragma unroll
-    for (int i = 0; i < CX; ++i) {
-        const int src = s_src[rsub + 64 * i];
-        ox[i] = src >= 0 ? (uint32_t)src * xpitch + part * 16 : kOOB;
-    }
     // physical chunk of logical chunk c in row r: c ^ (r & 7) ^ ((r >> 3) & 1).
     // Any 8 consecutive rows, and any 16 consecutive rows split by parity,
     // land on distinct 16-byte bank groups.
@@ -450,14 +434,18 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
         return (uint32_t)kt * RB;
     };
     // part ph (0..3) of a k step: weight chunks [ph*CW/4, (ph+1)*CW/4), token chunks likewise
-    auto gload_part = [&](int kt, int ph) {
+    auto gload_part = [&](int kt, int ph, bool wts = true, bool toks = true) {
         const uint32_t kw = kw_of(kt), kx = (uint32_t)kt * RB;
+        if (wts) {
 #pragma unroll
-        for (int i = 0; i < CW; ++i)
-            if (i * 4 / CW == ph) sw[i] = bload((UP && i >= CW / 2) ? rw_b : rw_a, ow[i], kw);
+            for (int i = 0; i < CW; ++i)
+                if (i * 4 / CW == ph) sw[i] = bload((UP && i >= CW / 2) ? rw_b : rw_a, ow[i], kw);
+        }
+        if (toks) {
 #pragma unroll
-        for (int i = 0; i < CX; ++i)
-            if (i * 4 / CX == ph) sx[i] = bload(rx, ox[i], kx);
+            for (int i = 0; i < CX; ++i)
+                if (i * 4 / CX == ph) sx[i] = bload(rx, ox[i], kx);
+        }
     };
     auto sstore_part = [&](int stg, int ph) {
 #pragma unroll
@@ -519,8 +507,28 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
         // Stage kt&1 holds k step kt; the registers hold step kt+1.  During
         // the 4 sub-steps of step kt, quarter ph of the registers is written
         // to the other stage and refilled with step kt+2, between MFMAs.
+        // the weight rows of step 0 depend on the tile alone: their loads go
+        // out before the token sources are gathered (for the up projection a
+        // dependent global read), so the two latencies overlap
 #pragma unroll
-        for (int ph = 0; ph < 4; ++ph) gload_part(0, ph);
+        for (int ph = 0; ph < 4; ++ph) gload_part(0, ph, true, false);
+        if (tid < BM) {
+            const int row = m0 + tid;
+            int src = -1;
+            if (tid < nr) {
+                if (UP) src = shared ? row : P.sorted_token[row_off + row];
+                else src = row_off + row;
+            }
+            s_src[tid] = src;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < CX; ++i) {
+            const int src = s_src[rsub + 64 * i];
+            ox[i] = src >= 0 ? (uint32_t)src * xpitch + part * 16 : kOOB;
+        }
+#pragma unroll
+        for (int ph = 0; ph < 4; ++ph) gload_part(0, ph, false, true);
 #pragma unroll
         for (int ph = 0; ph < 4; ++ph) sstore_part(0, ph);
         __syncthreads();
@@ -635,11 +643,19 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
     const int ld = UP ? (shared ? P.Ks * P.w : P.w) : P.d;   // features of an output row
     const int col0 = n_tile * NC;
     uint16_t *out = (uint16_t *)(UP && shared ? P.out_shared : P.out_routed);
-    for (int i = tid; i < BM * C16; i += NT) {
+    constexpr int ITER = BM * C16 / NT;   // 16-byte pieces per thread
+    uint4 piece[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {   // every LDS read first, then the stores
+        const int i = tid + it * NT;
+        piece[it] = *(const uint4 *)slot(i / C16, i % C16);
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int i = tid + it * NT;
         const int r = i / C16, c = i % C16;
-        if (r >= nr || col0 + c * 8 >= ld) continue;
-        const uint4 v = *(const uint4 *)slot(r, c);
-        *(uint4 *)(out + (size_t)(row_off + m0 + r) * ld + col0 + c * 8) = v;
+        if (r < nr && col0 + c * 8 < ld)
+            *(uint4 *)(out + (size_t)(row_off + m0 + r) * ld + col0 + c * 8) = piece[it];
     }
 }
 
