@@ -64,14 +64,30 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int K, const
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
     }
-    for (int k = 0; k < K; ++k) {
-        const int slot = slot_of[(size_t)t * K + k];
-        if (slot < 0) continue;
-        const float g = gate[(size_t)t * K + k];
-        float y[8];
-        load8(y_routed + (size_t)slot * d + c, y);
+    // k in batches of 4: the batch's slots and gates, then its rows, are
+    // loaded before any use (independent loads in flight); the sums still run
+    // in k order
+    constexpr int KB = 4;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        int slot[KB];
+        float g[KB];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(g, y[j], acc[j]);
+        for (int u = 0; u < KB; ++u) {
+            const bool in = k0 + u < K;
+            slot[u] = in ? slot_of[(size_t)t * K + k0 + u] : -1;
+            g[u] = in ? gate[(size_t)t * K + k0 + u] : 0.0f;
+        }
+        float y[KB][8];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            if (slot[u] >= 0) load8(y_routed + (size_t)slot[u] * d + c, y[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            if (slot[u] < 0) continue;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(g[u], y[u][j], acc[j]);
+        }
     }
     float u[8];
     load8(x + (size_t)t * d + c, u);

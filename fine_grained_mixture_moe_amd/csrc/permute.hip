@@ -25,18 +25,27 @@
 namespace moe {
 namespace {
 
+// The (t, k) entries of a block's tokens are one contiguous run of idx: the
+// threads read it together (consecutive threads, consecutive entries, 4
+// independent loads in flight per thread).
+constexpr int kUnroll = 4;
+
 __global__ __launch_bounds__(256) void perm_hist_kernel(int T, int Nr, int K,
                                                         const int32_t *__restrict__ idx,
                                                         int32_t *__restrict__ hist) {
     __shared__ int cnt[kPermuteMaxExperts];
     for (int r = threadIdx.x; r < Nr; r += 256) cnt[r] = 0;
     __syncthreads();
-    const int t = blockIdx.x * kPermuteTokens + threadIdx.x;
-    if (t < T) {
-        for (int k = 0; k < K; ++k) {
-            const int r = idx[(size_t)t * K + k];
-            if ((unsigned)r < (unsigned)Nr) atomicAdd(&cnt[r], 1);
-        }
+    const int t0 = blockIdx.x * kPermuteTokens;
+    const int n = min(kPermuteTokens, T - t0) * K;
+    const int32_t *run = idx + (size_t)t0 * K;
+    for (int e = threadIdx.x; e < n; e += kUnroll * 256) {
+        int v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? run[e + u * 256] : -1;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if ((unsigned)v[u] < (unsigned)Nr) atomicAdd(&cnt[v[u]], 1);
     }
     __syncthreads();
     for (int r = threadIdx.x; r < Nr; r += 256) hist[(size_t)r * gridDim.x + blockIdx.x] = cnt[r];
@@ -130,16 +139,24 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int Nr, int K,
     const int nblk = gridDim.x, b = blockIdx.x;
     for (int i = threadIdx.x; i < 4 * Nr; i += 256) mask[i / Nr][i % Nr] = 0ull;
     if (FUSED) {
-        for (int r = threadIdx.x; r < Nr; r += 256) {
-            const int32_t *row = hist + (size_t)r * nblk;
-            int tot = 0, before = 0;
-            for (int j = 0; j < nblk; ++j) {
-                const int v = row[j];
-                tot += v;
-                before += j < b ? v : 0;
+        for (int r = threadIdx.x; r < Nr; r += 256) { s_tot[r] = 0; s_first[r] = 0; }
+        __syncthreads();
+        // expert totals and this block's preceding counts: every (expert,
+        // block) entry of hist read once, summed with integer LDS atomics
+        const int nh = Nr * nblk;
+        for (int e = threadIdx.x; e < nh; e += kUnroll * 256) {
+            int v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < nh ? hist[e + u * 256] : 0;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int f = e + u * 256;
+                if (f < nh && v[u] != 0) {
+                    const int r = f / nblk, j = f % nblk;
+                    atomicAdd(&s_tot[r], v[u]);
+                    if (j < b) atomicAdd(&s_first[r], v[u]);
+                }
             }
-            s_tot[r] = tot;
-            s_first[r] = before;
         }
         __syncthreads();
         const int all = block_exscan_experts(s_tot, Nr, s_w);
@@ -152,28 +169,44 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int Nr, int K,
         for (int r = threadIdx.x; r < Nr; r += 256) s_first[r] = base[(size_t)r * nblk + b];
     }
     __syncthreads();
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = b * kPermuteTokens + threadIdx.x;
-    const bool live = t < T;
-    if (live)
-        for (int k = 0; k < K; ++k) {
-            const int r = idx[(size_t)t * K + k];
-            if ((unsigned)r < (unsigned)Nr) atomicOr(&mask[wave][r], 1ull << lane);
+    // entries of this block: token t0 + e / K, slot k = e % K; its wave and lane
+    // are those of the token within the block (64 tokens per wave)
+    const int t0 = b * kPermuteTokens;
+    const int n = min(kPermuteTokens, T - t0) * K;
+    const int32_t *run = idx + (size_t)t0 * K;
+    for (int e = threadIdx.x; e < n; e += kUnroll * 256) {
+        int v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? run[e + u * 256] : -1;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int tt = (e + u * 256) / K;
+            if ((unsigned)v[u] < (unsigned)Nr) atomicOr(&mask[tt >> 6][v[u]], 1ull << (tt & 63));
         }
+    }
     __syncthreads();
-    if (!live) return;
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int k = 0; k < K; ++k) {
-        const int r = idx[(size_t)t * K + k];
-        if ((unsigned)r >= (unsigned)Nr) {
-            slot_of[(size_t)t * K + k] = -1;
-            continue;
+    for (int e = threadIdx.x; e < n; e += kUnroll * 256) {
+        int v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? run[e + u * 256] : -1;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int f = e + u * 256;
+            if (f >= n) continue;
+            const int r = v[u];
+            if ((unsigned)r >= (unsigned)Nr) {
+                slot_of[(size_t)t0 * K + f] = -1;
+                continue;
+            }
+            // rank of token tt among this block's tokens that chose r, in token order
+            const int tt = f / K, w = tt >> 6, l = tt & 63;
+            const unsigned long long below = l == 0 ? 0ull : (~0ull >> (64 - l));
+            int rank = __popcll(mask[w][r] & below);
+            for (int ww = 0; ww < w; ++ww) rank += __popcll(mask[ww][r]);
+            const int pos = s_first[r] + rank;
+            sorted_token[pos] = t0 + tt;
+            slot_of[(size_t)t0 * K + f] = pos;
         }
-        int rank = __popcll(mask[wave][r] & below);
-        for (int w = 0; w < wave; ++w) rank += __popcll(mask[w][r]);
-        const int pos = s_first[r] + rank;
-        sorted_token[pos] = t;
-        slot_of[(size_t)t * K + k] = pos;
     }
 }
 
