@@ -11,6 +11,8 @@ timed alongside for the fine/coarse ratio.  Other workloads: --config.
 
 Extra modes (used to produce the committed profile summaries):
   --copy-probe       also run a plain device copy of known size (counter calibration)
+  --zero-weights     zero every expert weight after upload (power probe: the same launches
+                     on operands that do not toggle; never a bench line of the workload)
   --ingest-pmc DIR   read rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs under DIR
                      and write profiles/traffic_<kernel>_<workload>.json
 """
@@ -125,6 +127,12 @@ def run(args) -> dict:
     wl = inp.wl
     log(f"[bench] {name}: {wl.description} (inputs in {time.perf_counter() - t_gen:.1f}s)")
     dl = DeviceLayer(inp, device="cuda:0")
+    if args.zero_weights:
+        for t in (dl.w1_r, dl.w3_r, dl.w2_r, dl.w1_s, dl.w3_s, dl.w2_s):
+            if t is not None:
+                t.zero_()
+        torch.cuda.synchronize()
+        log("[bench] expert weights zeroed (power probe)")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -210,7 +218,7 @@ def run(args) -> dict:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{name}: {wl.description}", "T": wl.T, "d": wl.d, "n_shared": wl.n_shared,
+        "config": {"workload": f"{name}: {wl.description}" + (" [power probe: expert weights zeroed]" if args.zero_weights else ""), "T": wl.T, "d": wl.d, "n_shared": wl.n_shared,
                    "n_routed": wl.n_routed, "top_k": wl.top_k, "inter": wl.inter, "parallelism": "none (1 GPU)"},
         "active_tflops": round(tflops, 2),
         "active_mfma_frac": round(tflops / mfma_peak, 4),
@@ -218,7 +226,7 @@ def run(args) -> dict:
         "stage_ms": breakdown,
         "roofline": roof,
     }
-    if coarse is not None and name == "c2b" and not args.no_pair:
+    if coarse is not None and name == "c2b" and not args.no_pair and not args.zero_weights:
         dc = DeviceLayer(coarse, device="cuda:0")
         for _ in range(args.warmup):
             dc.forward()
@@ -230,7 +238,7 @@ def run(args) -> dict:
         ms_a = (time.perf_counter() - t0) * 1e3 / args.steps
         out["pair"] = {"c2a_gshard_ms_per_step": round(ms_a, 4), "fine_over_coarse_time": round(ms / ms_a, 3)}
         del dc
-    if not args.no_cpu:
+    if not args.no_cpu and not args.zero_weights:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     return out
 
@@ -301,6 +309,7 @@ def main():
     ap.add_argument("--no-pair", action="store_true", help="skip timing the coarse c2a half")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--zero-weights", action="store_true", help="power probe: zero the expert weights")
     ap.add_argument("--ingest-pmc", default=None)
     ap.add_argument("--summarize-trace", default=None, help="rocprofv3 output dir to summarize")
     ap.add_argument("--trace-command", default="", help="command that produced --summarize-trace")

@@ -79,8 +79,7 @@ int moe_route(const moe_problem *p, const void *x, const float *centroids, const
     if ((x && !aligned16(x)) || !aligned16(centroids)) return MOE_ERR_INVALID_ARG;
     WsLayout L;
     if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
-    return hip_status(launch_route(*p, x, centroids, bias, idx, gate, probs, (float *)at(ws, L.route_eblk),
-                                   (int32_t *)at(ws, L.route_counts), (double *)at(ws, L.route_psum),
+    return hip_status(launch_route(*p, x, centroids, bias, idx, gate, probs, (int32_t *)at(ws, L.route_counts), (double *)at(ws, L.route_psum),
                                    counts, prob_sum, (hipStream_t)stream));
 }
 

@@ -29,7 +29,6 @@ inline size_t dtype_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 // Byte offsets of each call's scratch inside the caller's workspace.  The
 // regions are disjoint, so one workspace serves a whole layer pass.
 struct WsLayout {
-    size_t route_eblk;     // fp32   [d/8, N', 8]        centroids in blocked layout
     size_t route_counts;   // int32  [route_blocks, N']  per-block expert counts
     size_t route_psum;     // double [route_blocks, N']  per-block affinity sums
     size_t perm_hist;      // int32  [N', perm_blocks]   per-block histogram (expert-major)
@@ -50,7 +49,6 @@ inline WsLayout ws_layout(const moe_problem &p) {
     const size_t es = dtype_bytes(p.dtype);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes, 256); return at; };
-    L.route_eblk = take(nr * (size_t)p.d * sizeof(float));
     L.route_counts = take(rb * nr * sizeof(int32_t));
     L.route_psum = take(rb * nr * sizeof(double));
     L.perm_hist = take(pb * nr * sizeof(int32_t));
@@ -65,7 +63,7 @@ inline WsLayout ws_layout(const moe_problem &p) {
 
 hipError_t launch_route(const moe_problem &p, const void *x, const float *centroids,
                         const float *bias, int32_t *idx, float *gate, float *probs,
-                        float *centroids_blocked, int32_t *part_counts, double *part_psum,
+                        int32_t *part_counts, double *part_psum,
                         int32_t *counts, float *prob_sum, hipStream_t s);
 
 hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *offsets,

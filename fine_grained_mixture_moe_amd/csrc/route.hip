@@ -6,33 +6,28 @@
 // "【论文总结】MoE" section 2.2: the affinity is computed against a learnable
 // centroid e_i per expert.
 //
-// Three launches: the centroids are copied into a blocked layout (see
-// route_kernel), one launch computes logits, softmax, Top-K' and
-// per-workgroup partial statistics, and one sums the partials in a fixed
-// order.
+// Two launches: one computes logits, softmax, Top-K' and per-workgroup
+// partial statistics, one sums the partials in a fixed order.
 //
 // Logits.  Every z_{t,r} is ONE fused multiply-add chain over k = 0..d-1 in
 // ascending order starting from +0, so the value - and therefore the
 // selected experts - is reproducible bit for bit on any IEEE host.  No MFMA
 // and no split of k: both would change the summation order.  The work is
-// T*N' independent chains of length d; the kernel is built so that nothing
-// but the fma issue rate bounds it:
+// T*N' independent chains of length d:
 //   * lane = expert (l + 64 j for j < NJ), a wave owns RT consecutive tokens,
 //     so each lane runs RT*NJ independent chains;
+//   * the centroids are staged in LDS in chunks of 32 KB (KC values of k for
+//     all experts), double-buffered, and every wave of the workgroup reads
+//     them from there: one L2 read of E per workgroup instead of one per
+//     wave.  A chunk is stored as slices of 8 k, [slice][expert][8], so a
+//     step of a wave's 64 experts is one contiguous 2 KB span; E itself is
+//     read in its natural [N'][d] layout;
 //   * the token values are the same in every lane, so they feed the fma as
-//     its scalar operand: the wave loads its RT token rows in 128-byte
-//     chunks (one 16-byte piece per lane, ordinary vector loads issued 3
-//     to 4 chunks ahead), and each step moves the packed bf16 pairs it needs to
-//     SGPRs with v_readlane (one VALU op per two fmas of a lane's chain) and
-//     unpacks them on the scalar unit.  Scalar loads would save that op but
-//     return out of order, so a wave could not keep several in flight;
-//   * each lane streams its centroid values from L2 through a ring of P
-//     register stages (loads issued P steps of 8 k ahead), reused by the
-//     wave's RT tokens; no LDS and no barrier in the chain.
-// Measured on MI355X (why not more tokens per wave): with one wave per SIMD
-// an fma with independent neighbours still costs ~9-11 cycles of issue, with
-// 2-4 waves per SIMD ~5, so the kernel trades centroid reuse for waves.
-//
+//     its scalar operand: each wave loads its RT token rows of a chunk with
+//     ordinary vector loads (one 16-byte piece per lane, a chunk ahead) and
+//     each step moves the packed values it needs to SGPRs with v_readlane.
+//     Scalar loads would save that op but return out of order, and they
+//     share their wait counter with the LDS reads.
 // Selection, per token, with the wave holding every logit (bias added) of it:
 //   * softmax over the routed experts: maximum and sum by DPP row reductions
 //     (fixed order, so deterministic), fp32 exp;
@@ -44,6 +39,7 @@
 // The per-expert counts and fp64 affinity sums run over the wave's tokens in
 // order, then over the 4 waves in order.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -235,135 +231,193 @@ __device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int
     }
 }
 
-// RT tokens per wave, NJ expert lanes per lane, P register stages of 8 k of
-// centroids, PX stages of 128-byte token chunks.  The centroids come in the
-// blocked layout Eb[d/8][N'][8]: one step of a wave's 64 experts is one
-// contiguous 2 KB span (row-major rows would put the 64 lanes of every load
-// d*4 bytes apart; measured 2-3x slower at d >= 2048).
-template <int RT, int NJ, int P, int PX, bool XB>
-__global__ __launch_bounds__(256) void route_kernel(int T, int d, int Nr, int K, const void *__restrict__ x,
-                                                    const float *__restrict__ E, const float *__restrict__ bias,
-                                                    int32_t *__restrict__ idx, float *__restrict__ gate,
-                                                    float *__restrict__ probs, int32_t *__restrict__ part_counts,
-                                                    double *__restrict__ part_psum) {
-    constexpr int SPC = XB ? 8 : 4;   // steps of 8 k in a 128-byte token chunk
-    static_assert(RT <= 8, "one chunk load per wave");
-    static_assert((PX * SPC) % P == 0, "centroid ring slots repeat every PX chunks");
-    static_assert(P <= PX * SPC, "ring within a chunk group");
-    __shared__ double s_ps[4][NJ * 64];
-    __shared__ int s_cnt[4][NJ * 64];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int t0 = (blockIdx.x * 4 + wave) * RT;
+// W waves of RT tokens; NJ experts per lane.  Centroid chunks of KC k for
+// the padded NE = 64*NJ experts (64 B per thread: 32 KB with 8 waves) are
+// double-buffered in LDS; each thread fills two 32-byte pieces (8 k of one
+// expert), the KC/8 threads of an expert row reading its KC values
+// contiguously.  Slices are NE*32+16 bytes apart, so those writes land on
+// distinct banks.
+template <int RT, int NJ, int W, bool XB>
+__global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int K, const void *x, const float *E,
+                                                        const float *__restrict__ bias,
+                                                        int32_t *__restrict__ idx, float *__restrict__ gate,
+                                                        float *__restrict__ probs, int32_t *__restrict__ part_counts,
+                                                        double *__restrict__ part_psum) {
+    constexpr int NT = W * 64;
+    constexpr int NE = NJ * 64;
+    constexpr int KC = 16 * NT / NE;         // k per chunk (two 32-byte fill pieces per thread)
+    constexpr int SL = KC / 8;               // steps of 8 k per chunk
+    static_assert(KC >= 8 && KC <= 128 && KC % 8 == 0, "chunk of whole steps");
+    constexpr int SS = NE * 32 + 16;         // slice pitch (bytes)
+    constexpr int FR = NE * SL / NT;         // 32-byte fill pieces per thread
+    constexpr int ES = XB ? 2 : 4;           // token element bytes
+    constexpr int PPT = KC * ES / 16;        // 16-byte token pieces per token and chunk
+    constexpr int XPL = (RT * PPT + 63) / 64;
+    constexpr int NW = XB ? 4 : 8;           // 32-bit token words per step
+    static_assert(NE * SL % NT == 0, "whole fill rounds");
+    static_assert(W * NE * (8 + 4) <= 2 * SL * SS, "statistics fit in the chunk stages");
+    __shared__ __attribute__((aligned(16))) uint8_t s_e[2][SL * SS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t0 = (blockIdx.x * W + wave) * RT;
+
+    // ---- centroid fill: piece f of this thread is (expert row, slice) ----
+    int frow[FR], fsl[FR];
+    const float *fsrc[FR];
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+        const int pc = tid + f * NT;
+        frow[f] = pc / SL;
+        fsl[f] = pc % SL;
+        fsrc[f] = E + (size_t)min(frow[f], Nr - 1) * d;   // rows of absent experts repeat row N'-1
+    }
+    // (named registers, not an array: the array ended up in scratch memory)
+    static_assert(FR == 2, "two fill pieces per thread");
+    float4 fe0a, fe0b, fe1a, fe1b;
+    const float *fs0 = fsrc[0] + 8 * fsl[0], *fs1 = fsrc[1] + 8 * fsl[1];
+    const int flim0 = d - 8 - 8 * fsl[0], flim1 = d - 8 - 8 * fsl[1];
+    uint8_t *fd0 = &s_e[0][0] + fsl[0] * SS + frow[0] * 32, *fd1 = &s_e[0][0] + fsl[1] * SS + frow[1] * 32;
+#define MOE_FILL_LOAD(c)                                              \
+    {                                                                 \
+        const float *a_ = fs0 + min((c) * KC, flim0);                 \
+        const float *b_ = fs1 + min((c) * KC, flim1);                 \
+        fe0a = *(const float4 *)a_;                                   \
+        fe0b = *(const float4 *)(a_ + 4);                             \
+        fe1a = *(const float4 *)b_;                                   \
+        fe1b = *(const float4 *)(b_ + 4);                             \
+    }
+#define MOE_FILL_STORE(stg)                                           \
+    {                                                                 \
+        const int o_ = (stg) * (SL * SS);                             \
+        *(float4 *)(fd0 + o_) = fe0a;                                 \
+        *(float4 *)(fd0 + o_ + 16) = fe0b;                            \
+        *(float4 *)(fd1 + o_) = fe1a;                                 \
+        *(float4 *)(fd1 + o_ + 16) = fe1b;                            \
+    }
+    // ---- token pieces: piece p = i*PPT + q is bytes [16q, 16q+16) of token
+    //      t0+i within the chunk; lane l holds pieces l + 64u ----
+    const uint8_t *xsrc[XPL];
+    int xoff[XPL];
+#pragma unroll
+    for (int u = 0; u < XPL; ++u) {
+        const int pc = lane + 64 * u;
+        const int i = min(pc / PPT, RT - 1);
+        xsrc[u] = (const uint8_t *)x + (size_t)max(min(t0 + i, T - 1), 0) * d * ES;
+        xoff[u] = (pc % PPT) * 16;
+    }
+#define MOE_XLOAD(c, xr)                                                                  \
+    _Pragma("unroll") for (int u = 0; u < XPL; ++u)                                       \
+        xr[u] = *(const uint4 *)(xsrc[u] + min((c) * KC * ES + xoff[u], d * ES - 16));
+
+    float acc[RT][NJ];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = 0.0f;
+
+    // NS steps of chunk stage stg with token words xc: per step, the wave's
+    // centroid values from LDS, the RT tokens' words to SGPRs, then for each
+    // k of the step the fmas of all RT*NJ chains (independent neighbours)
+    auto compute = [&](auto ns_t, int stg, const uint4 (&xc)[XPL]) {
+        constexpr int NS = decltype(ns_t)::value;
+        const uint8_t *eb = s_e[stg] + lane * 32;
+        float4 ev[2][NJ][2];   // step st in ev[st & 1]; step st+1 is read while st computes
+        auto eread = [&](int st, float4 (&e)[NJ][2]) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                e[j][0] = *(const float4 *)(eb + st * SS + j * 64 * 32);
+                e[j][1] = *(const float4 *)(eb + st * SS + j * 64 * 32 + 16);
+            }
+        };
+        eread(0, ev[0]);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            if (st + 1 < NS) eread(st + 1, ev[(st + 1) & 1]);
+            float e8[NJ][8];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float4 a = ev[st & 1][j][0], b = ev[st & 1][j][1];
+                e8[j][0] = a.x; e8[j][1] = a.y; e8[j][2] = a.z; e8[j][3] = a.w;
+                e8[j][4] = b.x; e8[j][5] = b.y; e8[j][6] = b.z; e8[j][7] = b.w;
+            }
+            uint32_t w[RT][NW];
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+#pragma unroll
+                for (int h = 0; h < NW; ++h) {
+                    const int pp = i * PPT + (XB ? st : 2 * st + (h >> 2));
+                    const uint4 xv = xc[pp / 64];
+                    const uint32_t v = (h & 3) == 0 ? xv.x : (h & 3) == 1 ? xv.y : (h & 3) == 2 ? xv.z : xv.w;
+                    w[i][h] = (uint32_t)__builtin_amdgcn_readlane((int)v, pp % 64);
+                }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int i = 0; i < RT; ++i) {
+                    const float xv = XB ? __uint_as_float((kk & 1) ? (w[i][kk >> 1] & 0xffff0000u)
+                                                                   : (w[i][kk >> 1] << 16))
+                                        : __uint_as_float(w[i][kk]);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_fmaf(xv, e8[j][kk], acc[i][j]);
+                }
+            // one step at a time: the scheduler would otherwise hoist every
+            // step's readlanes and run out of SGPRs
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Full chunks in the loop: the loads of chunk c+1 (global -> registers)
+    // go out before chunk c is computed, the compiler barrier keeps them
+    // there, and they are stored to the other stage afterwards.  d % 64 == 0,
+    // so only KC = 128 can leave a last chunk of 64 k; the last iteration
+    // loads it (or re-loads the last full chunk into the idle stage).
+    const int nchunk = (d + KC - 1) / KC, nfull = d / KC;
+    uint4 xc[XPL], xn[XPL];
+    MOE_FILL_LOAD(0)
+    MOE_XLOAD(0, xc)
+    MOE_FILL_STORE(0)
+    __syncthreads();
+    for (int c = 0; c < nfull; ++c) {
+        const int cn = min(c + 1, nchunk - 1);
+        MOE_FILL_LOAD(cn)
+        MOE_XLOAD(cn, xn)
+        // keeps the loads above ahead of the compute
+        __builtin_amdgcn_sched_barrier(0);
+        compute(std::integral_constant<int, SL>{}, c & 1, xc);
+        MOE_FILL_STORE((c + 1) & 1)
+#pragma unroll
+        for (int u = 0; u < XPL; ++u) xc[u] = xn[u];
+        __syncthreads();
+    }
+    if (nfull < nchunk) compute(std::integral_constant<int, (SL / 2 > 0 ? SL / 2 : 1)>{}, nfull & 1, xc);
+#undef MOE_FILL_LOAD
+#undef MOE_FILL_STORE
+#undef MOE_XLOAD
 
     double ps[NJ];
     int cnt[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) { ps[j] = 0.0; cnt[j] = 0; }
+    if (t0 < T) finish_tokens<RT, NJ>(t0, min(RT, T - t0), Nr, K, lane, acc, bias, idx, gate, probs, ps, cnt);
 
-    if (t0 < T) {
-        // this lane's experts in the blocked centroids (absent experts read expert Nr-1; their logits are dropped)
-        const float *erow[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) erow[j] = E + (size_t)min(lane + 64 * j, Nr - 1) * 8;
-        const size_t estep = (size_t)Nr * 8;   // floats from one step to the next
-        // token chunks: lane 8i+q (i < RT) holds bytes [16q, 16q+16) of token t0+i's
-        // current 128-byte chunk (lanes past 8*RT repeat the last token; tokens
-        // past T read row T-1 and are not finished)
-        const int xi = min(lane >> 3, RT - 1), xq = lane & 7;
-        const uint8_t *xrow = (const uint8_t *)x + (size_t)min(t0 + xi, T - 1) * d * (XB ? 2 : 4) + xq * 16;
-        auto xload = [&](int c) -> uint4 { return *(const uint4 *)(xrow + (size_t)c * 128); };
-
-        float acc[RT][NJ];
-#pragma unroll
-        for (int i = 0; i < RT; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[i][j] = 0.0f;
-
-        float4 ering[P][NJ][2];
-        auto eload = [&](int st, int pe) {
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                ering[pe][j][0] = *(const float4 *)(erow[j] + (size_t)st * estep);
-                ering[pe][j][1] = *(const float4 *)(erow[j] + (size_t)st * estep + 4);
-            }
-        };
-        // nch is a multiple of PX (the launcher's choice) and nst of P, so the
-        // loop body has no branch: prefetches past the end re-read the last
-        // chunk / step (clamped), which keeps the load order the same in every
-        // iteration and lets each wait cover only the stage it consumes.
-        const int nch = d / (SPC * 8);
-        const int nst = d / 8;
-        uint4 xring[PX];
-#pragma unroll
-        for (int pc = 0; pc < PX; ++pc) xring[pc] = xload(pc);
-#pragma unroll
-        for (int pe = 0; pe < P; ++pe) eload(pe, pe);
-
-        for (int c0 = 0; c0 < nch; c0 += PX) {
-#pragma unroll
-            for (int pc = 0; pc < PX; ++pc) {
-                const int c = c0 + pc;
-                const uint4 xc = xring[pc];
-#pragma unroll
-                for (int q = 0; q < SPC; ++q) {
-                    const int st = c * SPC + q;
-                    const int pe = (pc * SPC + q) % P;
-                    float ev[NJ][8];
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const float4 a = ering[pe][j][0], b = ering[pe][j][1];
-                        ev[j][0] = a.x; ev[j][1] = a.y; ev[j][2] = a.z; ev[j][3] = a.w;
-                        ev[j][4] = b.x; ev[j][5] = b.y; ev[j][6] = b.z; ev[j][7] = b.w;
-                    }
-                    eload(min(st + P, nst - 1), pe);
-                    // the RT tokens' words of this step, moved to scalar registers;
-                    // then, for each k of the step, the fmas of all RT*NJ chains
-                    // (independent, so back-to-back issue never waits on a result)
-                    constexpr int NW = XB ? 4 : 8;
-                    uint32_t w[RT][NW];
-#pragma unroll
-                    for (int i = 0; i < RT; ++i)
-#pragma unroll
-                        for (int h = 0; h < NW; ++h) {
-                            const int src = XB ? i * 8 + q : i * 8 + 2 * q + (h >> 2);
-                            const uint32_t v = (h & 3) == 0 ? xc.x : (h & 3) == 1 ? xc.y : (h & 3) == 2 ? xc.z : xc.w;
-                            w[i][h] = (uint32_t)__builtin_amdgcn_readlane((int)v, src);
-                        }
-#pragma unroll
-                    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                        for (int i = 0; i < RT; ++i) {
-                            const float xv = XB ? __uint_as_float((kk & 1) ? (w[i][kk >> 1] & 0xffff0000u)
-                                                                           : (w[i][kk >> 1] << 16))
-                                                : __uint_as_float(w[i][kk]);
-#pragma unroll
-                            for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_fmaf(xv, ev[j][kk], acc[i][j]);
-                        }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                // the chunk is consumed: its stage takes chunk c + PX
-                xring[pc] = xload(min(c + PX, nch - 1));
-            }
-        }
-
-        finish_tokens<RT, NJ>(t0, min(RT, T - t0), Nr, K, lane, acc, bias, idx, gate, probs, ps, cnt);
-    }
-
-    // the 4 waves' per-expert sums, combined in wave order, at row blockIdx.x
+    // the W waves' per-expert sums, combined in wave order, at row blockIdx.x
+    // (the chunk stages are free after the last barrier of the loop)
+    double *s_ps = (double *)&s_e[0][0];
+    int *s_cnt = (int *)(s_ps + W * NE);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        s_ps[wave][lane + 64 * j] = ps[j];
-        s_cnt[wave][lane + 64 * j] = cnt[j];
+        s_ps[wave * NE + lane + 64 * j] = ps[j];
+        s_cnt[wave * NE + lane + 64 * j] = cnt[j];
     }
     __syncthreads();
-    for (int r = threadIdx.x; r < Nr; r += 256) {
+    for (int r = tid; r < Nr; r += NT) {
         double a = 0.0;
-        int c = 0;
+        int cc = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) { a += s_ps[w][r]; c += s_cnt[w][r]; }
+        for (int w = 0; w < W; ++w) { a += s_ps[w * NE + r]; cc += s_cnt[w * NE + r]; }
         part_psum[(size_t)blockIdx.x * Nr + r] = a;
-        part_counts[(size_t)blockIdx.x * Nr + r] = c;
+        part_counts[(size_t)blockIdx.x * Nr + r] = cc;
     }
 }
 
@@ -395,37 +449,35 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(
     }
 }
 
-// Tokens per wave: more waves per SIMD hide the chain and load latencies,
-// more tokens per wave reuse each centroid load; measured best: 4 from 8192
-// tokens, 2 from 1024, else 1.
-int route_tokens_per_wave(int T) { return T >= 8192 ? 4 : T >= 1024 ? 2 : 1; }
+// Waves per workgroup and tokens per wave, from a sweep of (2, 4, 8) x
+// (1, 2, 4) on MI355X: 8 waves from 2048 tokens (one centroid chunk read
+// serves 8 waves), 4 below (more CUs stream the centroids for small
+// batches); 2 tokens per wave from 4096 tokens and 4 from 16384 (each
+// centroid value read from LDS feeds more chains, while the chip keeps about
+// two waves per SIMD).
+int route_waves(int T) { return T >= 2048 ? 8 : 4; }
+int route_tokens_per_wave(int T) { return T >= 16384 ? 4 : T >= 4096 ? 2 : 1; }
 
-// Centroid register stages: about 16 steps of lookahead in fmas per lane
-// (RT*NJ*8 per step), at least 2, at most the steps of the token ring.  Token chunk
-// stages: 4 chunks ahead when the chunk count allows it, else 1.
-constexpr int ring_stages(int rt, int nj, int steps) {
-    return (16 / (rt * nj) < 2 ? 2 : 16 / (rt * nj)) < steps ? (16 / (rt * nj) < 2 ? 2 : 16 / (rt * nj)) : steps;
-}
-
-template <int RT, int NJ, int PX, bool XB>
-void launch_rtj(const moe_problem &p, int nblk, const void *x, const float *E, const float *bias, int32_t *idx,
+template <int RT, int W, bool XB>
+void launch_rtw(const moe_problem &p, int nblk, const void *x, const float *E, const float *bias, int32_t *idx,
                 float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
-    constexpr int P = ring_stages(RT, NJ, PX * (XB ? 8 : 4));
-    route_kernel<RT, NJ, P, PX, XB><<<nblk, 256, 0, s>>>(p.T, p.d, p.n_routed, p.top_k, x, E, bias, idx,
-                                                               gate, probs, pc, pp);
+    const int nj = cdiv(p.n_routed, 64);
+#define MOE_L(NJ) route_kernel<RT, NJ, W, XB><<<nblk, W * 64, 0, s>>>( \
+        p.T, p.d, p.n_routed, p.top_k, x, E, bias, idx, gate, probs, pc, pp)
+    if (nj == 1) MOE_L(1);
+    else if (nj == 2) MOE_L(2);
+    else MOE_L(4);
+#undef MOE_L
 }
 
 template <int RT, bool XB>
 void launch_rt(const moe_problem &p, int nblk, const void *x, const float *E, const float *bias, int32_t *idx,
                float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
-    const int nj = cdiv(p.n_routed, 64);
-    const int nch = p.d / (XB ? 64 : 32);
-#define MOE_L(NJ) (nch % 4 == 0 ? launch_rtj<RT, NJ, 4, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s) \
-                                : launch_rtj<RT, NJ, 1, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s))
-    if (nj == 1) MOE_L(1);
-    else if (nj == 2) MOE_L(2);
-    else MOE_L(4);
-#undef MOE_L
+    switch (route_waves(p.T)) {
+        case 8: launch_rtw<RT, 8, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+        case 4: launch_rtw<RT, 4, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+        default: launch_rtw<RT, 2, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+    }
 }
 
 template <bool XB>
@@ -438,33 +490,19 @@ void launch_route_typed(const moe_problem &p, int nblk, const void *x, const flo
     }
 }
 
-// Centroids [N'][d] -> blocked [d/8][N'][8].
-__global__ __launch_bounds__(256) void block_centroids_kernel(int Nr, int d, const float *__restrict__ E,
-                                                              float *__restrict__ Eb) {
-    const int64_t n = (int64_t)Nr * d / 4;   // float4 units (d % 64 == 0)
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const int64_t e = i * 4;
-        const int r = (int)(e / d), k = (int)(e % d);
-        *(float4 *)(Eb + ((int64_t)(k / 8) * Nr + r) * 8 + (k % 8)) = *(const float4 *)(E + e);
-    }
-}
-
 }  // namespace
 
-int route_blocks(int T) { return cdiv(T, 4 * route_tokens_per_wave(T)); }
+int route_blocks(int T) { return cdiv(T, route_waves(T) * route_tokens_per_wave(T)); }
 
 hipError_t launch_route(const moe_problem &p, const void *x, const float *centroids, const float *bias,
-                        int32_t *idx, float *gate, float *probs, float *centroids_blocked, int32_t *part_counts,
-                        double *part_psum, int32_t *counts, float *prob_sum, hipStream_t s) {
+                        int32_t *idx, float *gate, float *probs, int32_t *part_counts, double *part_psum,
+                        int32_t *counts, float *prob_sum, hipStream_t s) {
     const int nblk = p.T > 0 ? route_blocks(p.T) : 0;
     if (nblk > 0) {
-        const int64_t n4 = (int64_t)p.n_routed * p.d / 4;
-        const int gb = (int)std::min<int64_t>((n4 + 255) / 256, 1024);
-        block_centroids_kernel<<<gb, 256, 0, s>>>(p.n_routed, p.d, centroids, centroids_blocked);
         if (p.dtype == MOE_BF16)
-            launch_route_typed<true>(p, nblk, x, centroids_blocked, bias, idx, gate, probs, part_counts, part_psum, s);
+            launch_route_typed<true>(p, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
         else
-            launch_route_typed<false>(p, nblk, x, centroids_blocked, bias, idx, gate, probs, part_counts, part_psum, s);
+            launch_route_typed<false>(p, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

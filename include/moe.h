@@ -41,9 +41,9 @@
  *    undefined).
  *  - Expert weights, per expert, "out x in": W1 and W3 are [w, d], W2 is
  *    [d, w].  Shared experts are stacked [K_s, ...], routed [N', ...].
- *  - The workspace `ws` (size from moe_workspace_size) holds a blocked copy
- *    of the centroids, the per-block partial statistics, the grouping
- *    scratch and the SwiGLU activations.
+ *  - The workspace `ws` (size from moe_workspace_size) holds the per-block
+ *    partial routing statistics, the grouping scratch and the SwiGLU
+ *    activations.
  *    The calls use disjoint parts of it, so one workspace serves a whole
  *    layer pass on one stream.
  */
