@@ -43,11 +43,13 @@ SMALL = [
     (257, 128, 1, 100, 3, 128, "f32", 6, None, 5),
     (700, 128, 3, 2, 2, 192, "bf16", 7, None, 2),
     (130, 64, 0, 1, 1, 64, "f32", 8, None, 1),
-    (2500, 192, 1, 40, 5, 128, "bf16", 15, 1.1, 4),    # routing: 2 experts per wave, 64-wide chunks
-    (8300, 128, 0, 70, 4, 64, "f32", 16, None, 7),     # routing: 4 tokens per wave, 2 expert lanes, ragged T
-    (16500, 64, 0, 130, 3, 64, "bf16", 17, None, 5),   # routing: 8 tokens per wave, 3 expert lanes
+    (2500, 192, 1, 40, 5, 128, "bf16", 15, 1.1, 4),    # routing: 8 waves, 128-k chunks + a 64-k last chunk
+    (8300, 128, 0, 70, 4, 64, "f32", 16, None, 7),     # routing: 2 tokens per wave, 2 expert lanes, ragged T
+    (16500, 64, 0, 130, 3, 64, "bf16", 17, None, 5),   # routing: 4 tokens per wave, 3 of 4 expert lanes
     (5000, 64, 0, 256, 16, 64, "bf16", 18, 1.1, 8),    # routing: N'=256, K'=16, skewed
-    (9000, 2048, 1, 64, 6, 64, "bf16", 19, 1.1, 4),    # routing: large d, 4 tokens per wave
+    (9000, 2048, 1, 64, 6, 64, "bf16", 19, 1.1, 4),    # routing: large d, 16 chunks
+    (16400, 192, 0, 32, 4, 64, "f32", 20, None, 4),    # routing: fp32 tokens, 2 pieces per lane, last chunk
+    (16400, 64, 0, 48, 2, 64, "f32", 21, None, 4),     # routing: d below one chunk (no full chunk)
 ]
 
 
@@ -128,5 +130,5 @@ def test_two_runs_are_bitwise_identical():
     dl.forward()
     b = dl.results()
     for k in ("idx", "gate", "probs", "counts", "prob_sum", "offsets", "sorted_token", "slot_of", "y_routed",
-              "y_shared", "h", "f", "P"):
+              "y_shared", "h", "f", "P", "f_dev", "P_dev", "exp_bal", "dev_bal"):
         assert np.array_equal(a[k], b[k]), k
