@@ -1,5 +1,6 @@
 /*
- * moe_oracle.c -- plain, slow CPU oracle of the DeepSeekMoE layer forward.
+ * moe_oracle.c -- plain, slow CPU oracle of the DeepSeekMoE layer forward and
+ * its backward pass.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the checker the HIP path is
  * compared against.  Only the tests, the smoke check and the benchmark's CPU
@@ -347,4 +348,233 @@ int oracle_forward(int n_tok, int d, int Ks, int Nr, int K, int w, int D,
     free(idx); free(gate); free(counts); free(psum); free(offsets); free(sorted);
     free(slot); free(tokens); free(f); free(P); free(fd); free(Pd);
     return rc;
+}
+
+/* ========================================================================
+ * Backward pass of the layer (training is the setting of [S] "Method
+ * details", whose loss adds alpha_1 * ExpBal + alpha_2 * DevBal to the task
+ * loss).  Given dh = dL_task/dh [T, d] the gradients follow from the chain
+ * rule on the forward definitions above, in fp64:
+ *
+ *   per used (t, e) with upstream dy (dy = g_{t,k} dh_t for a routed pair,
+ *   dy = dh_t for a shared expert):
+ *     da_j = sum_i W2[i,j] dy_i
+ *     dq_j = da_j SiLU(p_j),  dp_j = da_j q_j sig_j (1 + p_j (1 - sig_j))
+ *     dx_t += sum_j W1[j,:] dp_j + W3[j,:] dq_j
+ *     dW2 += dy a^T,  dW1 += dp x_t^T,  dW3 += dq x_t^T
+ *   routed pair:  dg_{t,k} = dh_t . FFN_e(u_t)
+ *   router:  ds_{t,r} = dg_{t,k} (r = idx[t,k]) + alpha_1 f_r / T
+ *                       + alpha_2 f'_{group(r)} / T
+ *            dz_{t,r} = s_{t,r} (ds_{t,r} - sum_r' s_{t,r'} ds_{t,r'})
+ *            dx_t += sum_r dz_{t,r} e_r,  dE_r = sum_t dz_{t,r} u_t,
+ *            dbias_r = sum_t dz_{t,r}
+ *   plus the residual: dx_t += dh_t.
+ *
+ * Readings (the pages give the losses, not their gradients): the Top-K
+ * selection is held fixed (it is piecewise constant); f and f' are counts
+ * of that selection, so they are constants; P and P' are differentiable
+ * through the softmax.  The affinities s and gates g are the forward's
+ * outputs (probs, gate).
+ * ====================================================================== */
+
+/* p, q, a of one expert on one token (fp64). */
+static void ffn_hidden(int d, int w, const float *u, const float *W1, const float *W3,
+                       double *p, double *q, double *a) {
+    for (int j = 0; j < w; ++j) {
+        double pj = 0.0, qj = 0.0;
+        const float *r1 = W1 + (size_t)j * d, *r3 = W3 + (size_t)j * d;
+        for (int k = 0; k < d; ++k) {
+            pj += (double)r1[k] * (double)u[k];
+            qj += (double)r3[k] * (double)u[k];
+        }
+        p[j] = pj;
+        q[j] = qj;
+        a[j] = pj / (1.0 + exp(-pj)) * qj;
+    }
+}
+
+/* da -> dp, dq (SwiGLU backward). */
+static void swiglu_backward(int w, const double *p, const double *q, const double *da,
+                            double *dp, double *dq) {
+    for (int j = 0; j < w; ++j) {
+        const double sg = 1.0 / (1.0 + exp(-p[j]));
+        dq[j] = da[j] * p[j] * sg;
+        dp[j] = da[j] * q[j] * sg * (1.0 + p[j] * (1.0 - sg));
+    }
+}
+
+/* da_j = sum_i W2[i,j] dy_i */
+static void down_backward(int d, int w, const float *W2, const double *dy, double *da) {
+    for (int j = 0; j < w; ++j) da[j] = 0.0;
+    for (int i = 0; i < d; ++i) {
+        const float *r2 = W2 + (size_t)i * w;
+        const double v = dy[i];
+        for (int j = 0; j < w; ++j) da[j] += (double)r2[j] * v;
+    }
+}
+
+/* dx += W1^T dp + W3^T dq */
+static void up_backward_dx(int d, int w, const float *W1, const float *W3, const double *dp,
+                           const double *dq, double *dx) {
+    for (int j = 0; j < w; ++j) {
+        const float *r1 = W1 + (size_t)j * d, *r3 = W3 + (size_t)j * d;
+        for (int k = 0; k < d; ++k) dx[k] += (double)r1[k] * dp[j] + (double)r3[k] * dq[j];
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Per-token part of the backward for the listed tokens (tokens[n]):
+ *   dgate[n, k]  = dh_t . FFN_{idx[t,k]}(u_t)
+ *   dz[n, r]     = router logit gradient (NULL: not written)
+ *   dx[n, :]     = dh_t + FFN part + router part
+ * T is the whole batch (it scales the balance-loss terms).  groups D
+ * divides N'.  f [N'], fdev [D] are the forward's statistics.
+ * ---------------------------------------------------------------------- */
+void oracle_backward_tokens(int n_tok, const int32_t *tokens, int T, int d, int Ks, int Nr,
+                            int K, int w, int D, double alpha1, double alpha2,
+                            const float *x, const float *E, const int32_t *idx,
+                            const float *gate, const float *probs, const float *f,
+                            const float *fdev, const float *W1s, const float *W3s,
+                            const float *W2s, const float *W1r, const float *W3r,
+                            const float *W2r, const float *dh, double *dgate, double *dz,
+                            double *dx) {
+    const size_t up = (size_t)w * d, down = (size_t)d * w;
+    const int gsz = (Nr > 0 && D > 0) ? Nr / D : 1;
+    #pragma omp parallel
+    {
+        const size_t nw = (size_t)(w > 0 ? w : 1), nd = (size_t)(d > 0 ? d : 1);
+        double *p = (double *)malloc(nw * sizeof(double)), *q = (double *)malloc(nw * sizeof(double));
+        double *a = (double *)malloc(nw * sizeof(double)), *da = (double *)malloc(nw * sizeof(double));
+        double *dp = (double *)malloc(nw * sizeof(double)), *dq = (double *)malloc(nw * sizeof(double));
+        double *dy = (double *)malloc(nd * sizeof(double)), *dxt = (double *)malloc(nd * sizeof(double));
+        double *ds = (double *)malloc((size_t)(Nr > 0 ? Nr : 1) * sizeof(double));
+        #pragma omp for schedule(dynamic, 1)
+        for (int n = 0; n < n_tok; ++n) {
+            const int t = tokens[n];
+            const float *u = x + (size_t)t * d, *g = dh + (size_t)t * d;
+            for (int i = 0; i < d; ++i) dxt[i] = (double)g[i];
+            for (int e = 0; e < Ks; ++e) {
+                for (int i = 0; i < d; ++i) dy[i] = (double)g[i];
+                ffn_hidden(d, w, u, W1s + e * up, W3s + e * up, p, q, a);
+                down_backward(d, w, W2s + e * down, dy, da);
+                swiglu_backward(w, p, q, da, dp, dq);
+                up_backward_dx(d, w, W1s + e * up, W3s + e * up, dp, dq, dxt);
+            }
+            for (int r = 0; r < Nr; ++r) ds[r] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const int r = idx[(size_t)t * K + k];
+                const float *W1 = W1r + r * up, *W3 = W3r + r * up, *W2 = W2r + r * down;
+                ffn_hidden(d, w, u, W1, W3, p, q, a);
+                double dgk = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    double yi = 0.0;
+                    const float *r2 = W2 + (size_t)i * w;
+                    for (int j = 0; j < w; ++j) yi += (double)r2[j] * a[j];
+                    dgk += (double)g[i] * yi;
+                }
+                if (dgate) dgate[(size_t)n * K + k] = dgk;
+                ds[r] += dgk;
+                const double gk = (double)gate[(size_t)t * K + k];
+                for (int i = 0; i < d; ++i) dy[i] = gk * (double)g[i];
+                down_backward(d, w, W2, dy, da);
+                swiglu_backward(w, p, q, da, dp, dq);
+                up_backward_dx(d, w, W1, W3, dp, dq, dxt);
+            }
+            if (Nr > 0) {
+                double dot = 0.0;
+                for (int r = 0; r < Nr; ++r) {
+                    ds[r] += alpha1 * (double)f[r] / (double)T + alpha2 * (double)fdev[r / gsz] / (double)T;
+                    dot += (double)probs[(size_t)t * Nr + r] * ds[r];
+                }
+                for (int r = 0; r < Nr; ++r) {
+                    const double z = (double)probs[(size_t)t * Nr + r] * (ds[r] - dot);
+                    if (dz) dz[(size_t)n * Nr + r] = z;
+                    const float *er = E + (size_t)r * d;
+                    for (int i = 0; i < d; ++i) dxt[i] += z * (double)er[i];
+                }
+            }
+            if (dx) memcpy(dx + (size_t)n * d, dxt, (size_t)d * sizeof(double));
+        }
+        free(p); free(q); free(a); free(da); free(dp); free(dq); free(dy); free(dxt); free(ds);
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Router parameter gradients from the logit gradients of ALL T tokens
+ * (dz [T, N'] from oracle_backward_tokens over every token):
+ *   dE[r, :] = sum_t dz[t, r] u_t (t ascending),  dbias[r] = sum_t dz[t, r]
+ * ---------------------------------------------------------------------- */
+void oracle_backward_router(int T, int d, int Nr, const float *x, const double *dz,
+                            double *dE, double *dbias) {
+    #pragma omp parallel for schedule(static)
+    for (int r = 0; r < Nr; ++r) {
+        double *er = dE + (size_t)r * d;
+        double b = 0.0;
+        for (int i = 0; i < d; ++i) er[i] = 0.0;
+        for (int t = 0; t < T; ++t) {
+            const double z = dz[(size_t)t * Nr + r];
+            b += z;
+            const float *u = x + (size_t)t * d;
+            for (int i = 0; i < d; ++i) er[i] += z * (double)u[i];
+        }
+        dbias[r] = b;
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Weight gradients of one expert, selected rows only.  Expert e is global
+ * (e < Ks shared, else routed r = e - Ks).  Its tokens: every token for a
+ * shared expert (dy = dh_t); the tokens t with idx[t,k] == r for a routed
+ * one (dy = gate[t,k] dh_t), t ascending.
+ *   dW1[rows1[n], :], dW3[rows1[n], :]   (n < n1; rows of [w, d])
+ *   dW2[rows2[n], :]                     (n < n2; rows of [d, w])
+ * ---------------------------------------------------------------------- */
+void oracle_backward_weight_rows(int e, int T, int d, int Ks, int K, int w, const float *x,
+                                 const int32_t *idx, const float *gate, const float *W1s,
+                                 const float *W3s, const float *W2s, const float *W1r,
+                                 const float *W3r, const float *W2r, const float *dh,
+                                 int n1, const int32_t *rows1, double *dW1, double *dW3,
+                                 int n2, const int32_t *rows2, double *dW2) {
+    const size_t up = (size_t)w * d, down = (size_t)d * w;
+    const int sh = e < Ks;
+    const int r = e - Ks;
+    const float *W1 = sh ? W1s + e * up : W1r + r * up;
+    const float *W3 = sh ? W3s + e * up : W3r + r * up;
+    const float *W2 = sh ? W2s + e * down : W2r + r * down;
+    for (size_t i = 0; i < (size_t)n1 * d; ++i) { dW1[i] = 0.0; dW3[i] = 0.0; }
+    for (size_t i = 0; i < (size_t)n2 * w; ++i) dW2[i] = 0.0;
+    const size_t nw = (size_t)(w > 0 ? w : 1), nd = (size_t)(d > 0 ? d : 1);
+    double *p = (double *)malloc(nw * sizeof(double)), *q = (double *)malloc(nw * sizeof(double));
+    double *a = (double *)malloc(nw * sizeof(double)), *da = (double *)malloc(nw * sizeof(double));
+    double *dp = (double *)malloc(nw * sizeof(double)), *dq = (double *)malloc(nw * sizeof(double));
+    double *dy = (double *)malloc(nd * sizeof(double));
+    for (int t = 0; t < T; ++t) {
+        double scale;
+        if (sh) {
+            scale = 1.0;
+        } else {
+            int kk = -1;
+            for (int k = 0; k < K; ++k)
+                if (idx[(size_t)t * K + k] == r) kk = k;
+            if (kk < 0) continue;
+            scale = (double)gate[(size_t)t * K + kk];
+        }
+        const float *u = x + (size_t)t * d, *g = dh + (size_t)t * d;
+        for (int i = 0; i < d; ++i) dy[i] = scale * (double)g[i];
+        ffn_hidden(d, w, u, W1, W3, p, q, a);
+        down_backward(d, w, W2, dy, da);
+        swiglu_backward(w, p, q, da, dp, dq);
+        for (int n = 0; n < n1; ++n) {
+            const int j = rows1[n];
+            for (int k = 0; k < d; ++k) {
+                dW1[(size_t)n * d + k] += dp[j] * (double)u[k];
+                dW3[(size_t)n * d + k] += dq[j] * (double)u[k];
+            }
+        }
+        for (int n = 0; n < n2; ++n) {
+            const double v = dy[rows2[n]];
+            for (int j = 0; j < w; ++j) dW2[(size_t)n * w + j] += v * a[j];
+        }
+    }
+    free(p); free(q); free(a); free(da); free(dp); free(dq); free(dy);
 }

@@ -46,6 +46,14 @@ def lib():
         L.oracle_forward.argtypes = [_i, _i, _i, _i, _i, _i, _i, _f32p, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _f64p, _f32p, _f32p]
         L.oracle_forward.restype = _i
+        _d = ctypes.c_double
+        L.oracle_backward_tokens.argtypes = [_i, _i32p, _i, _i, _i, _i, _i, _i, _i, _d, _d, _f32p, _vp,
+                                             _i32p, _f32p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _f32p, _vp, _vp, _vp]
+        L.oracle_backward_router.argtypes = [_i, _i, _i, _f32p, _f64p, _f64p, _f64p]
+        L.oracle_backward_weight_rows.argtypes = [_i, _i, _i, _i, _i, _i, _f32p, _i32p, _f32p, _vp, _vp,
+                                                  _vp, _vp, _vp, _vp, _f32p, _i, _i32p, _f64p, _f64p,
+                                                  _i, _i32p, _f64p]
         _lib = L
     return _lib
 
@@ -180,3 +188,89 @@ def forward(n_tok: int, x, E, bias, top_k: int, groups: int, w1_s, w3_s, w2_s, w
     if rc != 0:
         raise ValueError("oracle_forward failed")
     return h, float(eb[0]), float(db[0])
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (see moe_oracle.c for the chain-rule formulas and readings).
+# ---------------------------------------------------------------------------
+
+def _weights(w1_s, w3_s, w2_s, w1_r, w3_r, w2_r):
+    ws = [None if a is None or np.size(a) == 0 else _c(a) for a in (w1_s, w3_s, w2_s)]
+    wr = [None if a is None or np.size(a) == 0 else _c(a) for a in (w1_r, w3_r, w2_r)]
+    Ks = 0 if ws[0] is None else ws[0].shape[0]
+    Nr = 0 if wr[0] is None else wr[0].shape[0]
+    w = (ws[0] if Ks else wr[0]).shape[1]
+    return ws, wr, Ks, Nr, w
+
+
+def backward_tokens(tokens, x, E, idx, gate, probs, f, f_dev, alpha1: float, alpha2: float, dh,
+                    w1_s, w3_s, w2_s, w1_r, w3_r, w2_r):
+    """Per-token backward for the listed tokens.
+
+    -> dict(dgate [n,K'] fp64, dz [n,N'] fp64, dx [n,d] fp64).  probs [T,N'], f [N'], f_dev [D]
+    are the forward's outputs; dh [T,d] the upstream gradient; alpha1/alpha2 weight ExpBal/DevBal.
+    """
+    tokens = _c(tokens, np.int32)
+    x, dh = _c(x), _c(dh)
+    T, d = x.shape
+    ws, wr, Ks, Nr, w = _weights(w1_s, w3_s, w2_s, w1_r, w3_r, w2_r)
+    n = tokens.shape[0]
+    if Nr:
+        idx = _c(idx, np.int32).reshape(T, -1)
+        K = idx.shape[1]
+        gate = _c(gate).reshape(T, K)
+        probs, f, f_dev, E = _c(probs), _c(f), _c(f_dev), _c(E)
+        D = f_dev.shape[0]
+    else:
+        K, D = 0, 1
+        idx = np.zeros(1, np.int32)
+        gate = np.zeros(1, np.float32)
+    dgate = np.empty((n, max(K, 1)), np.float64)
+    dz = np.empty((n, max(Nr, 1)), np.float64)
+    dx = np.empty((n, d), np.float64)
+    lib().oracle_backward_tokens(n, tokens, T, d, Ks, Nr, K, w, D, float(alpha1), float(alpha2), x,
+                                 _ptr(E) if Nr else None, idx, gate,
+                                 _ptr(probs) if Nr else None, _ptr(f) if Nr else None,
+                                 _ptr(f_dev) if Nr else None,
+                                 *[_ptr(a) for a in ws], *[_ptr(a) for a in wr], dh,
+                                 _ptr(dgate), _ptr(dz), _ptr(dx))
+    return dict(dgate=dgate[:, :K], dz=dz[:, :Nr], dx=dx)
+
+
+def backward_router(x, dz):
+    """dE [N',d] = dz^T x and dbias [N'] = column sums of dz, from dz [T,N'] of every token (fp64)."""
+    x = _c(x)
+    dz = _c(dz, np.float64)
+    T, d = x.shape
+    Nr = dz.shape[1]
+    dE = np.empty((Nr, d), np.float64)
+    db = np.empty(Nr, np.float64)
+    lib().oracle_backward_router(T, d, Nr, x, dz, dE, db)
+    return dE, db
+
+
+def backward_weight_rows(e: int, x, idx, gate, dh, w1_s, w3_s, w2_s, w1_r, w3_r, w2_r,
+                         rows_up, rows_down):
+    """Selected rows of the weight gradients of global expert e (shared first).
+
+    -> (dW1 [n1,d], dW3 [n1,d], dW2 [n2,w]) fp64 for rows_up of [w,d] and rows_down of [d,w].
+    """
+    x, dh = _c(x), _c(dh)
+    T, d = x.shape
+    ws, wr, Ks, Nr, w = _weights(w1_s, w3_s, w2_s, w1_r, w3_r, w2_r)
+    if Nr:
+        idx = _c(idx, np.int32).reshape(T, -1)
+        K = idx.shape[1]
+        gate = _c(gate).reshape(T, K)
+    else:
+        K = 0
+        idx = np.zeros(1, np.int32)
+        gate = np.zeros(1, np.float32)
+    r1 = _c(rows_up, np.int32)
+    r2 = _c(rows_down, np.int32)
+    dW1 = np.empty((max(r1.size, 1), d), np.float64)
+    dW3 = np.empty((max(r1.size, 1), d), np.float64)
+    dW2 = np.empty((max(r2.size, 1), w), np.float64)
+    lib().oracle_backward_weight_rows(int(e), T, d, Ks, K, w, x, idx, gate, *[_ptr(a) for a in ws],
+                                      *[_ptr(a) for a in wr], dh, r1.size, r1, dW1, dW3, r2.size, r2, dW2)
+    return dW1[:r1.size], dW3[:r1.size], dW2[:r2.size]
