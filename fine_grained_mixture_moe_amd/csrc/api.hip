@@ -2,7 +2,7 @@
 //
 // Host side only: argument validation (before anything is enqueued), the
 // workspace layout, and dispatch to the kernels of route.hip, permute.hip,
-// expert_ffn.hip and combine_stats.hip.
+// expert_ffn.hip, combine_stats.hip and backward.hip.
 #include <stdint.h>
 
 #include "moe_internal.h"
@@ -222,6 +222,85 @@ int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *count
     if (!counts || !prob_sum || !f || !P || !f_dev || !P_dev || !exp_bal || !dev_bal) return MOE_ERR_INVALID_ARG;
     return hip_status(launch_balance_stats(*p, groups, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, dev_bal,
                                            (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// backward pass
+// ---------------------------------------------------------------------------
+
+int moe_backward_workspace_size(const moe_problem *p, size_t *bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    const int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    *bytes = bwd_ws_layout(*p).total;
+    return MOE_OK;
+}
+
+int moe_combine_backward(const moe_problem *p, const void *dh, const void *y_routed, const float *gate,
+                         const int32_t *slot_of, void *dy_routed, float *dgate, void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if ((int64_t)p->T * p->top_k == 0) return MOE_OK;
+    if (!dh || !y_routed || !gate || !slot_of || !dy_routed || !dgate) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(dh) || !aligned16(y_routed) || !aligned16(dy_routed)) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_combine_backward(*p, dh, y_routed, gate, slot_of, dy_routed, dgate,
+                                              (hipStream_t)stream));
+}
+
+int moe_expert_ffn_backward(const moe_problem *p, const void *x, const int32_t *offsets,
+                            const int32_t *sorted_token, const int32_t *slot_of, const void *w1_routed,
+                            const void *w3_routed, const void *w2_routed, const void *w1_shared,
+                            const void *w3_shared, const void *w2_shared, const void *dh, const void *dy_routed,
+                            float *dx_ffn, float *dw1_routed, float *dw3_routed, float *dw2_routed,
+                            float *dw1_shared, float *dw3_shared, float *dw2_shared, void *ws, size_t ws_bytes,
+                            void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    const bool routed = p->n_routed > 0, shared = p->n_shared > 0;
+    if (routed && (!offsets || !w1_routed || !w3_routed || !w2_routed || !dw1_routed || !dw3_routed || !dw2_routed))
+        return MOE_ERR_INVALID_ARG;
+    if (routed && p->T > 0 && (!sorted_token || !slot_of || !dy_routed)) return MOE_ERR_INVALID_ARG;
+    if (shared && (!w1_shared || !w3_shared || !w2_shared || !dw1_shared || !dw3_shared || !dw2_shared))
+        return MOE_ERR_INVALID_ARG;
+    if (p->T > 0 && (!x || !dh || !dx_ffn)) return MOE_ERR_INVALID_ARG;
+    for (const void *q : {x, dh, dy_routed, (const void *)dx_ffn, w1_routed, w3_routed, w2_routed, w1_shared,
+                          w3_shared, w2_shared, (const void *)dw1_routed, (const void *)dw3_routed,
+                          (const void *)dw2_routed, (const void *)dw1_shared, (const void *)dw3_shared,
+                          (const void *)dw2_shared})
+        if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
+    const BwdWsLayout L = bwd_ws_layout(*p);
+    if (L.total > 0 && (!ws || ws_bytes < L.total || ((uintptr_t)ws & 255u) != 0)) return MOE_ERR_WORKSPACE;
+    BwdFfnArgs a{};
+    a.x = x; a.dh = dh; a.dy_routed = dy_routed;
+    a.offsets = offsets; a.sorted_token = sorted_token; a.slot_of = slot_of;
+    a.w1_r = w1_routed; a.w3_r = w3_routed; a.w2_r = w2_routed;
+    a.w1_s = w1_shared; a.w3_s = w3_shared; a.w2_s = w2_shared;
+    a.da_r = at(ws, L.da_r); a.dp_r = at(ws, L.dp_r); a.dq_r = at(ws, L.dq_r); a.a_r = at(ws, L.a_r);
+    a.da_s = at(ws, L.da_s); a.dp_s = at(ws, L.dp_s); a.dq_s = at(ws, L.dq_s); a.a_s = at(ws, L.a_s);
+    a.dxr = (float *)at(ws, L.dxr); a.dxs = (float *)at(ws, L.dxs); a.dx_ffn = dx_ffn;
+    a.dw1_r = dw1_routed; a.dw3_r = dw3_routed; a.dw2_r = dw2_routed;
+    a.dw1_s = dw1_shared; a.dw3_s = dw3_shared; a.dw2_s = dw2_shared;
+    return hip_status(launch_expert_backward(*p, a, (hipStream_t)stream));
+}
+
+int moe_route_backward(const moe_problem *p, int32_t groups, float alpha1, float alpha2, const void *x,
+                       const float *centroids, const float *probs, const int32_t *idx, const float *dgate,
+                       const float *f, const float *f_dev, const void *dh, const float *dx_ffn, float *dx,
+                       float *dcentroids, float *dbias, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (p->n_routed < 1) return MOE_ERR_INVALID_ARG;
+    if (p->n_routed > kRouteMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if (groups < 1 || p->n_routed % groups != 0) return MOE_ERR_INVALID_ARG;
+    if (!centroids || !f || !f_dev || !dcentroids) return MOE_ERR_INVALID_ARG;
+    if (p->T > 0 && (!x || !probs || !idx || !dgate || !dh || !dx)) return MOE_ERR_INVALID_ARG;
+    for (const void *q : {x, dh, (const void *)dx_ffn, (const void *)dx, (const void *)centroids})
+        if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
+    const BwdWsLayout L = bwd_ws_layout(*p);
+    if (L.total > 0 && (!ws || ws_bytes < L.total || ((uintptr_t)ws & 255u) != 0)) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_route_backward(*p, groups, alpha1, alpha2, x, centroids, probs, idx, dgate, f, f_dev,
+                                            dh, dx_ffn, dx, dcentroids, dbias, (float *)at(ws, L.dz),
+                                            (float *)at(ws, L.de_part), (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -93,4 +93,63 @@ hipError_t launch_balance_stats(const moe_problem &p, int groups, const int32_t 
                                 const float *prob_sum, float *f, float *P, float *f_dev,
                                 float *P_dev, float *exp_bal, float *dev_bal, hipStream_t s);
 
+// ---- backward pass (backward.hip) ------------------------------------------
+
+// Token chunks of the centroid-gradient partial sums.
+int route_backward_chunks(int T);
+
+// Byte offsets of the backward scratch inside the caller's backward workspace.
+struct BwdWsLayout {
+    size_t da_r, dp_r, dq_r, a_r;   // dtype [T*K', w]
+    size_t da_s, dp_s, dq_s, a_s;   // dtype [T, K_s*w]
+    size_t dxr;                     // fp32  [T*K', d]   dx of every grouped row
+    size_t dxs;                     // fp32  [T, d]      dx of the shared experts
+    size_t dz;                      // fp32  [T, N']     router logit gradient
+    size_t de_part;                 // fp32  [chunks, N', d+4] centroid-gradient partials
+    size_t total;
+};
+
+inline BwdWsLayout bwd_ws_layout(const moe_problem &p) {
+    BwdWsLayout L{};
+    const size_t es = dtype_bytes(p.dtype);
+    const size_t tk = (size_t)p.T * p.top_k, ts = (size_t)p.T * p.n_shared;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes, 256); return at; };
+    L.da_r = take(tk * p.inter * es);
+    L.dp_r = take(tk * p.inter * es);
+    L.dq_r = take(tk * p.inter * es);
+    L.a_r = take(tk * p.inter * es);
+    L.da_s = take(ts * p.inter * es);
+    L.dp_s = take(ts * p.inter * es);
+    L.dq_s = take(ts * p.inter * es);
+    L.a_s = take(ts * p.inter * es);
+    L.dxr = take(tk * p.d * sizeof(float));
+    L.dxs = take((p.n_shared > 0 ? (size_t)p.T : 0) * p.d * sizeof(float));
+    L.dz = take((size_t)p.T * p.n_routed * sizeof(float));
+    L.de_part = take((size_t)route_backward_chunks(p.T) * p.n_routed * (p.d + 4) * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+hipError_t launch_combine_backward(const moe_problem &p, const void *dh, const void *y_routed,
+                                   const float *gate, const int32_t *slot_of, void *dy_routed,
+                                   float *dgate, hipStream_t s);
+
+struct BwdFfnArgs {
+    const void *x, *dh, *dy_routed;
+    const int32_t *offsets, *sorted_token, *slot_of;
+    const void *w1_r, *w3_r, *w2_r, *w1_s, *w3_s, *w2_s;
+    void *da_r, *dp_r, *dq_r, *a_r, *da_s, *dp_s, *dq_s, *a_s;
+    float *dxr, *dxs, *dx_ffn;
+    float *dw1_r, *dw3_r, *dw2_r, *dw1_s, *dw3_s, *dw2_s;
+};
+hipError_t launch_expert_backward(const moe_problem &p, const BwdFfnArgs &a, hipStream_t s);
+
+hipError_t launch_route_backward(const moe_problem &p, int groups, float alpha1, float alpha2,
+                                 const void *x, const float *centroids, const float *probs,
+                                 const int32_t *idx, const float *dgate, const float *f,
+                                 const float *f_dev, const void *dh, const float *dx_ffn, float *dx,
+                                 float *dcentroids, float *dbias, float *dz, float *part,
+                                 hipStream_t s);
+
 }  // namespace moe

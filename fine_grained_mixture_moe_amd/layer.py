@@ -137,6 +137,63 @@ class DeviceLayer:
         self.expert_ffn(stream)
         self.combine(stream)
 
+    # -- backward pass -----------------------------------------------------
+    def backward(self, dh: np.ndarray, alpha1: float, alpha2: float, stream=None):
+        """Backward pass through the three backward calls, for upstream gradient dh [T, d].
+
+        dh is fp32 values (bf16 bits for a bf16 layer: pass the exact upcast of
+        bf16 values).  Needs a forward with want_probs=True and the statistics.
+        Leaves dx, dcentroids, dbias, dgate and the weight gradients (fp32) on
+        the device.
+        """
+        torch = _torch()
+        p = self.prob
+        T, d, Ks, Nr, w = p.T, p.d, p.n_shared, p.n_routed, p.inter
+        K = p.top_k
+        dev = self.device
+        f32 = torch.float32
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        if not hasattr(self, "bws"):
+            self.bws_bytes = M.moe_backward_workspace_size(p)
+            self.bws = torch.empty(max(self.bws_bytes, 256), dtype=torch.uint8, device=dev)
+            self.dy_routed = torch.empty((max(T * K, 1), d), dtype=tdt, device=dev)
+            self.dgate = torch.empty((T, K), dtype=f32, device=dev)
+            self.dx_ffn = torch.empty((T, d), dtype=f32, device=dev)
+            self.dx = torch.empty((T, d), dtype=f32, device=dev)
+            self.dw1_r = torch.empty((Nr, w, d), dtype=f32, device=dev) if Nr else None
+            self.dw3_r = torch.empty((Nr, w, d), dtype=f32, device=dev) if Nr else None
+            self.dw2_r = torch.empty((Nr, d, w), dtype=f32, device=dev) if Nr else None
+            self.dw1_s = torch.empty((Ks, w, d), dtype=f32, device=dev) if Ks else None
+            self.dw3_s = torch.empty((Ks, w, d), dtype=f32, device=dev) if Ks else None
+            self.dw2_s = torch.empty((Ks, d, w), dtype=f32, device=dev) if Ks else None
+            self.dcent = torch.empty((max(Nr, 1), d), dtype=f32, device=dev)
+            self.dbias = torch.empty(max(Nr, 1), dtype=f32, device=dev)
+        if self.dtype == "bf16":
+            from .workloads import bf16_bits_from_f32
+            self.dh = to_device(bf16_bits_from_f32(np.ascontiguousarray(dh, np.float32)), "bf16", dev)
+        else:
+            self.dh = to_device(np.ascontiguousarray(dh, np.float32), "f32", dev)
+        if Nr:
+            M.moe_combine_backward(p, self.dh, self.y_routed, self.gate, self.slot_of, self.dy_routed, self.dgate,
+                                   stream)
+        M.moe_expert_ffn_backward(p, self.x, self.offsets, self.sorted_token, self.slot_of, self.w1_r, self.w3_r,
+                                  self.w2_r, self.w1_s, self.w3_s, self.w2_s, self.dh, self.dy_routed, self.dx_ffn,
+                                  self.dw1_r, self.dw3_r, self.dw2_r, self.dw1_s, self.dw3_s, self.dw2_s,
+                                  self.bws, self.bws_bytes, stream)
+        if Nr:
+            M.moe_route_backward(p, max(self.groups, 1), alpha1, alpha2, self.x, self.centroids, self.probs,
+                                 self.idx, self.dgate, self.f, self.f_dev, self.dh, self.dx_ffn, self.dx,
+                                 self.dcent, self.dbias, self.bws, self.bws_bytes, stream)
+
+    def backward_results(self) -> dict:
+        torch = _torch()
+        torch.cuda.synchronize(self.device)
+        g = lambda t: None if t is None else t.cpu().numpy()
+        Nr = self.prob.n_routed
+        return dict(dgate=g(self.dgate), dx=g(self.dx), dx_ffn=g(self.dx_ffn), dw1_r=g(self.dw1_r),
+                    dw3_r=g(self.dw3_r), dw2_r=g(self.dw2_r), dw1_s=g(self.dw1_s), dw3_s=g(self.dw3_s),
+                    dw2_s=g(self.dw2_s), dcent=g(self.dcent)[:Nr], dbias=g(self.dbias)[:Nr])
+
     # -- readback ----------------------------------------------------------
     def results(self) -> dict:
         torch = _torch()

@@ -64,8 +64,13 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_down.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_combine.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_balance_stats.argtypes = [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_backward_workspace_size.argtypes = [_pp, ctypes.POINTER(_sz)]
+        L.moe_combine_backward.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_expert_ffn_backward.argtypes = [_pp] + [_vp] * 20 + [_sz, _vp]
+        L.moe_route_backward.argtypes = [_pp, ctypes.c_int32, ctypes.c_float, ctypes.c_float] + [_vp] * 13 + [_sz, _vp]
         for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up",
-                   "moe_expert_down", "moe_combine", "moe_balance_stats"):
+                   "moe_expert_down", "moe_combine", "moe_balance_stats", "moe_backward_workspace_size",
+                   "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -146,3 +151,35 @@ def moe_balance_stats(p, groups, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, 
     _check("moe_balance_stats", lib().moe_balance_stats(
         ctypes.byref(p), int(groups), _ptr(counts), _ptr(prob_sum), _ptr(f), _ptr(P), _ptr(f_dev),
         _ptr(P_dev), _ptr(exp_bal), _ptr(dev_bal), _stream(stream)))
+
+
+# -- backward pass ------------------------------------------------------------
+
+def moe_backward_workspace_size(p: moe_problem) -> int:
+    n = _sz(0)
+    _check("moe_backward_workspace_size", lib().moe_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def moe_combine_backward(p, dh, y_routed, gate, slot_of, dy_routed, dgate, stream=None):
+    _check("moe_combine_backward", lib().moe_combine_backward(ctypes.byref(p), _ptr(dh), _ptr(y_routed),
+                                                              _ptr(gate), _ptr(slot_of), _ptr(dy_routed),
+                                                              _ptr(dgate), _stream(stream)))
+
+
+def moe_expert_ffn_backward(p, x, offsets, sorted_token, slot_of, w1_routed, w3_routed, w2_routed, w1_shared,
+                            w3_shared, w2_shared, dh, dy_routed, dx_ffn, dw1_routed, dw3_routed, dw2_routed,
+                            dw1_shared, dw3_shared, dw2_shared, ws, ws_bytes, stream=None):
+    _check("moe_expert_ffn_backward", lib().moe_expert_ffn_backward(
+        ctypes.byref(p), _ptr(x), _ptr(offsets), _ptr(sorted_token), _ptr(slot_of), _ptr(w1_routed),
+        _ptr(w3_routed), _ptr(w2_routed), _ptr(w1_shared), _ptr(w3_shared), _ptr(w2_shared), _ptr(dh),
+        _ptr(dy_routed), _ptr(dx_ffn), _ptr(dw1_routed), _ptr(dw3_routed), _ptr(dw2_routed), _ptr(dw1_shared),
+        _ptr(dw3_shared), _ptr(dw2_shared), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_route_backward(p, groups, alpha1, alpha2, x, centroids, probs, idx, dgate, f, f_dev, dh, dx_ffn, dx,
+                       dcentroids, dbias, ws, ws_bytes, stream=None):
+    _check("moe_route_backward", lib().moe_route_backward(
+        ctypes.byref(p), int(groups), float(alpha1), float(alpha2), _ptr(x), _ptr(centroids), _ptr(probs),
+        _ptr(idx), _ptr(dgate), _ptr(f), _ptr(f_dev), _ptr(dh), _ptr(dx_ffn), _ptr(dx), _ptr(dcentroids),
+        _ptr(dbias), _ptr(ws), ws_bytes, _stream(stream)))

@@ -212,6 +212,87 @@ int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *count
                       const float *prob_sum, float *f, float *P, float *f_dev,
                       float *P_dev, float *exp_bal, float *dev_bal, void *stream);
 
+
+/* ========================================================================
+ * Backward pass.  Training is the pages' setting ("[ACL 2024] DeepSeekMoE
+ * ..." section "Method details": the loss adds alpha_1 * ExpBal +
+ * alpha_2 * DevBal to the task loss).  Given dh = dL_task/dh of the layer
+ * output, three calls mirror the forward ones (same problem, same stream):
+ *
+ *   moe_combine_backward     dh -> dy_routed (= gate * dh per grouped row), dgate
+ *   moe_expert_ffn_backward  -> dx_ffn and the expert weight gradients
+ *   moe_route_backward       -> dx (= dh + dx_ffn + router part), dcentroids, dbias
+ *
+ * Chain rule on the forward definitions, with the Top-K selection held fixed
+ * (it is piecewise constant) and f, f' (counts of that selection) constant;
+ * P and P' are differentiable through the softmax:
+ *   per used (t, e), dy = gate * dh_t (routed) or dh_t (shared):
+ *     da = W2^T dy, dq = da SiLU(p), dp = da q s (1 + p (1 - s)), s = sigmoid(p)
+ *     dx_t += W1^T dp + W3^T dq; dW2 += dy a^T; dW1 += dp u_t^T; dW3 += dq u_t^T
+ *   dgate[t,k] = dh_t . y_routed[slot_of[t,k]]
+ *   ds[t,r] = dgate[t,k] (r = idx[t,k]) + (alpha1 f_r + alpha2 f'_{g(r)}) / T
+ *   dz[t,r] = s[t,r] (ds[t,r] - sum_r' s[t,r'] ds[t,r'])
+ *   dx_t += sum_r dz[t,r] e_r;  dcentroids = dz^T x;  dbias = column sums of dz
+ * The backward workspace (moe_backward_workspace_size, 256-byte aligned) is
+ * separate from the forward one; it holds the per-row intermediates (da,
+ * dp, dq, a in dtype, the grouped rows' dx in fp32) and the router's dz.
+ * Gradients are fp32; accumulation is fp32; the intermediates are rounded
+ * to dtype as the forward rounds its activations.  Every output is
+ * overwritten.  Deterministic: no atomics, fixed summation orders.
+ * ====================================================================== */
+
+int moe_backward_workspace_size(const moe_problem *p, size_t *bytes);
+
+/*
+ * moe_combine_backward -- gradient through h = u + y_shared + sum_k g y_routed.
+ *   dh         [T, d]      dtype in   upstream gradient
+ *   y_routed   [T*K', d]   dtype in   from moe_expert_ffn
+ *   gate, slot_of [T, K']             from moe_route / moe_permute
+ *   dy_routed  [T*K', d]   dtype out  dy_routed[slot_of[t,k]] = gate[t,k] dh_t
+ *   dgate      [T, K']     fp32  out  dh_t . y_routed[slot_of[t,k]] (fp32 sum)
+ */
+int moe_combine_backward(const moe_problem *p, const void *dh, const void *y_routed, const float *gate,
+                         const int32_t *slot_of, void *dy_routed, float *dgate, void *stream);
+
+/*
+ * moe_expert_ffn_backward -- expert FFN gradients ("[ACL 2024] DeepSeekMoE
+ * ..." sections "Two core strategies" and "Method details").
+ *   x, offsets, sorted_token, weights     as in moe_expert_ffn
+ *   slot_of   [T, K']        from moe_permute
+ *   dh        [T, d]   dtype upstream gradient (the shared experts' dy)
+ *   dy_routed [T*K', d] dtype from moe_combine_backward
+ *   dx_ffn    [T, d]   fp32 out  sum over the token's experts of W1^T dp + W3^T dq
+ *   dw1_*, dw3_* [E, w, d], dw2_* [E, d, w]  fp32 out (routed E = N', shared
+ *             E = K_s; every expert written, unused ones with zeros)
+ * The SwiGLU pre-activations are recomputed (one more up-projection).
+ */
+int moe_expert_ffn_backward(const moe_problem *p, const void *x, const int32_t *offsets,
+                            const int32_t *sorted_token, const int32_t *slot_of, const void *w1_routed,
+                            const void *w3_routed, const void *w2_routed, const void *w1_shared,
+                            const void *w3_shared, const void *w2_shared, const void *dh, const void *dy_routed,
+                            float *dx_ffn, float *dw1_routed, float *dw3_routed, float *dw2_routed,
+                            float *dw1_shared, float *dw3_shared, float *dw2_shared, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * moe_route_backward -- router gradient and the layer's input gradient.
+ * Source: "[ACL 2024] DeepSeekMoE ..." section "Method details" (gates,
+ * balance losses), "【论文总结】MoE" sections 2.2-2.4.
+ *   groups D, alpha1, alpha2    weights of ExpBal and DevBal in the loss
+ *   x [T, d] dtype, centroids [N', d] fp32
+ *   probs [T, N'] fp32          the forward's affinities (required)
+ *   idx [T, K'], dgate [T, K']  from moe_route / moe_combine_backward
+ *   f [N'], f_dev [D]           from moe_balance_stats
+ *   dh [T, d] dtype, dx_ffn [T, d] fp32 (NULL = 0)
+ *   dx [T, d] fp32 out          dh + dx_ffn + sum_r dz[t,r] e_r
+ *   dcentroids [N', d] fp32 out, dbias [N'] fp32 out (NULL = not written)
+ * Envelope: N' <= 256, D | N'.
+ */
+int moe_route_backward(const moe_problem *p, int32_t groups, float alpha1, float alpha2, const void *x,
+                       const float *centroids, const float *probs, const int32_t *idx, const float *dgate,
+                       const float *f, const float *f_dev, const void *dh, const float *dx_ffn, float *dx,
+                       float *dcentroids, float *dbias, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -102,3 +102,28 @@ def test_other_calls_reject_bad_arguments_before_launch():
     with pytest.raises(M.MoEError) as e:   # D does not divide N'
         M.moe_balance_stats(p, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
     assert e.value.status == M.MOE_ERR_INVALID_ARG
+
+
+def test_backward_calls_reject_bad_arguments_before_launch():
+    p = M.moe_problem.make(64, 128, 1, 8, 2, 64, "bf16")
+    wsb = M.moe_backward_workspace_size(p)
+    assert wsb > 0
+    with pytest.raises(M.MoEError) as e:   # dgate missing
+        M.moe_combine_backward(p, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    args = [FAKE] * 19
+    with pytest.raises(M.MoEError) as e:   # backward workspace missing
+        M.moe_expert_ffn_backward(p, *args, None, 0, 0)
+    assert e.value.status == M.MOE_ERR_WORKSPACE
+    args[12] = None                        # dx_ffn missing
+    with pytest.raises(M.MoEError) as e:
+        M.moe_expert_ffn_backward(p, *args, FAKE, wsb, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:   # D does not divide N'
+        M.moe_route_backward(p, 3, 0.1, 0.1, *([FAKE] * 12), FAKE, wsb, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:   # probs missing
+        a = [FAKE] * 12
+        a[2] = None
+        M.moe_route_backward(p, 2, 0.1, 0.1, *a, FAKE, wsb, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
