@@ -13,6 +13,9 @@ Extra modes (used to produce the committed profile summaries):
   --copy-probe       also run a plain device copy of known size (counter calibration)
   --zero-weights     zero every expert weight after upload (power probe: the same launches
                      on operands that do not toggle; never a bench line of the workload)
+  --backward         time the backward pass instead (moe_combine_backward ->
+                     moe_expert_ffn_backward -> moe_route_backward after one forward);
+                     prints its own JSON line
   --ingest-pmc DIR   read rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs under DIR
                      and write profiles/traffic_<kernel>_<workload>.json
 """
@@ -243,6 +246,80 @@ def run(args) -> dict:
     return out
 
 
+def run_backward(args) -> dict:
+    """Backward pass of the layer: upstream gradient dh (seeded), alpha1 = alpha2 = 0.01."""
+    import numpy as np
+    import torch
+    from fine_grained_mixture_moe_amd import workloads as W
+    from fine_grained_mixture_moe_amd.layer import DeviceLayer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    name = args.config
+    inp = W.make_c2_fine(independent_centroids=True) if name == "c2b" else (
+        W.make_c2_coarse() if name == "c2a" else W.make_inputs(W.WORKLOADS[name]))
+    wl = inp.wl
+    dl = DeviceLayer(inp, device="cuda:0", want_probs=True)
+    dl.forward()
+    rng = np.random.default_rng(1234)
+    dh = rng.standard_normal((wl.T, wl.d)).astype(np.float32)
+    stream = torch.cuda.current_stream()
+    dl.backward(dh, 0.01, 0.01)      # allocates the gradient buffers
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        dl.backward(dh, 0.01, 0.01)
+    torch.cuda.synchronize()
+    # time the three calls without the host-side dh upload: reuse the uploaded dh
+    import fine_grained_mixture_moe_amd.moe as M
+    p = dl.prob
+
+    def calls(marks=None):
+        if marks:
+            marks[0].record(stream)
+        if p.n_routed:
+            M.moe_combine_backward(p, dl.dh, dl.y_routed, dl.gate, dl.slot_of, dl.dy_routed, dl.dgate)
+        if marks:
+            marks[1].record(stream)
+        M.moe_expert_ffn_backward(p, dl.x, dl.offsets, dl.sorted_token, dl.slot_of, dl.w1_r, dl.w3_r, dl.w2_r,
+                                  dl.w1_s, dl.w3_s, dl.w2_s, dl.dh, dl.dy_routed, dl.dx_ffn, dl.dw1_r, dl.dw3_r,
+                                  dl.dw2_r, dl.dw1_s, dl.dw3_s, dl.dw2_s, dl.bws, dl.bws_bytes)
+        if marks:
+            marks[2].record(stream)
+        if p.n_routed:
+            M.moe_route_backward(p, max(dl.groups, 1), 0.01, 0.01, dl.x, dl.centroids, dl.probs, dl.idx, dl.dgate,
+                                 dl.f, dl.f_dev, dl.dh, dl.dx_ffn, dl.dx, dl.dcent, dl.dbias, dl.bws, dl.bws_bytes)
+        if marks:
+            marks[3].record(stream)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        calls()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(min(args.steps, 10))]
+    for m in marks:
+        calls(m)
+    torch.cuda.synchronize()
+    stages = {k: round(sum(m[j].elapsed_time(m[j + 1]) for m in marks) / len(marks), 4)
+              for j, k in enumerate(["combine_backward", "expert_ffn_backward", "route_backward"])}
+    pairs = wl.T * (wl.top_k + wl.n_shared)
+    ffn_flops = 16.0 * wl.d * wl.inter * pairs
+    router_flops = 4.0 * wl.T * wl.d * wl.n_routed
+    mfma_peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    ffn_ms = stages["expert_ffn_backward"]
+    return {
+        "metric": "MoE-layer backward tokens/s (dh -> dx, dW, dcentroids) on 1 MI355X",
+        "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": wl.dtype,
+        "data": "synthetic", "config": {"workload": f"{name}: {wl.description}", "alpha1": 0.01, "alpha2": 0.01},
+        "stage_ms": stages,
+        "expert_ffn_backward": {"flops": ffn_flops, "tflops": round(ffn_flops / (ffn_ms * 1e-3) / 1e12, 2),
+                                "frac_of_mfma_peak": round(ffn_flops / (ffn_ms * 1e-3) / 1e12 / mfma_peak, 4)},
+        "active_tflops": round((ffn_flops + router_flops) / (ms * 1e-3) / 1e12, 2),
+    }
+
+
 def ingest_pmc(pmc_dir: str, workload: str) -> None:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the up kernel, scaled by the copy probe's readings."""
     rows = []
@@ -310,6 +387,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--zero-weights", action="store_true", help="power probe: zero the expert weights")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass (own JSON line)")
     ap.add_argument("--ingest-pmc", default=None)
     ap.add_argument("--summarize-trace", default=None, help="rocprofv3 output dir to summarize")
     ap.add_argument("--trace-command", default="", help="command that produced --summarize-trace")
@@ -324,7 +402,7 @@ def main():
         print(f"bench.py runs on one GPU only: this layer pass has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
-    out = run(args)
+    out = run_backward(args) if args.backward else run(args)
     print(json.dumps(out), flush=True)
 
 

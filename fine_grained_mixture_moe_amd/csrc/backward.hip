@@ -622,9 +622,20 @@ hipError_t launch_expert_backward(const moe_problem &p, const BwdFfnArgs &b, hip
     const int t3 = G * cdiv(2 * wmax, 128) * cdiv(p.d, 128);   // dW1, dW3
     const int t4 = rt * cdiv(2 * wmax, 128);                   // p, q -> dp, dq, a
     hipError_t e;
+    (void)t4;
     if (p.dtype == MOE_BF16) {
         if ((e = launch_bg<0, uint16_t>(a, t0, s)) != hipSuccess) return e;
-        if ((e = launch_bg<4, uint16_t>(a, t4, s)) != hipSuccess) return e;
+        // p, q recomputed by the forward up kernel, with the backward epilogue
+        FfnArgs f{};
+        f.x = b.x; f.offsets = b.offsets; f.sorted_token = b.sorted_token;
+        f.w1_r = b.w1_r; f.w3_r = b.w3_r; f.w1_s = b.w1_s; f.w3_s = b.w3_s;
+        f.act_shared = b.a_s; f.act_routed = b.a_r;
+        moe_problem q = p;
+        if (p.T == 0 || p.top_k == 0) q.n_routed = 0, q.top_k = 0;
+        if (p.T == 0) q.n_shared = 0;
+        if ((q.n_routed > 0 || q.n_shared > 0) &&
+            (e = launch_expert_up_backward(q, f, b.da_s, b.da_r, b.dp_s, b.dp_r, b.dq_s, b.dq_r, s)) != hipSuccess)
+            return e;
         if ((e = launch_bg<1, uint16_t>(a, t1, s)) != hipSuccess) return e;
         if ((e = launch_bg<2, uint16_t>(a, t2, s)) != hipSuccess) return e;
         if ((e = launch_bg<3, uint16_t>(a, t3, s)) != hipSuccess) return e;

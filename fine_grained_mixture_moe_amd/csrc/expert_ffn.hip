@@ -82,6 +82,10 @@ struct GemmParams {
     const uint8_t *wa_s, *wb_s;  // up: W1_s, W3_s  | down: W2_s
     uint8_t *out_shared;         // up: act_shared  | down: y_shared (fp32)
     uint8_t *out_routed;         // up: act_routed  | down: y_routed
+    // backward recompute of the up projection (BWD): da in, dp and dq out
+    // (act_* above take the recomputed activations a)
+    const uint8_t *da_shared, *da_routed;
+    uint8_t *dp_shared, *dp_routed, *dq_shared, *dq_routed;
 };
 
 // UP: true for the gate/up projection with SwiGLU epilogue, false for the down projection.
@@ -309,8 +313,9 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int BM, bool UP>
+template <int BM, bool UP, bool BWD = false>
 __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
+    static_assert(!BWD || UP, "the backward epilogue belongs to the up projection");
     constexpr int NT = 512;          // threads: 8 waves, 2 per SIMD
     constexpr int BN = 256;          // weight rows per tile
     constexpr int RB = 128;          // LDS row bytes
@@ -596,6 +601,83 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
         }
         return;
     }
+    if constexpr (BWD) {
+        // Backward recompute: p, q are in registers (acc[0], acc[1]); da of the
+        // same rows and units comes in through LDS (coalesced row loads into
+        // the weight stages), and a = SiLU(p) q, dq = da SiLU(p),
+        // dp = da q s (1 + p (1 - s)), s = sigmoid(p), go out through the
+        // token stages, one output at a time, as row-wise 16-byte stores.
+        constexpr int C16B = 16;                       // 128 units = 16 chunks of 16 B per row
+        constexpr int ITB = BM * C16B / NT;
+        const int ldb = shared ? P.Ks * P.w : P.w;
+        const int colb = n_tile * 128;
+        auto slot_in = [&](int r, int c) -> uint8_t * { return &s_w[0][0] + r * 256 + (c ^ (r & 15)) * 16; };
+        auto slot_out = [&](int r, int c) -> uint8_t * { return &s_x[0][0] + r * 256 + (c ^ (r & 15)) * 16; };
+        const uint16_t *dain = (const uint16_t *)(shared ? P.da_shared : P.da_routed);
+#pragma unroll
+        for (int it = 0; it < ITB; ++it) {
+            const int i = tid + it * NT;
+            const int r = i / C16B, c = i % C16B;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (r < nr && colb + c * 8 < ldb) v = *(const uint4 *)(dain + (size_t)(row_off + m0 + r) * ldb + colb + c * 8);
+            *(uint4 *)slot_in(r, c) = v;
+        }
+        __syncthreads();
+        // one output at a time (which = 0: a, 1: dp, 2: dq), recomputed from the
+        // accumulators, to keep the registers of a single packed tile live
+        auto pack = [&](int which, uint2 (&v)[MB][4]) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint2 dav = *(const uint2 *)(slot_in(xrow[mb], wn * 4 + q) + lhi * 8);
+                    const uint32_t dw[2] = {dav.x, dav.y};
+                    uint16_t h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float da = __uint_as_float((e & 1) ? (dw[e >> 1] & 0xffff0000u) : (dw[e >> 1] << 16));
+                        const float pg = acc[0][mb][4 * q + e];
+                        const float pu = acc[1][mb][4 * q + e];
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-pg));
+                        const float o = which == 0 ? pg * sg * pu
+                                      : which == 1 ? da * pu * sg * (1.0f + pg * (1.0f - sg))
+                                                   : da * pg * sg;
+                        h[e] = f2bf(o);
+                    }
+                    v[mb][q] = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                }
+        };
+        auto emit = [&](const uint2 (&v)[MB][4], uint8_t *outp) {
+            __syncthreads();   // the previous output's reads of the token stages are done
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) *(uint2 *)(slot_out(xrow[mb], wn * 4 + q) + lhi * 8) = v[mb][q];
+            __syncthreads();
+            uint16_t *out = (uint16_t *)outp;
+            uint4 piece[ITB];
+#pragma unroll
+            for (int it = 0; it < ITB; ++it) {
+                const int i = tid + it * NT;
+                piece[it] = *(const uint4 *)slot_out(i / C16B, i % C16B);
+            }
+#pragma unroll
+            for (int it = 0; it < ITB; ++it) {
+                const int i = tid + it * NT;
+                const int r = i / C16B, c = i % C16B;
+                if (r < nr && colb + c * 8 < ldb)
+                    *(uint4 *)(out + (size_t)(row_off + m0 + r) * ldb + colb + c * 8) = piece[it];
+            }
+        };
+        uint2 pv[MB][4];
+        pack(0, pv);
+        emit(pv, shared ? P.out_shared : P.out_routed);
+        pack(1, pv);
+        emit(pv, shared ? P.dp_shared : P.dp_routed);
+        pack(2, pv);
+        emit(pv, shared ? P.dq_shared : P.dq_routed);
+        return;
+    } else {
     // bf16 output tile (BM tokens x NC features) staged in the now idle LDS
     // stages, then written row by row with 16-byte stores: a wave covers whole
     // rows, where direct stores from the MFMA layout would touch 32 rows with
@@ -657,6 +739,7 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
         if (r < nr && col0 + c * 8 < ld)
             *(uint4 *)(out + (size_t)(row_off + m0 + r) * ld + col0 + c * 8) = piece[it];
     }
+    }
 }
 
 GemmParams make_params(const moe_problem &p, const FfnArgs &a, bool up) {
@@ -716,6 +799,30 @@ hipError_t launch_bf16(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Backward recompute of the up projection (bf16): act_* <- a, dp_*, dq_* from da_*.
+hipError_t launch_expert_up_backward(const moe_problem &p, const FfnArgs &a, const void *da_shared,
+                                     const void *da_routed, void *dp_shared, void *dp_routed, void *dq_shared,
+                                     void *dq_routed, hipStream_t s) {
+    GemmParams P = make_params(p, a, true);
+    P.da_shared = (const uint8_t *)da_shared;
+    P.da_routed = (const uint8_t *)da_routed;
+    P.dp_shared = (uint8_t *)dp_shared;
+    P.dp_routed = (uint8_t *)dp_routed;
+    P.dq_shared = (uint8_t *)dq_shared;
+    P.dq_routed = (uint8_t *)dq_routed;
+    const int64_t avg = p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / p.n_routed : (int64_t)p.T;
+    if (avg >= 256) {
+        const int tiles = tile_bound(p, true, 256, 128, 256);
+        if (tiles == 0) return hipSuccess;
+        grouped_ffn_bf16_kernel<256, true, true><<<tiles, 512, 0, s>>>(P);
+    } else {
+        const int tiles = tile_bound(p, true, 128, 128, 256);
+        if (tiles == 0) return hipSuccess;
+        grouped_ffn_bf16_kernel<128, true, true><<<tiles, 512, 0, s>>>(P);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_expert_up(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
     if (p.dtype == MOE_BF16) return launch_bf16<true>(p, a, s);

@@ -84,6 +84,11 @@ struct FfnArgs {
 // up: act = SiLU(X W1^T) * (X W3^T) into the workspace; down: y = act W2^T.
 hipError_t launch_expert_up(const moe_problem &p, const FfnArgs &a, hipStream_t s);
 hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_t s);
+// backward: the up projection recomputed, with a = SiLU(p) q written to act_*
+// and dp, dq formed from da in the epilogue (bf16 only)
+hipError_t launch_expert_up_backward(const moe_problem &p, const FfnArgs &a, const void *da_shared,
+                                     const void *da_routed, void *dp_shared, void *dp_routed, void *dq_shared,
+                                     void *dq_routed, hipStream_t s);
 
 hipError_t launch_combine(const moe_problem &p, const void *x, const void *y_routed,
                           const float *y_shared, const float *gate, const int32_t *slot_of,
