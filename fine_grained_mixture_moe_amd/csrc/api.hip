@@ -241,6 +241,7 @@ int moe_combine_backward(const moe_problem *p, const void *dh, const void *y_rou
     int rc = check_problem(p);
     if (rc != MOE_OK) return rc;
     if ((int64_t)p->T * p->top_k == 0) return MOE_OK;
+    if (p->top_k > kRouteMaxTopK) return MOE_ERR_UNSUPPORTED;
     if (!dh || !y_routed || !gate || !slot_of || !dy_routed || !dgate) return MOE_ERR_INVALID_ARG;
     if (!aligned16(dh) || !aligned16(y_routed) || !aligned16(dy_routed)) return MOE_ERR_INVALID_ARG;
     return hip_status(launch_combine_backward(*p, dh, y_routed, gate, slot_of, dy_routed, dgate,

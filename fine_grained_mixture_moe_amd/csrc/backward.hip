@@ -24,8 +24,8 @@
 //         reads da, writes dp, dq and a (A and B k-contiguous)
 //   gather_dx_kernel     dx_ffn[t] = dxs[t] + sum_k dxr[slot_of[t,k]] (k order)
 //   router_dz_kernel     ds, dz per token (wave per token, lane = expert)
-//   router_dx_kernel     dx = dh + dx_ffn + dz E
-//   router_dE_kernel     dE, dbias partials over token chunks, then a fixed-order sum
+//   router_dx_kernel     dx = dh + dx_ffn + dz E (LDS-tiled, 64 tokens x 64 columns)
+//   router_de_part/sum   dE, dbias partials over token chunks (x read once), then a fixed-order sum
 //
 // Operands are staged through LDS; a "transposed" operand (stored with its
 // m index contiguous) is read into MFMA fragments with ds_read_b64_tr_b16:
@@ -58,11 +58,38 @@ template <> __device__ __forceinline__ uint16_t from_f<uint16_t>(float v) { retu
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 
 // ---------------------------------------------------------------------------
-// combine backward: one wave per token.  Lane l covers columns 8l + 512 i.
+// combine backward: one wave per token.  Lane l covers columns 8l + 512 i
+// with 16-byte accesses; dh_t is read once for all K' slots.
 // dy_routed[slot_of[t,k]] = gate[t,k] * dh_t (rounded to dtype);
 // dgate[t,k] = sum_i dh_t[i] * y_routed[slot][i] in fp32, lane partials summed
 // by a fixed butterfly.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
+    const uint4 q = *(const uint4 *)p;
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float *p, float v[8]) {
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(uint16_t *p, const float v[8]) {
+    uint4 q;
+    q.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    q.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    q.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+    q.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    *(uint4 *)p = q;
+}
+__device__ __forceinline__ void store8(float *p, const float v[8]) {
+    *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4 *)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 template <typename DT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(int T, int d, int K, const DT *__restrict__ dh,
                                                           const DT *__restrict__ y, const float *__restrict__ gate,
@@ -71,28 +98,47 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(int T, int d, int K, c
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= T) return;
-    for (int k = 0; k < K; ++k) {
-        const int slot = slot_of[(size_t)t * K + k];
-        const float g = gate[(size_t)t * K + k];
-        float part = 0.0f;
-        if (slot >= 0) {
-            for (int c = lane * 8; c < d; c += 512) {
-                float hv[8], yv[8];
+    float part[kRouteMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kRouteMaxTopK; ++k) part[k] = 0.0f;
+    for (int c = lane * 8; c < d; c += 512) {
+        float hv[8];
+        load8(dh + (size_t)t * d + c, hv);
+        // K' in batches of 4: the batch's slots, then its 4 independent row loads
+#pragma unroll
+        for (int k0 = 0; k0 < kRouteMaxTopK; k0 += 4) {
+            if (k0 >= K) break;
+            int slot[4];
+            float g[4], yv[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool in = k0 + u < K;
+                slot[u] = in ? slot_of[(size_t)t * K + k0 + u] : -1;
+                g[u] = in ? gate[(size_t)t * K + k0 + u] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (slot[u] >= 0) load8(y + (size_t)slot[u] * d + c, yv[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (slot[u] < 0) continue;
+                float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    hv[e] = to_f(dh[(size_t)t * d + c + e]);
-                    yv[e] = to_f(y[(size_t)slot * d + c + e]);
+                    part[k0 + u] = __builtin_fmaf(hv[e], yv[u][e], part[k0 + u]);
+                    o[e] = g[u] * hv[e];
                 }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    part = __builtin_fmaf(hv[e], yv[e], part);
-                    dy[(size_t)slot * d + c + e] = from_f<DT>(g * hv[e]);
-                }
+                store8(dy + (size_t)slot[u] * d + c, o);
             }
         }
+    }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-        if (lane == 0) dgate[(size_t)t * K + k] = slot >= 0 ? part : 0.0f;
+    for (int k = 0; k < kRouteMaxTopK; ++k) {
+        if (k >= K) break;
+        float v = part[k];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) dgate[(size_t)t * K + k] = v;
     }
 }
 
@@ -216,7 +262,7 @@ __device__ __forceinline__ uint4 ld16(const void *p) {
 // 128 x 128 tile (mode 4: 128 rows x 64 units, both halves of B), 32 k per
 // step, 4 waves in 2 x 2, each 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.
 template <int MODE, typename DT>
-__global__ __launch_bounds__(256) void bgemm_kernel(BgArgs A) {
+__global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
     constexpr bool BF = std::is_same<DT, uint16_t>::value;
     constexpr int ES = sizeof(DT);
     constexpr int EC = 16 / ES;                       // elements per 16-byte chunk
@@ -229,8 +275,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgArgs A) {
     constexpr int CA = AT ? 32 * (128 / EC) : 128 * (32 / EC);   // chunks per A tile
     constexpr int CB = BT ? 32 * (128 / EC) : 128 * (32 / EC);
     constexpr int RA = CA / 256, RB = CB / 256;                   // chunks per thread
-    __shared__ __attribute__((aligned(16))) uint8_t s_a[SA];
-    __shared__ __attribute__((aligned(16))) uint8_t s_b[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_a2[1][SA];
+    __shared__ __attribute__((aligned(16))) uint8_t s_b2[1][SB];
     __shared__ int s_pref[BG_MAXG + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -293,7 +339,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgArgs A) {
             rb[i] = ld16(p);
         }
     };
-    auto store_tiles = [&]() {
+    auto store_tiles = [&](int stg) {
+        uint8_t *s_a = s_a2[stg], *s_b = s_b2[stg];
 #pragma unroll
         for (int i = 0; i < RA; ++i) {
             const int c = tid + 256 * i;
@@ -336,7 +383,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgArgs A) {
         const int k = 2 * ks + lhi;
         return tr ? *(const float *)(s + k * PT + (r0 + l32) * 4) : *(const float *)(s + (r0 + l32) * PK + k * 4);
     };
-    auto compute = [&]() {
+    auto compute = [&](int stg) {
+        const uint8_t *s_a = s_a2[stg], *s_b = s_b2[stg];
         if constexpr (BF) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -370,17 +418,20 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgArgs A) {
         }
     };
 
+    // One LDS stage; the registers prefetch the next step during the
+    // compute of the current one.  (Two stages with one barrier per step
+    // measured slower: the extra registers cost a wave per SIMD.)
     const int nk = cdiv(K, 32);
     if (nk > 0) {
         load_tiles(0);
-        store_tiles();
+        store_tiles(0);
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
             if (kt + 1 < nk) load_tiles((kt + 1) * 32);
-            compute();
+            compute(0);
             __syncthreads();
             if (kt + 1 < nk) {
-                store_tiles();
+                store_tiles(0);
                 __syncthreads();
             }
         }
@@ -510,54 +561,107 @@ __global__ __launch_bounds__(256) void router_dz_kernel(int T, int Nr, int K, in
     }
 }
 
-// dx[t, c..c+3] = dh + dx_ffn + sum_r dz[t, r] E[r, c..c+3] (r ascending).
-template <typename DT>
+// dx = dh + dx_ffn + dz E.  Workgroup tile: 64 tokens x 64 columns, thread
+// (token group tg, column group cg) owns 4 tokens x 4 columns; dz rows of the
+// tile and E columns of the tile are staged in LDS; the sum over r runs in
+// ascending order.
+template <typename DT, int NJ>
 __global__ __launch_bounds__(256) void router_dx_kernel(int T, int d, int Nr, const DT *__restrict__ dh,
                                                         const float *__restrict__ dx_ffn,
                                                         const float *__restrict__ dz, const float *__restrict__ E,
                                                         float *__restrict__ dx) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int q = d / 4;
-    if (i >= (int64_t)T * q) return;
-    const int t = (int)(i / q), c = (int)(i % q) * 4;
-    float a[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = to_f(dh[(size_t)t * d + c + e]) + (dx_ffn ? dx_ffn[(size_t)t * d + c + e] : 0.0f);
-    for (int r = 0; r < Nr; ++r) {
-        const float z = dz[(size_t)t * Nr + r];
-        const float4 e4 = *(const float4 *)(E + (size_t)r * d + c);
-        a[0] = __builtin_fmaf(z, e4.x, a[0]);
-        a[1] = __builtin_fmaf(z, e4.y, a[1]);
-        a[2] = __builtin_fmaf(z, e4.z, a[2]);
-        a[3] = __builtin_fmaf(z, e4.w, a[3]);
+    constexpr int NE = 64 * NJ;
+    __shared__ float s_dz[64][NE + 1];
+    __shared__ __attribute__((aligned(16))) float s_e[NE][64];
+    const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 64 * NE; i += 256) {
+        const int tt = i / NE, r = i % NE;
+        s_dz[tt][r] = (t0 + tt < T && r < Nr) ? dz[(size_t)(t0 + tt) * Nr + r] : 0.0f;
     }
-    *(float4 *)(dx + (size_t)t * d + c) = make_float4(a[0], a[1], a[2], a[3]);
+    for (int i = tid; i < NE * 16; i += 256) {
+        const int r = i / 16, c4 = (i % 16) * 4;
+        *(float4 *)&s_e[r][c4] = (r < Nr && c0 + c4 < d) ? *(const float4 *)(E + (size_t)r * d + c0 + c4)
+                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    const int cg = tid & 15, tg = tid >> 4;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int r = 0; r < Nr; ++r) {
+        const float4 e4 = *(const float4 *)&s_e[r][cg * 4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float z = s_dz[tg * 4 + i][r];
+            acc[i][0] = __builtin_fmaf(z, e4.x, acc[i][0]);
+            acc[i][1] = __builtin_fmaf(z, e4.y, acc[i][1]);
+            acc[i][2] = __builtin_fmaf(z, e4.z, acc[i][2]);
+            acc[i][3] = __builtin_fmaf(z, e4.w, acc[i][3]);
+        }
+    }
+    const int c = c0 + cg * 4;
+    if (c >= d) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + tg * 4 + i;
+        if (t >= T) continue;
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = to_f(dh[(size_t)t * d + c + j]) + (dx_ffn ? dx_ffn[(size_t)t * d + c + j] : 0.0f) + acc[i][j];
+        *(float4 *)(dx + (size_t)t * d + c) = make_float4(o[0], o[1], o[2], o[3]);
+    }
 }
 
-// dE partials over token chunks: block (chunk j, expert r, 1024 columns):
-// part[j][r][c] = sum_{t in chunk j} dz[t, r] x[t, c] (t ascending); column
-// d also carries sum dz (the bias gradient).  Row pitch d + 4 floats.
-constexpr int kDeTokens = 256;
-template <typename DT>
+// dE partials over token chunks of kDeTokens: workgroup (chunk j, 64
+// columns); thread (column col, expert group eg) accumulates, t ascending,
+// dz[t, r] x[t, c] for its 16 NJ consecutive experts r = eg * 16 NJ + i,
+// reading each x value once; dz of the chunk is staged in LDS, read as
+// 16-byte broadcasts (a wave shares eg).  part[j][r][c], row pitch d + 4;
+// column d carries sum_t dz (the bias gradient).
+constexpr int kDeTokens = 128;
+template <typename DT, int NJ>
 __global__ __launch_bounds__(256) void router_de_part_kernel(int T, int d, int Nr, const DT *__restrict__ x,
                                                              const float *__restrict__ dz,
                                                              float *__restrict__ part) {
-    const int j = blockIdx.x, r = blockIdx.y;
-    const int c = blockIdx.z * 1024 + threadIdx.x * 4;
-    const int t0 = j * kDeTokens, t1 = min(T, t0 + kDeTokens);
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    float b = 0.0f;
-    for (int t = t0; t < t1; ++t) {
-        const float z = dz[(size_t)t * Nr + r];
-        b += z;
-        if (c < d) {
+    constexpr int NE = 64 * NJ, PER = 16 * NJ;
+    __shared__ __attribute__((aligned(16))) float s_dz[kDeTokens][NE];
+    const int j = blockIdx.x, c0 = blockIdx.y * 64;
+    const int tid = threadIdx.x, col = tid & 63, eg = tid >> 6;
+    const int c = c0 + col;
+    const int t0 = j * kDeTokens, n = min(kDeTokens, T - t0);
+    for (int i = tid; i < kDeTokens * NE; i += 256) {
+        const int tt = i / NE, r = i % NE;
+        s_dz[tt][r] = (tt < n && r < Nr) ? dz[(size_t)(t0 + tt) * Nr + r] : 0.0f;
+    }
+    __syncthreads();
+    float acc[PER];
+    float bsum[PER];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(z, to_f(x[(size_t)t * d + c + e]), a[e]);
+    for (int i = 0; i < PER; ++i) { acc[i] = 0.0f; bsum[i] = 0.0f; }
+    for (int tt = 0; tt < n; ++tt) {
+        const float xv = to_f(x[(size_t)(t0 + tt) * d + c]);
+#pragma unroll
+        for (int i = 0; i < PER; i += 4) {
+            const float4 z = *(const float4 *)&s_dz[tt][eg * PER + i];
+            acc[i] = __builtin_fmaf(z.x, xv, acc[i]);
+            acc[i + 1] = __builtin_fmaf(z.y, xv, acc[i + 1]);
+            acc[i + 2] = __builtin_fmaf(z.z, xv, acc[i + 2]);
+            acc[i + 3] = __builtin_fmaf(z.w, xv, acc[i + 3]);
+            bsum[i] += z.x; bsum[i + 1] += z.y; bsum[i + 2] += z.z; bsum[i + 3] += z.w;
         }
     }
-    float *o = part + ((size_t)j * Nr + r) * (d + 4);
-    if (c < d) *(float4 *)(o + c) = make_float4(a[0], a[1], a[2], a[3]);
-    if (blockIdx.z == 0 && threadIdx.x == 0) o[d] = b;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int r = eg * PER + i;
+        if (r >= Nr) continue;
+        float *o = part + ((size_t)j * Nr + r) * (d + 4);
+        o[c] = acc[i];
+        if (blockIdx.y == 0 && col == 0) o[d] = bsum[i];
+    }
 }
 
 // dE[r][c] = sum_j part[j][r][c] (j ascending); dbias[r] = sum_j part[j][r][d].
@@ -662,22 +766,28 @@ hipError_t launch_route_backward(const moe_problem &p, int groups, float alpha1,
     if (p.T > 0) {
         router_dz_kernel<<<cdiv(p.T, 4), 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, alpha1, alpha2, probs, idx,
                                                       dgate, f, f_dev, dz);
-        const int64_t n = (int64_t)p.T * (p.d / 4);
-        const int gx = (int)((n + 255) / 256);
-        if (p.dtype == MOE_BF16)
-            router_dx_kernel<uint16_t><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const uint16_t *)dh, dx_ffn, dz,
-                                                          centroids, dx);
-        else
-            router_dx_kernel<float><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const float *)dh, dx_ffn, dz,
-                                                       centroids, dx);
+        const dim3 gx(cdiv(p.T, 64), cdiv(p.d, 64));
+        const int nj = cdiv(p.n_routed, 64);
+#define MOE_DX(DT, NJ) router_dx_kernel<DT, NJ><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const DT *)dh, dx_ffn, \
+                                                                   dz, centroids, dx)
+        if (p.dtype == MOE_BF16) {
+            if (nj == 1) MOE_DX(uint16_t, 1); else if (nj == 2) MOE_DX(uint16_t, 2); else MOE_DX(uint16_t, 4);
+        } else {
+            if (nj == 1) MOE_DX(float, 1); else if (nj == 2) MOE_DX(float, 2); else MOE_DX(float, 4);
+        }
+#undef MOE_DX
     }
     const int nchunk = cdiv(p.T, kDeTokens);
     if (nchunk > 0) {
-        dim3 g(nchunk, p.n_routed, cdiv(p.d, 1024));
-        if (p.dtype == MOE_BF16)
-            router_de_part_kernel<uint16_t><<<g, 256, 0, s>>>(p.T, p.d, p.n_routed, (const uint16_t *)x, dz, part);
-        else
-            router_de_part_kernel<float><<<g, 256, 0, s>>>(p.T, p.d, p.n_routed, (const float *)x, dz, part);
+        const dim3 g(nchunk, cdiv(p.d, 64));
+        const int nj = cdiv(p.n_routed, 64);
+#define MOE_DE(DT, NJ) router_de_part_kernel<DT, NJ><<<g, 256, 0, s>>>(p.T, p.d, p.n_routed, (const DT *)x, dz, part)
+        if (p.dtype == MOE_BF16) {
+            if (nj == 1) MOE_DE(uint16_t, 1); else if (nj == 2) MOE_DE(uint16_t, 2); else MOE_DE(uint16_t, 4);
+        } else {
+            if (nj == 1) MOE_DE(float, 1); else if (nj == 2) MOE_DE(float, 2); else MOE_DE(float, 4);
+        }
+#undef MOE_DE
     }
     const int64_t m = (int64_t)p.n_routed * (p.d + 1);
     router_de_sum_kernel<<<(int)((m + 255) / 256), 256, 0, s>>>(nchunk, p.d, p.n_routed, part, dcentroids, dbias);

@@ -250,6 +250,7 @@ int moe_backward_workspace_size(const moe_problem *p, size_t *bytes);
  *   gate, slot_of [T, K']             from moe_route / moe_permute
  *   dy_routed  [T*K', d]   dtype out  dy_routed[slot_of[t,k]] = gate[t,k] dh_t
  *   dgate      [T, K']     fp32  out  dh_t . y_routed[slot_of[t,k]] (fp32 sum)
+ * Envelope: K' <= 16 (as moe_route), MOE_ERR_UNSUPPORTED otherwise.
  */
 int moe_combine_backward(const moe_problem *p, const void *dh, const void *y_routed, const float *gate,
                          const int32_t *slot_of, void *dy_routed, float *dgate, void *stream);
