@@ -332,8 +332,11 @@ def ingest_pmc(pmc_dir: str, workload: str) -> None:
     for r in rows:
         kname = r.get("Kernel_Name", "")
         cname = r.get("Counter_Name", "")
-        if "grouped_ffn" in kname and ("true>" in kname or "Lb1E" in kname):
+        # template arguments <BM, UP, BWD>: the forward up projection is <*, true, false>
+        if "grouped_ffn" in kname and (", true, false>" in kname or "Lb1ELb0E" in kname):
             key = "up"
+        elif "grouped_ffn" in kname and ", true, true>" in kname:
+            continue
         elif "grouped_ffn" in kname:
             key = "down"
         elif "elementwise" in kname.lower():
