@@ -148,6 +148,73 @@ void oracle_route(int T, int d, int Nr, int K, const float *x, const float *E,
 }
 
 /* ------------------------------------------------------------------------
+ * Routing variants of the ablations on [S] "Expert specialization analysis"
+ * (Fig. 4: disabling the top routed experts) and the baselines of [S]
+ * "Experiment design" (Hash Layer's fixed hash routing; Switch's top-1 and
+ * GShard's top-2 are oracle_route with K' = 1, 2).
+ *
+ * oracle_route_ablate: as oracle_route, but each token's `skip` highest
+ * ranked routed experts (order z desc, r asc) are disabled and the token
+ * takes the next K: idx[t, 0..K-1] = ranks skip .. skip+K-1.  Affinities,
+ * gates (no renormalisation) and prob_sum are those of oracle_route.
+ * ---------------------------------------------------------------------- */
+void oracle_route_ablate(int T, int d, int Nr, int K, int skip, const float *x, const float *E,
+                         const float *bias, int32_t *idx, float *gate, float *probs,
+                         int32_t *counts, double *prob_sum) {
+    float *z = (float *)malloc((size_t)(T > 0 ? T : 1) * (Nr > 0 ? Nr : 1) * sizeof(float));
+    double *s = (double *)malloc((size_t)(T > 0 ? T : 1) * (Nr > 0 ? Nr : 1) * sizeof(double));
+    oracle_logits(T, d, Nr, x, E, bias, z);
+    #pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const float *zt = z + (size_t)t * Nr;
+        double *st = s + (size_t)t * Nr;
+        double m = -INFINITY;
+        for (int r = 0; r < Nr; ++r) if ((double)zt[r] > m) m = (double)zt[r];
+        double sum = 0.0;
+        for (int r = 0; r < Nr; ++r) { st[r] = exp((double)zt[r] - m); sum += st[r]; }
+        for (int r = 0; r < Nr; ++r) st[r] = st[r] / sum;
+        if (probs) for (int r = 0; r < Nr; ++r) probs[(size_t)t * Nr + r] = (float)st[r];
+        unsigned char *taken = (unsigned char *)calloc((size_t)Nr, 1);
+        for (int k = 0; k < skip + K; ++k) {
+            int best = -1;
+            for (int r = 0; r < Nr; ++r) {
+                if (taken[r]) continue;
+                if (best < 0 || ranks_before(zt[r], r, zt[best], best)) best = r;
+            }
+            taken[best] = 1;
+            if (k < skip) continue;   /* disabled */
+            idx[(size_t)t * K + (k - skip)] = best;
+            gate[(size_t)t * K + (k - skip)] = (float)st[best];
+        }
+        free(taken);
+    }
+    for (int r = 0; r < Nr; ++r) { counts[r] = 0; prob_sum[r] = 0.0; }
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) counts[idx[(size_t)t * K + k]] += 1;
+        for (int r = 0; r < Nr; ++r) prob_sum[r] += s[(size_t)t * Nr + r];
+    }
+    free(z);
+    free(s);
+}
+
+/* oracle_route_hash: one expert per token from a fixed hash of its token id
+ * (the Hash Layer baseline), gate 1:
+ *   h = (uint32) id * 2654435761 (mod 2^32)   (Knuth's multiplicative hash)
+ *   idx[t] = floor(h * N' / 2^32)              (multiply-shift range reduction)
+ *   counts[r] = #{t : idx[t] = r}                                          */
+void oracle_route_hash(int T, int Nr, const int32_t *token_ids, int32_t *idx, float *gate,
+                       int32_t *counts) {
+    for (int r = 0; r < Nr; ++r) counts[r] = 0;
+    for (int t = 0; t < T; ++t) {
+        const uint32_t h = (uint32_t)token_ids[t] * 2654435761u;
+        const int r = (int)(((uint64_t)h * (uint64_t)Nr) >> 32);
+        idx[t] = r;
+        gate[t] = 1.0f;
+        counts[r] += 1;
+    }
+}
+
+/* ------------------------------------------------------------------------
  * Grouping of (token, expert) pairs by routed expert, the bookkeeping behind
  * "token t selects expert i" ([N] section 2.3).  A counting sort:
  *   offsets[r] = sum_{r' < r} counts[r'],  offsets[Nr] = T*K

@@ -46,6 +46,8 @@ def lib():
         L.oracle_forward.argtypes = [_i, _i, _i, _i, _i, _i, _i, _f32p, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _f64p, _f32p, _f32p]
         L.oracle_forward.restype = _i
+        L.oracle_route_ablate.argtypes = [_i, _i, _i, _i, _i, _f32p, _f32p, _vp, _i32p, _f32p, _vp, _i32p, _f64p]
+        L.oracle_route_hash.argtypes = [_i, _i, _i32p, _i32p, _f32p, _i32p]
         _d = ctypes.c_double
         L.oracle_backward_tokens.argtypes = [_i, _i32p, _i, _i, _i, _i, _i, _i, _i, _d, _d, _f32p, _vp,
                                              _i32p, _f32p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -97,6 +99,32 @@ def route(x, E, top_k: int, bias=None, want_probs: bool = False):
     psum = np.empty(Nr, np.float64)
     lib().oracle_route(T, d, Nr, top_k, x, E, _ptr(b), idx, gate, _ptr(probs), counts, psum)
     return dict(idx=idx, gate=gate, probs=probs, counts=counts, prob_sum=psum)
+
+
+def route_ablate(x, E, top_k: int, skip: int, bias=None, want_probs: bool = False):
+    """Routing with each token's `skip` top-ranked routed experts disabled (ranks skip..skip+K'-1 taken)."""
+    x, E = _c(x), _c(E)
+    T, d = x.shape
+    Nr = E.shape[0]
+    b = None if bias is None else _c(bias)
+    idx = np.empty((T, top_k), np.int32)
+    gate = np.empty((T, top_k), np.float32)
+    probs = np.empty((T, Nr), np.float32) if want_probs else None
+    counts = np.empty(Nr, np.int32)
+    psum = np.empty(Nr, np.float64)
+    lib().oracle_route_ablate(T, d, Nr, top_k, int(skip), x, E, _ptr(b), idx, gate, _ptr(probs), counts, psum)
+    return dict(idx=idx, gate=gate, probs=probs, counts=counts, prob_sum=psum)
+
+
+def route_hash(token_ids, n_routed: int):
+    """Hash routing: idx [T,1] from a fixed multiplicative hash of the token ids, gate 1."""
+    ids = _c(token_ids, np.int32)
+    T = ids.shape[0]
+    idx = np.empty((T, 1), np.int32)
+    gate = np.empty((T, 1), np.float32)
+    counts = np.empty(n_routed, np.int32)
+    lib().oracle_route_hash(T, n_routed, ids if T else np.zeros(1, np.int32), idx, gate, counts)
+    return dict(idx=idx, gate=gate, counts=counts)
 
 
 def permute(idx, n_routed: int):
