@@ -67,20 +67,36 @@ int moe_workspace_size(const moe_problem *p, size_t *bytes) {
     return MOE_OK;
 }
 
-int moe_route(const moe_problem *p, const void *x, const float *centroids, const float *bias,
-              int32_t *idx, float *gate, float *probs, int32_t *counts, float *prob_sum, void *ws,
-              size_t ws_bytes, void *stream) {
+int moe_route_ablate(const moe_problem *p, int32_t disabled_top, const void *x, const float *centroids,
+                     const float *bias, int32_t *idx, float *gate, float *probs, int32_t *counts, float *prob_sum,
+                     void *ws, size_t ws_bytes, void *stream) {
     int rc = check_problem(p);
     if (rc != MOE_OK) return rc;
-    if (p->n_routed < 1) return MOE_ERR_INVALID_ARG;
-    if (p->n_routed > kRouteMaxExperts || p->top_k > kRouteMaxTopK) return MOE_ERR_UNSUPPORTED;
+    if (p->n_routed < 1 || disabled_top < 0) return MOE_ERR_INVALID_ARG;
+    if (disabled_top + p->top_k > p->n_routed) return MOE_ERR_INVALID_ARG;
+    if (p->n_routed > kRouteMaxExperts || disabled_top + p->top_k > kRouteMaxTopK) return MOE_ERR_UNSUPPORTED;
     if (!centroids || !counts || !prob_sum) return MOE_ERR_INVALID_ARG;
     if (p->T > 0 && (!x || !idx || !gate)) return MOE_ERR_INVALID_ARG;
     if ((x && !aligned16(x)) || !aligned16(centroids)) return MOE_ERR_INVALID_ARG;
     WsLayout L;
     if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
-    return hip_status(launch_route(*p, x, centroids, bias, idx, gate, probs, (int32_t *)at(ws, L.route_counts), (double *)at(ws, L.route_psum),
-                                   counts, prob_sum, (hipStream_t)stream));
+    return hip_status(launch_route(*p, disabled_top, x, centroids, bias, idx, gate, probs,
+                                   (int32_t *)at(ws, L.route_counts), (double *)at(ws, L.route_psum), counts,
+                                   prob_sum, (hipStream_t)stream));
+}
+
+int moe_route(const moe_problem *p, const void *x, const float *centroids, const float *bias, int32_t *idx,
+              float *gate, float *probs, int32_t *counts, float *prob_sum, void *ws, size_t ws_bytes, void *stream) {
+    return moe_route_ablate(p, 0, x, centroids, bias, idx, gate, probs, counts, prob_sum, ws, ws_bytes, stream);
+}
+
+int moe_route_hash(const moe_problem *p, const int32_t *token_ids, int32_t *idx, float *gate, int32_t *counts,
+                   void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (p->n_routed < 1 || p->top_k != 1) return MOE_ERR_INVALID_ARG;
+    if (!counts || (p->T > 0 && (!token_ids || !idx || !gate))) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_route_hash(*p, token_ids, idx, gate, counts, (hipStream_t)stream));
 }
 
 int moe_permute(const moe_problem *p, const int32_t *idx, int32_t *offsets, int32_t *sorted_token,

@@ -61,10 +61,13 @@ inline WsLayout ws_layout(const moe_problem &p) {
 
 // ---- launchers (each returns hipSuccess or the launch error) -------------
 
-hipError_t launch_route(const moe_problem &p, const void *x, const float *centroids,
+hipError_t launch_route(const moe_problem &p, int skip, const void *x, const float *centroids,
                         const float *bias, int32_t *idx, float *gate, float *probs,
                         int32_t *part_counts, double *part_psum,
                         int32_t *counts, float *prob_sum, hipStream_t s);
+
+hipError_t launch_route_hash(const moe_problem &p, const int32_t *token_ids, int32_t *idx, float *gate,
+                             int32_t *counts, hipStream_t s);
 
 hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *offsets,
                           int32_t *sorted_token, int32_t *slot_of, int32_t *hist,

@@ -99,10 +99,12 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // cross-lane steps overlap.  Adds each token's affinities and selections, in
 // token order, to the lane's running ps / cnt.
 template <int RT, int NJ>
-__device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int lane, const float (&acc)[RT][NJ],
+__device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int skip, int lane,
+                                              const float (&acc)[RT][NJ],
                                               const float *__restrict__ bias, int32_t *__restrict__ idx,
                                               float *__restrict__ gate, float *__restrict__ probs,
                                               double (&ps)[NJ], int (&cnt)[NJ]) {
+    const int KS = K + skip;   // selected, then the first `skip` dropped
     bool ev[NJ];
     float b[NJ];
 #pragma unroll
@@ -159,7 +161,7 @@ __device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int
             int c = 0;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) c += __popcll(__builtin_amdgcn_ballot_w64(key[i][j] >= cand));
-            tau[i] = c >= K ? cand : tau[i];
+            tau[i] = c >= KS ? cand : tau[i];
         }
     }
     // taken: keys above tau, then keys equal to tau by lowest index
@@ -169,7 +171,7 @@ __device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int
         int above = 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) above += __popcll(__builtin_amdgcn_ballot_w64(key[i][j] > tau[i]));
-        const int need = K - above;   // >= 1
+        const int need = KS - above;   // >= 1
         int eq_before = 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -190,7 +192,7 @@ __device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int
             place[i][j] = 0;
             mask[i][j] = __builtin_amdgcn_ballot_w64(sel[i][j]);
         }
-    for (int round = 0; round < K; ++round) {
+    for (int round = 0; round < KS; ++round) {
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             // next taken expert of token i: lowest set bit of the first non-empty group
@@ -223,9 +225,9 @@ __device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int
         const size_t t = (size_t)(t0 + i);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-            if (sel[i][j]) {
-                idx[t * K + place[i][j]] = lane + 64 * j;
-                gate[t * K + place[i][j]] = s[i][j];
+            if (sel[i][j] && place[i][j] >= skip) {   // the top `skip` are disabled
+                idx[t * K + place[i][j] - skip] = lane + 64 * j;
+                gate[t * K + place[i][j] - skip] = s[i][j];
                 cnt[j] += 1;
             }
     }
@@ -238,7 +240,8 @@ __device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int
 // contiguously.  Slices are NE*32+16 bytes apart, so those writes land on
 // distinct banks.
 template <int RT, int NJ, int W, bool XB>
-__global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int K, const void *x, const float *E,
+__global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int K, int skip, const void *x,
+                                                        const float *E,
                                                         const float *__restrict__ bias,
                                                         int32_t *__restrict__ idx, float *__restrict__ gate,
                                                         float *__restrict__ probs, int32_t *__restrict__ part_counts,
@@ -399,7 +402,8 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     int cnt[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) { ps[j] = 0.0; cnt[j] = 0; }
-    if (t0 < T) finish_tokens<RT, NJ>(t0, min(RT, T - t0), Nr, K, lane, acc, bias, idx, gate, probs, ps, cnt);
+    if (t0 < T)
+        finish_tokens<RT, NJ>(t0, min(RT, T - t0), Nr, K, skip, lane, acc, bias, idx, gate, probs, ps, cnt);
 
     // the W waves' per-expert sums, combined in wave order, at row blockIdx.x
     // (the chunk stages are free after the last barrier of the loop)
@@ -459,11 +463,11 @@ int route_waves(int T) { return T >= 2048 ? 8 : 4; }
 int route_tokens_per_wave(int T) { return T >= 16384 ? 4 : T >= 4096 ? 2 : 1; }
 
 template <int RT, int W, bool XB>
-void launch_rtw(const moe_problem &p, int nblk, const void *x, const float *E, const float *bias, int32_t *idx,
-                float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
+void launch_rtw(const moe_problem &p, int skip, int nblk, const void *x, const float *E, const float *bias,
+                int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
     const int nj = cdiv(p.n_routed, 64);
 #define MOE_L(NJ) route_kernel<RT, NJ, W, XB><<<nblk, W * 64, 0, s>>>( \
-        p.T, p.d, p.n_routed, p.top_k, x, E, bias, idx, gate, probs, pc, pp)
+        p.T, p.d, p.n_routed, p.top_k, skip, x, E, bias, idx, gate, probs, pc, pp)
     if (nj == 1) MOE_L(1);
     else if (nj == 2) MOE_L(2);
     else MOE_L(4);
@@ -471,22 +475,22 @@ void launch_rtw(const moe_problem &p, int nblk, const void *x, const float *E, c
 }
 
 template <int RT, bool XB>
-void launch_rt(const moe_problem &p, int nblk, const void *x, const float *E, const float *bias, int32_t *idx,
-               float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
+void launch_rt(const moe_problem &p, int skip, int nblk, const void *x, const float *E, const float *bias,
+               int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
     switch (route_waves(p.T)) {
-        case 8: launch_rtw<RT, 8, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
-        case 4: launch_rtw<RT, 4, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
-        default: launch_rtw<RT, 2, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+        case 8: launch_rtw<RT, 8, XB>(p, skip, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+        case 4: launch_rtw<RT, 4, XB>(p, skip, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+        default: launch_rtw<RT, 2, XB>(p, skip, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
     }
 }
 
 template <bool XB>
-void launch_route_typed(const moe_problem &p, int nblk, const void *x, const float *E, const float *bias,
+void launch_route_typed(const moe_problem &p, int skip, int nblk, const void *x, const float *E, const float *bias,
                         int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
     switch (route_tokens_per_wave(p.T)) {
-        case 4: launch_rt<4, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
-        case 2: launch_rt<2, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
-        default: launch_rt<1, XB>(p, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+        case 4: launch_rt<4, XB>(p, skip, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+        case 2: launch_rt<2, XB>(p, skip, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
+        default: launch_rt<1, XB>(p, skip, nblk, x, E, bias, idx, gate, probs, pc, pp, s); break;
     }
 }
 
@@ -494,19 +498,53 @@ void launch_route_typed(const moe_problem &p, int nblk, const void *x, const flo
 
 int route_blocks(int T) { return cdiv(T, route_waves(T) * route_tokens_per_wave(T)); }
 
-hipError_t launch_route(const moe_problem &p, const void *x, const float *centroids, const float *bias,
+hipError_t launch_route(const moe_problem &p, int skip, const void *x, const float *centroids, const float *bias,
                         int32_t *idx, float *gate, float *probs, int32_t *part_counts, double *part_psum,
                         int32_t *counts, float *prob_sum, hipStream_t s) {
     const int nblk = p.T > 0 ? route_blocks(p.T) : 0;
     if (nblk > 0) {
         if (p.dtype == MOE_BF16)
-            launch_route_typed<true>(p, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
+            launch_route_typed<true>(p, skip, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
         else
-            launch_route_typed<false>(p, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
+            launch_route_typed<false>(p, skip, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum,
+                                      s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     route_reduce_kernel<<<p.n_routed, 256, 0, s>>>(nblk, p.n_routed, part_counts, part_psum, counts, prob_sum);
+    return hipGetLastError();
+}
+
+// Hash routing (the Hash Layer baseline): expert = floor(h * N' / 2^32) with
+// h = id * 2654435761 mod 2^32 (Knuth's multiplicative hash), gate 1; then
+// one workgroup per expert counts its tokens (integer, fixed order).
+namespace {
+__global__ __launch_bounds__(256) void route_hash_kernel(int T, int Nr, const int32_t *__restrict__ ids,
+                                                         int32_t *__restrict__ idx, float *__restrict__ gate) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    const uint32_t h = (uint32_t)ids[t] * 2654435761u;
+    idx[t] = (int32_t)(((uint64_t)h * (uint64_t)Nr) >> 32);
+    gate[t] = 1.0f;
+}
+__global__ __launch_bounds__(256) void route_hash_counts_kernel(int T, const int32_t *__restrict__ idx,
+                                                                int32_t *__restrict__ counts) {
+    __shared__ int s_c[4];
+    const int r = blockIdx.x;
+    int c = 0;
+    for (int t = threadIdx.x; t < T; t += 256) c += idx[t] == r ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    if ((threadIdx.x & 63) == 0) s_c[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) counts[r] = s_c[0] + s_c[1] + s_c[2] + s_c[3];
+}
+}  // namespace
+
+hipError_t launch_route_hash(const moe_problem &p, const int32_t *token_ids, int32_t *idx, float *gate,
+                             int32_t *counts, hipStream_t s) {
+    if (p.T > 0) route_hash_kernel<<<cdiv(p.T, 256), 256, 0, s>>>(p.T, p.n_routed, token_ids, idx, gate);
+    route_hash_counts_kernel<<<p.n_routed, 256, 0, s>>>(p.T, idx, counts);
     return hipGetLastError();
 }
 

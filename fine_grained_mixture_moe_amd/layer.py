@@ -94,6 +94,13 @@ class DeviceLayer:
         M.moe_route(self.prob, self.x, self.centroids, self.bias, self.idx, self.gate, self.probs, self.counts,
                     self.prob_sum, self.ws, self.ws_bytes, stream)
 
+    def route_ablate(self, disabled_top: int, stream=None):
+        M.moe_route_ablate(self.prob, disabled_top, self.x, self.centroids, self.bias, self.idx, self.gate,
+                           self.probs, self.counts, self.prob_sum, self.ws, self.ws_bytes, stream)
+
+    def route_hash(self, token_ids, stream=None):
+        M.moe_route_hash(self.prob, token_ids, self.idx, self.gate, self.counts, stream)
+
     def permute(self, stream=None):
         M.moe_permute(self.prob, self.idx, self.offsets, self.sorted_token, self.slot_of, self.ws, self.ws_bytes,
                       stream)

@@ -64,13 +64,16 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_down.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_combine.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_balance_stats.argtypes = [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_route_ablate.argtypes = [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_route_hash.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp]
         L.moe_backward_workspace_size.argtypes = [_pp, ctypes.POINTER(_sz)]
         L.moe_combine_backward.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_expert_ffn_backward.argtypes = [_pp] + [_vp] * 20 + [_sz, _vp]
         L.moe_route_backward.argtypes = [_pp, ctypes.c_int32, ctypes.c_float, ctypes.c_float] + [_vp] * 13 + [_sz, _vp]
         for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up",
                    "moe_expert_down", "moe_combine", "moe_balance_stats", "moe_backward_workspace_size",
-                   "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward"):
+                   "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward", "moe_route_ablate",
+                   "moe_route_hash"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -114,6 +117,18 @@ def moe_route(p, x, centroids, bias, idx, gate, probs, counts, prob_sum, ws, ws_
     _check("moe_route", lib().moe_route(ctypes.byref(p), _ptr(x), _ptr(centroids), _ptr(bias), _ptr(idx),
                                         _ptr(gate), _ptr(probs), _ptr(counts), _ptr(prob_sum), _ptr(ws),
                                         ws_bytes, _stream(stream)))
+
+
+def moe_route_ablate(p, disabled_top, x, centroids, bias, idx, gate, probs, counts, prob_sum, ws, ws_bytes,
+                     stream=None):
+    _check("moe_route_ablate", lib().moe_route_ablate(ctypes.byref(p), int(disabled_top), _ptr(x), _ptr(centroids),
+                                                      _ptr(bias), _ptr(idx), _ptr(gate), _ptr(probs), _ptr(counts),
+                                                      _ptr(prob_sum), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_route_hash(p, token_ids, idx, gate, counts, stream=None):
+    _check("moe_route_hash", lib().moe_route_hash(ctypes.byref(p), _ptr(token_ids), _ptr(idx), _ptr(gate),
+                                                  _ptr(counts), _stream(stream)))
 
 
 def moe_permute(p, idx, offsets, sorted_token, slot_of, ws, ws_bytes, stream=None):

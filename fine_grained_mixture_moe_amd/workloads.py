@@ -257,11 +257,40 @@ def make_random_case(T: int, d: int, n_shared: int, n_routed: int, top_k: int, i
     return LayerInputs(wl, make_x(wl), make_centroids(wl), make_bias(wl), w1, w3, w2)
 
 
+def ablated_inputs(inp: LayerInputs, drop_shared: bool = False, top_k: Optional[int] = None) -> LayerInputs:
+    """The same layer (same tokens, router and expert weights) run with fewer experts:
+    the shared experts removed and/or a different number K' of activated routed experts.
+    These are the inference-time ablations of the paper's expert-specialization analysis
+    (shared expert disabled; only 4 routed experts activated; Switch-style top-1)."""
+    wl = inp.wl
+    ks = wl.n_shared
+    k = wl.top_k if top_k is None else top_k
+    name = wl.name + ("-noshared" if drop_shared else "") + (f"-top{k}" if top_k is not None else "")
+    nwl = wl.replace(name=name, n_shared=0 if drop_shared else ks, top_k=k,
+                     description=f"{wl.description} [ablation: shared {'off' if drop_shared else 'on'}, top-{k}]")
+    cut = ks if drop_shared else 0
+
+    def keep(t: Tensor) -> Tensor:
+        return Tensor(t.f32[cut:], None if t.bf16 is None else t.bf16[cut:])
+
+    return LayerInputs(nwl, inp.x, inp.centroids, inp.bias, keep(inp.w1), keep(inp.w3), keep(inp.w2))
+
+
 def balanced_routing(T: int, n_routed: int, top_k: int) -> np.ndarray:
     """idx[t, k] = (t*K' + k) mod N': every expert gets exactly K'T/N' tokens when N' | K'T."""
     t = np.arange(T, dtype=np.int64)[:, None]
     k = np.arange(top_k, dtype=np.int64)[None, :]
     return ((t * top_k + k) % n_routed).astype(np.int32)
+
+
+def token_ids(T: int, vocab: int, seed: int = 0, zipf_s: float = 1.0) -> np.ndarray:
+    """Seeded token ids in [0, vocab) with a Zipf(s) frequency law over a shuffled vocabulary
+    (text-like repetition: frequent ids recur, so hash routing sees realistic collisions).
+    The 2B validation model uses an 8K vocabulary, the 16B model a 100K one."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([515151, T, vocab, seed])))
+    p = 1.0 / np.arange(1, vocab + 1, dtype=np.float64) ** zipf_s
+    ranks = rng.choice(vocab, size=T, p=p / p.sum())
+    return rng.permutation(vocab)[ranks].astype(np.int32)
 
 
 def sample_tokens(T: int, n: int, seed: int = 7) -> np.ndarray:

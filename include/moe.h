@@ -116,6 +116,34 @@ int moe_route(const moe_problem *p, const void *x, const float *centroids,
               void *stream);
 
 /*
+ * moe_route_ablate -- moe_route with each token's `disabled_top` highest
+ * ranked routed experts disabled: the token takes the experts of ranks
+ * disabled_top .. disabled_top+K'-1 in the order (z desc, r asc).  This is the
+ * redundancy ablation of "[ACL 2024] DeepSeekMoE ..." section "Expert
+ * specialization analysis" (Fig. 4, disabling the top routed experts).
+ * Affinities, gates (not renormalised), probs and prob_sum are as in
+ * moe_route; counts count the taken experts.  disabled_top = 0 is moe_route.
+ * Envelope: disabled_top + K' <= min(N', 16).
+ */
+int moe_route_ablate(const moe_problem *p, int32_t disabled_top, const void *x, const float *centroids,
+                     const float *bias, int32_t *idx, float *gate, float *probs, int32_t *counts, float *prob_sum,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_route_hash -- fixed hash routing, the Hash Layer baseline of "[ACL
+ * 2024] DeepSeekMoE ..." section "Experiment design": one expert per token
+ * from its token id, gate 1 (no learned gate).  K' must be 1.
+ *   token_ids [T] int32 in;  idx [T, 1] int32 out;  gate [T, 1] fp32 out (1.0)
+ *   counts [N'] int32 out
+ *   expert = floor(h * N' / 2^32),  h = id * 2654435761 mod 2^32 (uint32)
+ * (Knuth's multiplicative hash with a multiply-shift range reduction; the
+ * pages name the baseline, not its hash).  The rest of the layer (permute,
+ * expert FFNs, combine) runs unchanged on this routing.
+ */
+int moe_route_hash(const moe_problem *p, const int32_t *token_ids, int32_t *idx, float *gate, int32_t *counts,
+                   void *stream);
+
+/*
  * moe_permute -- group (token, expert) pairs by routed expert: histogram,
  * exclusive scan, stable scatter (tokens ascending within an expert).  This
  * is the bookkeeping behind "token t selects expert i" ("【论文总结】MoE"

@@ -127,3 +127,25 @@ def test_backward_calls_reject_bad_arguments_before_launch():
         a[2] = None
         M.moe_route_backward(p, 2, 0.1, 0.1, *a, FAKE, wsb, 0)
     assert e.value.status == M.MOE_ERR_INVALID_ARG
+
+
+def test_routing_variants_reject_bad_arguments_before_launch():
+    p = M.moe_problem.make(64, 128, 1, 8, 2, 64, "f32")
+    ws = M.moe_workspace_size(p)
+    a = [FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, 0]
+    for skip, status in ((-1, M.MOE_ERR_INVALID_ARG),      # negative count
+                         (7, M.MOE_ERR_INVALID_ARG)):      # skip + K' > N'
+        with pytest.raises(M.MoEError) as e:
+            M.moe_route_ablate(p, skip, *a)
+        assert e.value.status == status
+    q = M.moe_problem.make(64, 128, 0, 64, 4, 64, "f32")   # skip + K' beyond the 16-way selection
+    with pytest.raises(M.MoEError) as e:
+        M.moe_route_ablate(q, 13, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, 0)
+    assert e.value.status == M.MOE_ERR_UNSUPPORTED
+    with pytest.raises(M.MoEError) as e:                    # hash routing takes one expert per token
+        M.moe_route_hash(p, FAKE, FAKE, FAKE, FAKE, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    h = M.moe_problem.make(64, 128, 1, 8, 1, 64, "f32")
+    with pytest.raises(M.MoEError) as e:                    # token ids missing
+        M.moe_route_hash(h, None, FAKE, FAKE, FAKE, 0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
