@@ -1,8 +1,9 @@
 """Benchmark of the DeepSeekMoE layer forward on one MI355X.
 
 One step = one whole layer pass through the C ABI on synthetic seeded inputs
-already resident in HBM: moe_route -> moe_permute -> moe_expert_up ->
-moe_expert_down -> moe_combine -> moe_balance_stats.  Prints ONE JSON line.
+already resident in HBM: moe_route -> moe_permute -> moe_expert_ffn (bf16: the
+up and down projections in one fused launch) -> moe_combine ->
+moe_balance_stats.  Prints ONE JSON line.
 
 Default workload: the fine-grained half of the granularity-equivalence pair
 (T=4096, d=1280, 64 routed experts of width 512, top-8, bf16); the
@@ -54,18 +55,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def up_algorithmic(wl, counts) -> dict:
-    """Algorithmic work of one up-projection launch (gate+up GEMMs with SwiGLU).
+def ffn_algorithmic(wl, counts) -> dict:
+    """Algorithmic work of one moe_expert_ffn call (both projections of every expert).
 
-    Per (token, expert) pair: 4*d*w FLOPs (two d x w products).  Bytes: W1 and
-    W3 of every touched expert (all shared + routed experts with tokens), the
-    token rows read once, the SwiGLU activations written once.
+    Per (token, expert) pair: 6*d*w FLOPs (gate and up: 2 x 2*d*w, down: 2*d*w).
+    Bytes: W1, W3 and W2 of every touched expert (all shared + routed experts with
+    tokens), the token rows read once, the routed outputs written once (dtype) and
+    the shared output (fp32).  The SwiGLU activations are an intermediate: their
+    round trip through HBM is implementation traffic (it shows in the measured
+    FETCH/WRITE counters), not part of the algorithmic minimum.
     """
     es = 2 if wl.dtype == "bf16" else 4
     pairs = wl.T * (wl.top_k + wl.n_shared)
-    flops = 4.0 * wl.d * wl.inter * pairs
+    flops = 6.0 * wl.d * wl.inter * pairs
     touched = wl.n_shared + int((counts > 0).sum())
-    byts = 2.0 * wl.inter * wl.d * es * touched + wl.T * wl.d * es + pairs * wl.inter * es
+    byts = (3.0 * wl.inter * wl.d * es * touched + wl.T * wl.d * es
+            + wl.T * wl.top_k * wl.d * es + (wl.T * wl.d * 4 if wl.n_shared else 0))
     return dict(flops=flops, bytes=byts, pairs=pairs, touched=touched)
 
 
@@ -143,10 +148,9 @@ def run(args) -> dict:
         dl.permute()
         if ev is not None:
             ev[0].record(stream)
-        dl.expert_up()
+        dl.expert_ffn()
         if ev is not None:
             ev[1].record(stream)
-        dl.expert_down()
         dl.combine()
         dl.balance_stats()
 
@@ -161,12 +165,12 @@ def run(args) -> dict:
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    up_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ffn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     ms = elapsed * 1e3 / args.steps
     counts = dl.counts.cpu().numpy()[:wl.n_routed]
 
     # per-stage breakdown (separate, untimed-for-value loop)
-    stages = ["route", "permute", "expert_up", "expert_down", "combine", "balance_stats"]
+    stages = ["route", "permute", "expert_ffn", "combine", "balance_stats"]
     n_b = min(args.steps, 10)
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_b)]
     for i in range(n_b):
@@ -186,27 +190,29 @@ def run(args) -> dict:
         torch.cuda.synchronize()
         log(f"[bench] copy probe: 3 x {COPY_BYTES} bytes")
 
-    up = up_algorithmic(wl, counts)
+    ffn = ffn_algorithmic(wl, counts)
     tflops = wl.flops() / (ms * 1e-3) / 1e12
-    ai = up["flops"] / up["bytes"]
+    ai = ffn["flops"] / ffn["bytes"]
     mfma_peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if ai >= ridge:
-        achieved = up["flops"] / (up_ms * 1e-3) / 1e12
+        achieved = ffn["flops"] / (ffn_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": mfma_peak, "unit": "TFLOP/s",
                 "frac": round(achieved / mfma_peak, 4)}
     else:
-        achieved = up["bytes"] / (up_ms * 1e-3) / 1e9
+        achieved = ffn["bytes"] / (ffn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    tr = load_traffic("up", name)
+    tr = load_traffic("ffn", name)
     roof["traffic"] = None if tr is None else tr["bytes_per_launch"]
     avg_rows = wl.T * wl.top_k / wl.n_routed if wl.n_routed else wl.T
-    roof["kernel"] = (f"grouped_ffn_bf16_kernel<{256 if avg_rows >= 256 else 128}, up>" if wl.dtype == "bf16"
-                      else "grouped_ffn_kernel<f32, up>")
-    roof["kernel_ms"] = round(up_ms, 4)
-    roof["algorithmic"] = {"flops": up["flops"], "bytes": up["bytes"], "pairs": up["pairs"],
-                           "touched_experts": up["touched"]}
+    # the events bracket the whole moe_expert_ffn call: for bf16 the fused launch
+    # plus the 1-block kernel that clears its control words before it
+    roof["kernel"] = (f"grouped_ffn_fused_kernel<{256 if avg_rows >= 256 else 128}> (up + down)" if wl.dtype == "bf16"
+                      else "grouped_ffn_kernel<f32, up> + grouped_ffn_kernel<f32, down>")
+    roof["kernel_ms"] = round(ffn_ms, 4)
+    roof["algorithmic"] = {"flops": ffn["flops"], "bytes": ffn["bytes"], "pairs": ffn["pairs"],
+                           "touched_experts": ffn["touched"]}
 
     out = {
         "metric": METRIC,
@@ -321,7 +327,8 @@ def run_backward(args) -> dict:
 
 
 def ingest_pmc(pmc_dir: str, workload: str) -> None:
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the up kernel, scaled by the copy probe's readings."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused expert-FFN kernel, scaled by the copy
+    probe's readings."""
     rows = []
     for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
@@ -332,13 +339,8 @@ def ingest_pmc(pmc_dir: str, workload: str) -> None:
     for r in rows:
         kname = r.get("Kernel_Name", "")
         cname = r.get("Counter_Name", "")
-        # template arguments <BM, UP, BWD>: the forward up projection is <*, true, false>
-        if "grouped_ffn" in kname and (", true, false>" in kname or "Lb1ELb0E" in kname):
-            key = "up"
-        elif "grouped_ffn" in kname and ", true, true>" in kname:
-            continue
-        elif "grouped_ffn" in kname:
-            key = "down"
+        if "grouped_ffn_fused_kernel" in kname:
+            key = "ffn"
         elif "elementwise" in kname.lower():
             key = "copy"
         else:
@@ -347,17 +349,17 @@ def ingest_pmc(pmc_dir: str, workload: str) -> None:
     rec = {"workload": workload, "source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
     for cname in ("FETCH_SIZE", "WRITE_SIZE"):
         cp = per.get(("copy", cname))
-        up = per.get(("up", cname))
-        if not cp or not up:
+        k = per.get(("ffn", cname))
+        if not cp or not k:
             continue
         # copy reads COPY_BYTES and writes COPY_BYTES: bytes per counter unit
         copy_kib = max(cp)
         scale = COPY_BYTES / copy_kib
-        rec[cname] = {"up_kib_per_dispatch": sum(up) / len(up), "copy_kib": copy_kib, "bytes_per_unit": scale,
-                      "up_bytes": sum(up) / len(up) * scale}
+        rec[cname] = {"kib_per_dispatch": sum(k) / len(k), "dispatches": len(k), "copy_kib": copy_kib,
+                      "bytes_per_unit": scale, "bytes": sum(k) / len(k) * scale}
     if "FETCH_SIZE" in rec and "WRITE_SIZE" in rec:
-        rec["bytes_per_launch"] = rec["FETCH_SIZE"]["up_bytes"] + rec["WRITE_SIZE"]["up_bytes"]
-    out = os.path.join(ROOT, "profiles", f"traffic_up_{workload}.json")
+        rec["bytes_per_launch"] = rec["FETCH_SIZE"]["bytes"] + rec["WRITE_SIZE"]["bytes"]
+    out = os.path.join(ROOT, "profiles", f"traffic_ffn_{workload}.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))

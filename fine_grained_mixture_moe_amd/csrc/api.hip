@@ -211,9 +211,7 @@ int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets, 
     const FfnArgs a = ffn_args(x, offsets, sorted_token, w1_routed, w3_routed, w2_routed, w1_shared, w3_shared,
                                w2_shared, y_routed, y_shared, ws, L);
     const moe_problem q = active_part(*p, routed, shared);
-    hipError_t e = launch_expert_up(q, a, (hipStream_t)stream);
-    if (e == hipSuccess) e = launch_expert_down(q, a, (hipStream_t)stream);
-    return hip_status(e);
+    return hip_status(launch_expert_ffn(q, a, (int32_t *)at(ws, L.ffn_ctl), (hipStream_t)stream));
 }
 
 int moe_combine(const moe_problem *p, const void *x, const void *y_routed, const float *y_shared,

@@ -308,13 +308,35 @@ constexpr uint32_t kOOB = 0x80000000u;   // offset beyond any buffer: reads as z
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Cache policy of the loads and stores that carry data between workgroups of
+// one launch: sc1, the agent-coherent form (what the compiler emits for
+// relaxed agent-scope atomic loads and stores), visible across the XCDs' L2s.
+constexpr int kCoherent = 16;
+template <int AUX = 0>
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int AUX = 0>
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint4 v) {
+    v4u w;
+    w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, 0, AUX);
+}
 
-template <int BM, bool UP, bool BWD = false>
-__global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
+// One tile of the bf16 grouped GEMM: rows [m0, m0+nr) of a group (the
+// shared experts, or routed expert r) against weight tile n_tile.  FUSED:
+// the tile runs inside the fused up+down launch, whose activations pass
+// between workgroups through agent-coherent stores and loads.
+struct TileDesc {
+    bool shared;
+    int r, row_off, m0, nr, n_tile;
+};
+
+template <int BM, bool UP, bool BWD, bool FUSED>
+__device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDesc td, uint8_t (&s_w)[2][256 * 128],
+                                              uint8_t (&s_x)[2][BM * 128], int (&s_src)[BM],
+                                              int *head = nullptr, int *next = nullptr) {
     static_assert(!BWD || UP, "the backward epilogue belongs to the up projection");
     constexpr int NT = 512;          // threads: 8 waves, 2 per SIMD
     constexpr int BN = 256;          // weight rows per tile
@@ -323,68 +345,14 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
     constexpr int NB = 2;            // 32-row weight blocks per wave
     constexpr int CW = BN * 8 / NT;  // weight chunks per thread (4)
     constexpr int CX = BM * 8 / NT;  // token chunks per thread (4 or 2)
-    __shared__ __attribute__((aligned(16))) uint8_t s_w[2][BN * RB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * RB];
-    __shared__ int s_pref[MAXG + 1];
-    __shared__ int s_src[BM];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int G = (P.Ks > 0 ? 1 : 0) + P.Nr;
-    const int ntn_s = UP ? cdiv(P.Ks * P.w, 128) : cdiv(P.d, BN);
-    const int ntn_r = UP ? cdiv(P.w, 128) : cdiv(P.d, BN);
-
-    if (wave == 0) {
-        int carry = 0;
-        if (lane == 0) s_pref[0] = 0;
-        for (int g0 = 0; g0 < G; g0 += 64) {
-            const int g = g0 + lane;
-            int tiles = 0;
-            if (g < G) {
-                const bool sh = P.Ks > 0 && g == 0;
-                const int r = g - (P.Ks > 0 ? 1 : 0);
-                const int rows = sh ? P.T : P.offsets[r + 1] - P.offsets[r];
-                tiles = cdiv(rows, BM) * (sh ? ntn_s : ntn_r);
-            }
-            int incl = tiles;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int v = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += v;
-            }
-            if (g < G) s_pref[g + 1] = carry + incl;
-            carry += __shfl(incl, 63, 64);
-        }
-    }
-    __syncthreads();
-    const int total = s_pref[G];
-    const int bid = blockIdx.x;
-    if (bid >= total) return;
-    // Renumbering: workgroups reach the 8 XCDs round-robin, so within each run
-    // of 256 workgroups XCD x gets the 32 consecutive tiles [32x, 32x+32) of
-    // that run (they are co-resident there and share operands in its L2);
-    // runs follow each other in tile order, which keeps the XCDs balanced.
-    // The tail run (< 256 tiles) keeps the identity order.
-    const int L = (bid < (total & ~255)) ? ((bid & ~255) + (bid & 7) * 32 + ((bid >> 3) & 31)) : bid;
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] <= L) lo = mid; else hi = mid;
-    }
-    const int g = lo;
-    const bool shared = P.Ks > 0 && g == 0;
-    const int r = g - (P.Ks > 0 ? 1 : 0);
-    const int row_off = shared ? 0 : P.offsets[r];
-    const int rows = shared ? P.T : P.offsets[r + 1] - row_off;
-    const int mt = cdiv(rows, BM);
-    const int lt = L - s_pref[g];
-    const int m_tile = lt % mt, n_tile = lt / mt;
-    // The group's rows are cut into mt runs of equal length rounded up to 32
-    // (never above BM, never empty), so a group of 530 rows makes tiles of
-    // 192, 192 and 146 rows instead of 256, 256 and 18: the work of a tile
-    // follows its live 32-row blocks, which the waves skip when empty.
-    const int run = (cdiv(rows, mt) + 31) & ~31;
-    const int m0 = m_tile * run;
-    const int nr = min(run, rows - m0);
+    int tid_ = threadIdx.x;
+    // in the persistent launch, keep the lane-dependent offsets inside the tile:
+    // hoisted out of the tile loop they would stay live across both projections
+    // and spill (the empty asm is opaque to loop-invariant code motion)
+    if constexpr (FUSED) asm volatile("" : "+v"(tid_));
+    const int tid = tid_, lane = tid & 63, wave = tid >> 6;
+    const bool shared = td.shared;
+    const int r = td.r, row_off = td.row_off, m0 = td.m0, nr = td.nr, n_tile = td.n_tile;
 
     const int K = UP ? P.d : (shared ? P.Ks * P.w : P.w);
     const uint32_t xpitch = (uint32_t)K * 2u;   // token-side row bytes
@@ -449,7 +417,7 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
         if (toks) {
 #pragma unroll
             for (int i = 0; i < CX; ++i)
-                if (i * 4 / CX == ph) sx[i] = bload(rx, ox[i], kx);
+                if (i * 4 / CX == ph) sx[i] = bload<(FUSED && !UP) ? kCoherent : 0>(rx, ox[i], kx);
         }
     };
     auto sstore_part = [&](int stg, int ph) {
@@ -579,6 +547,12 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
         else kloop(integral_constant<int, 0>{});
     }
 
+    // the fused launch takes its next ticket here: a device-scope atomic has
+    // microseconds of latency, which the epilogue hides (issued before the
+    // tile, the first wait on the tile's loads would wait for it as well)
+    if constexpr (FUSED) {
+        if (tid == 0) *next = atomicAdd(head, 1);
+    }
     // ---- epilogue: lane owns token column l32 of each block; register quad q
     //      holds weight rows 8q + 4*lhi + {0..3} of the block ----
     if (!UP && shared) {
@@ -725,6 +699,9 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
     const int ld = UP ? (shared ? P.Ks * P.w : P.w) : P.d;   // features of an output row
     const int col0 = n_tile * NC;
     uint16_t *out = (uint16_t *)(UP && shared ? P.out_shared : P.out_routed);
+    // in the fused launch the activations go out as agent-coherent stores: the
+    // down tiles that read them may run on another XCD, behind another L2
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + (size_t)(row_off + m0) * ld, (uint32_t)((size_t)nr * ld * 2));
     constexpr int ITER = BM * C16 / NT;   // 16-byte pieces per thread
     uint4 piece[ITER];
 #pragma unroll
@@ -736,10 +713,240 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
     for (int it = 0; it < ITER; ++it) {
         const int i = tid + it * NT;
         const int r = i / C16, c = i % C16;
-        if (r < nr && col0 + c * 8 < ld)
-            *(uint4 *)(out + (size_t)(row_off + m0 + r) * ld + col0 + c * 8) = piece[it];
+        if (r < nr && col0 + c * 8 < ld) {
+            if constexpr (FUSED && UP) bstore<kCoherent>(rout, ((uint32_t)r * ld + col0 + c * 8) * 2u, piece[it]);
+            else *(uint4 *)(out + (size_t)(row_off + m0 + r) * ld + col0 + c * 8) = piece[it];
+        }
     }
     }
+}
+
+template <int BM, bool UP, bool BWD = false>
+__global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
+    constexpr int BN = 256;          // weight rows per tile
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[2][256 * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * 128];
+    __shared__ int s_pref[MAXG + 1];
+    __shared__ int s_src[BM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = (P.Ks > 0 ? 1 : 0) + P.Nr;
+    const int ntn_s = UP ? cdiv(P.Ks * P.w, 128) : cdiv(P.d, BN);
+    const int ntn_r = UP ? cdiv(P.w, 128) : cdiv(P.d, BN);
+
+    if (wave == 0) {
+        int carry = 0;
+        if (lane == 0) s_pref[0] = 0;
+        for (int g0 = 0; g0 < G; g0 += 64) {
+            const int g = g0 + lane;
+            int tiles = 0;
+            if (g < G) {
+                const bool sh = P.Ks > 0 && g == 0;
+                const int r = g - (P.Ks > 0 ? 1 : 0);
+                const int rows = sh ? P.T : P.offsets[r + 1] - P.offsets[r];
+                tiles = cdiv(rows, BM) * (sh ? ntn_s : ntn_r);
+            }
+            int incl = tiles;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += v;
+            }
+            if (g < G) s_pref[g + 1] = carry + incl;
+            carry += __shfl(incl, 63, 64);
+        }
+    }
+    __syncthreads();
+    const int total = s_pref[G];
+    const int bid = blockIdx.x;
+    if (bid >= total) return;
+    // Renumbering: workgroups reach the 8 XCDs round-robin, so within each run
+    // of 256 workgroups XCD x gets the 32 consecutive tiles [32x, 32x+32) of
+    // that run (they are co-resident there and share operands in its L2);
+    // runs follow each other in tile order, which keeps the XCDs balanced.
+    // The tail run (< 256 tiles) keeps the identity order.
+    const int L = (bid < (total & ~255)) ? ((bid & ~255) + (bid & 7) * 32 + ((bid >> 3) & 31)) : bid;
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= L) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const bool shared = P.Ks > 0 && g == 0;
+    const int r = g - (P.Ks > 0 ? 1 : 0);
+    const int row_off = shared ? 0 : P.offsets[r];
+    const int rows = shared ? P.T : P.offsets[r + 1] - row_off;
+    const int mt = cdiv(rows, BM);
+    const int lt = L - s_pref[g];
+    const int m_tile = lt % mt, n_tile = lt / mt;
+    // The group's rows are cut into mt runs of equal length rounded up to 32
+    // (never above BM, never empty), so a group of 530 rows makes tiles of
+    // 192, 192 and 146 rows instead of 256, 256 and 18: the work of a tile
+    // follows its live 32-row blocks, which the waves skip when empty.
+    const int run = (cdiv(rows, mt) + 31) & ~31;
+    const int m0 = m_tile * run;
+    const int nr = min(run, rows - m0);
+    ffn_tile_bf16<BM, UP, BWD, false>(P, TileDesc{shared, r, row_off, m0, nr, n_tile}, s_w, s_x, s_src);
+}
+
+// ---------------------------------------------------------------------------
+// Fused expert FFN: the up and the down projection of every group in ONE
+// persistent launch of one workgroup per CU.
+//
+// Separate launches leave each projection with its own partial last round of
+// tiles (c2b: 640 up tiles = 2.5 per CU, 800 down tiles = 3.1 per CU), so a
+// third of the up launch and a quarter of the down launch run with most CUs
+// idle.  Here the tiles of both projections share one schedule:
+//   * a token run is one of the mt equal row runs of a group (as in the
+//     separate kernels); its up tiles write the run's activations, its down
+//     tiles read them;
+//   * the runs are split into kQueues contiguous ranges, one queue per XCD
+//     (workgroup b starts on queue b % 8, the XCD the hardware gives it), so
+//     the tiles of one expert stay on one XCD and share its L2;
+//   * inside a queue, tickets are taken in order from an atomic counter: all
+//     up tiles of the queue's runs (run-major), then all its down tiles; a
+//     workgroup whose queue is empty takes tickets from the other queues;
+//   * a down tile waits until the up tiles of its run are done (a per-run
+//     counter, bumped after the tile's coherent activation stores complete).
+// No wait can deadlock: a ticket is only ever held by a running workgroup,
+// up tiles never wait, a down tile's up tiles precede it in its queue, and a
+// workgroup takes its next ticket only after the current tile's wait is
+// over.  The wait is still bounded (kSpinLimit sleeps, then an error flag).
+// ---------------------------------------------------------------------------
+constexpr int kQueues = 8;
+constexpr int kSpinLimit = 1 << 22;
+
+struct FusedCtl {
+    int *head;   // [kQueues] next ticket of each queue
+    int *err;    // [1] set when a wait ran out of its budget
+    int *done;   // [runs] finished up tiles of each token run
+};
+
+template <int BM>
+__global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, GemmParams Pd, FusedCtl C) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[2][256 * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * 128];
+    __shared__ int s_src[BM];
+    __shared__ int s_runp[MAXG + 1];   // prefix of the token runs over the groups
+    __shared__ int s_offs[MAXG + 1];   // the routed group offsets
+    __shared__ int s_ticket;
+
+    const GemmParams &P = Pu;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = (P.Ks > 0 ? 1 : 0) + P.Nr;
+    if (wave == 0) {
+        int carry = 0;
+        if (lane == 0) s_runp[0] = 0;
+        for (int g0 = 0; g0 < G; g0 += 64) {
+            const int g = g0 + lane;
+            int runs = 0;
+            if (g < G) {
+                int rows = P.T;
+                if (!(P.Ks > 0 && g == 0)) {
+                    const int r = g - (P.Ks > 0 ? 1 : 0);
+                    const int a = P.offsets[r], b = P.offsets[r + 1];
+                    rows = b - a;
+                    s_offs[r] = a;
+                    if (r + 1 == P.Nr) s_offs[P.Nr] = b;
+                }
+                runs = cdiv(rows, BM);
+            }
+            int incl = runs;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += v;
+            }
+            if (g < G) s_runp[g + 1] = carry + incl;
+            carry += __shfl(incl, 63, 64);
+        }
+    }
+    __syncthreads();
+    // wave-uniform bookkeeping lives in SGPRs (readfirstlane of the LDS values):
+    // the tile bodies need every VGPR
+    auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    const int R = uni(s_runp[G]);
+    const int mts = P.Ks > 0 ? uni(s_runp[1]) : 0;                  // runs of the shared group
+    const int nus = cdiv(P.Ks * P.w, 128), nur = cdiv(P.w, 128);    // up tiles per run
+    const int nd = cdiv(P.d, 256);                                  // down tiles per run
+    auto upp = [&](int r) { return r * nur + min(r, mts) * (nus - nur); };   // up tiles before run r
+
+    const int q0 = blockIdx.x % kQueues;
+    for (int qi = 0; qi < kQueues; ++qi) {
+        const int q = (q0 + qi) % kQueues;
+        const int ra = (int)((int64_t)R * q / kQueues), rb = (int)((int64_t)R * (q + 1) / kQueues);
+        const int u0 = upp(ra), nU = upp(rb) - u0;
+        const int len = nU + (rb - ra) * nd;
+        if (len == 0) continue;
+        if (tid == 0) s_ticket = atomicAdd(&C.head[q], 1);
+        __syncthreads();
+        int t = uni(s_ticket);
+        __syncthreads();   // every wave has read the ticket before it is rewritten
+        while (t < len) {
+            const bool up = t < nU;
+            int run, n;
+            if (up) {
+                const int u = u0 + t;
+                if (u < mts * nus) { run = u / nus; n = u % nus; }
+                else { const int v = u - mts * nus; run = mts + v / nur; n = v % nur; }
+            } else {
+                const int v = t - nU;
+                run = ra + v / nd;
+                n = v % nd;
+            }
+            // group of the run: the number of prefix entries s_runp[1..G] <= run,
+            // one ballot per 64 groups (each wave on its own)
+            int g = 0;
+            for (int g0 = 1; g0 <= G; g0 += 64) {
+                const int gi = g0 + lane;
+                const bool le = gi <= G && s_runp[gi] <= run;
+                g += __builtin_popcountll(__ballot(le));
+            }
+            g = uni(g);
+            TileDesc td;
+            td.shared = P.Ks > 0 && g == 0;
+            td.r = g - (P.Ks > 0 ? 1 : 0);
+            td.row_off = td.shared ? 0 : uni(s_offs[td.r]);
+            const int rows = td.shared ? P.T : uni(s_offs[td.r + 1]) - td.row_off;
+            const int rp = uni(s_runp[g]);
+            const int mt = uni(s_runp[g + 1]) - rp;
+            const int rl = (cdiv(rows, mt) + 31) & ~31;
+            td.m0 = (run - rp) * rl;
+            td.nr = min(rl, rows - td.m0);
+            td.n_tile = n;
+            if (!up) {
+                const int need = td.shared ? nus : nur;
+                if (tid == 0) {
+                    int spins = 0;
+                    while (__hip_atomic_load(&C.done[run], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+                        if (++spins > kSpinLimit) {
+                            __hip_atomic_store(C.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(4);
+                    }
+                }
+                __syncthreads();
+            }
+            int next = 0;
+            if (up) {
+                ffn_tile_bf16<BM, true, false, true>(Pu, td, s_w, s_x, s_src, &C.head[q], &next);
+                __builtin_amdgcn_s_waitcnt(0);   // this thread's activation stores are complete
+                __syncthreads();
+                if (tid == 0) __hip_atomic_fetch_add(&C.done[run], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                ffn_tile_bf16<BM, false, false, true>(Pd, td, s_w, s_x, s_src, &C.head[q], &next);
+            }
+            if (tid == 0) s_ticket = next;
+            __syncthreads();
+            t = uni(s_ticket);
+            __syncthreads();
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void ffn_ctl_zero_kernel(int *ctl, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) ctl[i] = 0;
 }
 
 GemmParams make_params(const moe_problem &p, const FfnArgs &a, bool up) {
@@ -798,6 +1005,21 @@ hipError_t launch_bf16(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_fused(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s) {
+    const int n = ffn_ctl_ints(p);
+    ffn_ctl_zero_kernel<<<min(cdiv(n, 256), 64), 256, 0, s>>>(ctl, n);
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const GemmParams Pu = make_params(p, a, true), Pd = make_params(p, a, false);
+    const FusedCtl C{ctl, ctl + kQueues, ctl + kQueues + 1};
+    const int64_t avg = p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / p.n_routed : (int64_t)p.T;
+    if (avg >= 256) grouped_ffn_fused_kernel<256><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+    else grouped_ffn_fused_kernel<128><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Backward recompute of the up projection (bf16): act_* <- a, dp_*, dq_* from da_*.
@@ -832,6 +1054,13 @@ hipError_t launch_expert_up(const moe_problem &p, const FfnArgs &a, hipStream_t 
 hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
     if (p.dtype == MOE_BF16) return launch_bf16<false>(p, a, s);
     return launch_typed<float, false>(p, a, s);
+}
+
+hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s) {
+    if (p.dtype == MOE_BF16) return launch_fused(p, a, ctl, s);
+    hipError_t e = launch_typed<float, true>(p, a, s);
+    if (e == hipSuccess) e = launch_typed<float, false>(p, a, s);
+    return e;
 }
 
 }  // namespace moe

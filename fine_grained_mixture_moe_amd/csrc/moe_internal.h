@@ -35,8 +35,18 @@ struct WsLayout {
     size_t perm_base;      // int32  [N', perm_blocks]   first slot of each (expert, block)
     size_t act_shared;     // dtype  [T, K_s*w]          SwiGLU activations, shared experts
     size_t act_routed;     // dtype  [T*K', w]           SwiGLU activations, grouped order
+    size_t ffn_ctl;        // int32  [ffn_ctl_ints]      fused expert FFN: queue heads, error flag, per-run counters
     size_t total;
 };
+
+// Control words of the fused expert FFN launch: 8 queue heads, an error
+// flag, and one counter per token run; a group of c rows has ceil(c/128)
+// runs at most, so sum_g ceil(c_g/128) <= T K'/128 + N' (+ T/128 shared).
+inline int ffn_ctl_ints(const moe_problem &p) {
+    const int64_t runs = (p.n_shared > 0 ? cdiv(p.T, 128) : 0) +
+                         (p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / 128 + p.n_routed : 0);
+    return (int)(8 + 1 + runs);
+}
 
 // Routing workgroups for T tokens (route.hip).
 int route_blocks(int T);
@@ -55,6 +65,7 @@ inline WsLayout ws_layout(const moe_problem &p) {
     L.perm_base = take(pb * nr * sizeof(int32_t));
     L.act_shared = take((size_t)p.T * p.n_shared * p.inter * es);
     L.act_routed = take((size_t)p.T * p.top_k * p.inter * es);
+    L.ffn_ctl = take((size_t)ffn_ctl_ints(p) * sizeof(int32_t));
     L.total = off;
     return L;
 }
@@ -87,6 +98,9 @@ struct FfnArgs {
 // up: act = SiLU(X W1^T) * (X W3^T) into the workspace; down: y = act W2^T.
 hipError_t launch_expert_up(const moe_problem &p, const FfnArgs &a, hipStream_t s);
 hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_t s);
+// both projections: bf16 as one fused persistent launch (ctl: the workspace's
+// control words), fp32 as the two launches above
+hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s);
 // backward: the up projection recomputed, with a = SiLU(p) q written to act_*
 // and dp, dq formed from da in the epilogue (bf16 only)
 hipError_t launch_expert_up_backward(const moe_problem &p, const FfnArgs &a, const void *da_shared,
