@@ -40,6 +40,7 @@
 // order, then over the 4 waves in order.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "moe_internal.h"
 
@@ -233,6 +234,20 @@ __device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int
     }
 }
 
+// acc += x * e with x taken from lane ST of the lane's 16-lane row (DPP
+// row_newbcast): the wave-uniform token value reaches every lane without a
+// readlane; one fused multiply-add, the same rounding as fmaf.
+template <int ST>
+__device__ __forceinline__ void fmac_row_bcast(float &acc, float x, float e) {
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(x), "v"(e), "i"(ST));
+}
+template <typename F, int... S>
+__device__ __forceinline__ void for_each_step(F &&f, std::integer_sequence<int, S...>) {
+    (f(std::integral_constant<int, S>{}), ...);
+}
+
 // W waves of RT tokens; NJ experts per lane.  Centroid chunks of KC k for
 // the padded NE = 64*NJ experts (64 B per thread: 32 KB with 8 waves) are
 // double-buffered in LDS; each thread fills two 32-byte pieces (8 k of one
@@ -300,17 +315,21 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     }
     // ---- token pieces: piece p = i*PPT + q is bytes [16q, 16q+16) of token
     //      t0+i within the chunk; lane l holds pieces l + 64u ----
-    const uint8_t *xsrc[XPL];
-    int xoff[XPL];
+    //      (fp32 tokens).  bf16 tokens: every 16-lane row holds the chunk's
+    //      pieces of all RT tokens, lane 16r+q piece q (one step of 8 k), so
+    //      step q of the chunk broadcasts lane q of each row ----
+    constexpr int XR = XB ? RT : XPL;   // 16-byte pieces per lane and chunk
+    const uint8_t *xsrc[XR];
+    int xoff[XR];
 #pragma unroll
-    for (int u = 0; u < XPL; ++u) {
-        const int pc = lane + 64 * u;
+    for (int u = 0; u < XR; ++u) {
+        const int pc = XB ? u * PPT + min(lane & 15, PPT - 1) : lane + 64 * u;
         const int i = min(pc / PPT, RT - 1);
         xsrc[u] = (const uint8_t *)x + (size_t)max(min(t0 + i, T - 1), 0) * d * ES;
         xoff[u] = (pc % PPT) * 16;
     }
 #define MOE_XLOAD(c, xr)                                                                  \
-    _Pragma("unroll") for (int u = 0; u < XPL; ++u)                                       \
+    _Pragma("unroll") for (int u = 0; u < XR; ++u)                                        \
         xr[u] = *(const uint4 *)(xsrc[u] + min((c) * KC * ES + xoff[u], d * ES - 16));
 
     float acc[RT][NJ];
@@ -322,7 +341,53 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     // NS steps of chunk stage stg with token words xc: per step, the wave's
     // centroid values from LDS, the RT tokens' words to SGPRs, then for each
     // k of the step the fmas of all RT*NJ chains (independent neighbours)
-    auto compute = [&](auto ns_t, int stg, const uint4 (&xc)[XPL]) {
+    auto compute_bcast = [&](auto ns_t, int stg, const uint4 (&xc)[XR]) {
+        constexpr int NS = decltype(ns_t)::value;
+        const uint8_t *eb = s_e[stg] + lane * 32;
+        float x8[RT][8];   // the lane's piece of each token, as fp32
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            const uint32_t wv[4] = {xc[i].x, xc[i].y, xc[i].z, xc[i].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                x8[i][2 * h] = __uint_as_float(wv[h] << 16);
+                x8[i][2 * h + 1] = __uint_as_float(wv[h] & 0xffff0000u);
+            }
+        }
+        float4 ev[2][NJ][2];
+        auto eread = [&](int st, float4 (&e)[NJ][2]) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                e[j][0] = *(const float4 *)(eb + st * SS + j * 64 * 32);
+                e[j][1] = *(const float4 *)(eb + st * SS + j * 64 * 32 + 16);
+            }
+        };
+        eread(0, ev[0]);
+        for_each_step(
+            [&](auto st_t) {
+                constexpr int ST = decltype(st_t)::value;
+                if (ST + 1 < NS) eread(ST + 1, ev[(ST + 1) & 1]);
+                float e8[NJ][8];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const float4 a = ev[ST & 1][j][0], b = ev[ST & 1][j][1];
+                    e8[j][0] = a.x; e8[j][1] = a.y; e8[j][2] = a.z; e8[j][3] = a.w;
+                    e8[j][4] = b.x; e8[j][5] = b.y; e8[j][6] = b.z; e8[j][7] = b.w;
+                }
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                    for (int i = 0; i < RT; ++i)
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j) fmac_row_bcast<ST>(acc[i][j], x8[i][kk], e8[j][kk]);
+                __builtin_amdgcn_sched_barrier(0);
+            },
+            std::make_integer_sequence<int, NS>{});
+    };
+    auto compute = [&](auto ns_t, int stg, const uint4 (&xc)[XR]) {
+        if constexpr (XB) {
+            compute_bcast(ns_t, stg, xc);
+        } else {
         constexpr int NS = decltype(ns_t)::value;
         const uint8_t *eb = s_e[stg] + lane * 32;
         float4 ev[2][NJ][2];   // step st in ev[st & 1]; step st+1 is read while st computes
@@ -368,6 +433,7 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
             // step's readlanes and run out of SGPRs
             __builtin_amdgcn_sched_barrier(0);
         }
+        }
     };
 
     // Full chunks in the loop: the loads of chunk c+1 (global -> registers)
@@ -376,7 +442,7 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     // so only KC = 128 can leave a last chunk of 64 k; the last iteration
     // loads it (or re-loads the last full chunk into the idle stage).
     const int nchunk = (d + KC - 1) / KC, nfull = d / KC;
-    uint4 xc[XPL], xn[XPL];
+    uint4 xc[XR], xn[XR];
     MOE_FILL_LOAD(0)
     MOE_XLOAD(0, xc)
     MOE_FILL_STORE(0)
@@ -390,7 +456,7 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
         compute(std::integral_constant<int, SL>{}, c & 1, xc);
         MOE_FILL_STORE((c + 1) & 1)
 #pragma unroll
-        for (int u = 0; u < XPL; ++u) xc[u] = xn[u];
+        for (int u = 0; u < XR; ++u) xc[u] = xn[u];
         __syncthreads();
     }
     if (nfull < nchunk) compute(std::integral_constant<int, (SL / 2 > 0 ? SL / 2 : 1)>{}, nfull & 1, xc);
