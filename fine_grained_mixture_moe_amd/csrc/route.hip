@@ -237,11 +237,25 @@ __device__ __forceinline__ void finish_tokens(int t0, int nt, int Nr, int K, int
 // acc += x * e with x taken from lane ST of the lane's 16-lane row (DPP
 // row_newbcast): the wave-uniform token value reaches every lane without a
 // readlane; one fused multiply-add, the same rounding as fmaf.
-template <int ST>
+//
+// A DPP instruction must not read a VGPR that a VALU instruction wrote in the
+// two wait states before it, and the compiler's hazard check does not see
+// into inline asm.  The operands are covered by construction: the centroid
+// values come straight from LDS loads (no VALU writer), the token values are
+// unpacked once per chunk and fenced off by two wait states (compute_bcast),
+// and an accumulator was last written by its chain's previous fma, C - 1
+// fmas back for C interleaved chains, so the asm adds NOPS = max(0, 3 - C)
+// wait states.  tests/test_route_dpp_hazards.py checks the generated code.
+template <int ST, int NOPS>
 __device__ __forceinline__ void fmac_row_bcast(float &acc, float x, float e) {
-    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                 : "+v"(acc)
-                 : "v"(x), "v"(e), "i"(ST));
+    if constexpr (NOPS == 0)
+        asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                     : "+v"(acc)
+                     : "v"(x), "v"(e), "i"(ST));
+    else
+        asm volatile("s_nop %4\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                     : "+v"(acc)
+                     : "v"(x), "v"(e), "i"(ST), "i"(NOPS - 1));
 }
 template <typename F, int... S>
 __device__ __forceinline__ void for_each_step(F &&f, std::integer_sequence<int, S...>) {
@@ -315,15 +329,19 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     }
     // ---- token pieces: piece p = i*PPT + q is bytes [16q, 16q+16) of token
     //      t0+i within the chunk; lane l holds pieces l + 64u ----
-    //      (fp32 tokens).  bf16 tokens: every 16-lane row holds the chunk's
-    //      pieces of all RT tokens, lane 16r+q piece q (one step of 8 k), so
-    //      step q of the chunk broadcasts lane q of each row ----
-    constexpr int XR = XB ? RT : XPL;   // 16-byte pieces per lane and chunk
+    //      (readlane form).  Broadcast form (bf16 tokens, RT >= 2): every
+    //      16-lane row holds the chunk's pieces of all RT tokens, lane 16r+q
+    //      piece q (one step of 8 k), so step q of the chunk broadcasts lane
+    //      q of each row.  With a single token per wave the chain's DPP wait
+    //      states are not hidden, and the readlane form is faster (decode
+    //      batches: c5a 28.6 vs 29.4 us, c5c 76.7 vs 81.7 us) ----
+    constexpr bool BC = XB && RT >= 2;
+    constexpr int XR = BC ? RT : XPL;   // 16-byte pieces per lane and chunk
     const uint8_t *xsrc[XR];
     int xoff[XR];
 #pragma unroll
     for (int u = 0; u < XR; ++u) {
-        const int pc = XB ? u * PPT + min(lane & 15, PPT - 1) : lane + 64 * u;
+        const int pc = BC ? u * PPT + min(lane & 15, PPT - 1) : lane + 64 * u;
         const int i = min(pc / PPT, RT - 1);
         xsrc[u] = (const uint8_t *)x + (size_t)max(min(t0 + i, T - 1), 0) * d * ES;
         xoff[u] = (pc % PPT) * 16;
@@ -354,6 +372,11 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
                 x8[i][2 * h + 1] = __uint_as_float(wv[h] & 0xffff0000u);
             }
         }
+        // the unpacked token values are read through DPP: two wait states
+        // after their last VALU write, with no instruction moved across
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 1");
+        __builtin_amdgcn_sched_barrier(0);
         float4 ev[2][NJ][2];
         auto eread = [&](int st, float4 (&e)[NJ][2]) {
 #pragma unroll
@@ -379,13 +402,14 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
 #pragma unroll
                     for (int i = 0; i < RT; ++i)
 #pragma unroll
-                        for (int j = 0; j < NJ; ++j) fmac_row_bcast<ST>(acc[i][j], x8[i][kk], e8[j][kk]);
+                        for (int j = 0; j < NJ; ++j)
+                            fmac_row_bcast<ST, (RT * NJ >= 3 ? 0 : 3 - RT * NJ)>(acc[i][j], x8[i][kk], e8[j][kk]);
                 __builtin_amdgcn_sched_barrier(0);
             },
             std::make_integer_sequence<int, NS>{});
     };
     auto compute = [&](auto ns_t, int stg, const uint4 (&xc)[XR]) {
-        if constexpr (XB) {
+        if constexpr (BC) {
             compute_bcast(ns_t, stg, xc);
         } else {
         constexpr int NS = decltype(ns_t)::value;
@@ -522,11 +546,11 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(
 // Waves per workgroup and tokens per wave, from a sweep of (2, 4, 8) x
 // (1, 2, 4) on MI355X: 8 waves from 2048 tokens (one centroid chunk read
 // serves 8 waves), 4 below (more CUs stream the centroids for small
-// batches); 2 tokens per wave from 4096 tokens and 4 from 16384 (each
+// batches); 2 tokens per wave from 4096 tokens and 4 from 8192 (each
 // centroid value read from LDS feeds more chains, while the chip keeps about
 // two waves per SIMD).
 int route_waves(int T) { return T >= 2048 ? 8 : 4; }
-int route_tokens_per_wave(int T) { return T >= 16384 ? 4 : T >= 4096 ? 2 : 1; }
+int route_tokens_per_wave(int T) { return T >= 8192 ? 4 : T >= 4096 ? 2 : 1; }
 
 template <int RT, int W, bool XB>
 void launch_rtw(const moe_problem &p, int skip, int nblk, const void *x, const float *E, const float *bias,

@@ -44,7 +44,12 @@ SMALL = [
     (700, 128, 3, 2, 2, 192, "bf16", 7, None, 2),
     (130, 64, 0, 1, 1, 64, "f32", 8, None, 1),
     (2500, 192, 1, 40, 5, 128, "bf16", 15, 1.1, 4),    # routing: 8 waves, 128-k chunks + a 64-k last chunk
-    (8300, 128, 0, 70, 4, 64, "f32", 16, None, 7),     # routing: 2 tokens per wave, 2 expert lanes, ragged T
+    (6100, 128, 0, 70, 4, 64, "f32", 16, None, 7),     # routing: 2 tokens per wave, 2 expert lanes, ragged T
+    (8200, 256, 0, 64, 6, 64, "bf16", 22, 1.1, 4),    # routing: 4 tokens per wave from 8192 tokens, ragged T
+    (300, 128, 0, 100, 4, 64, "bf16", 23, None, 4),   # routing, bf16 readlane form: 1 token x 2 expert lanes
+    (600, 256, 0, 64, 4, 64, "bf16", 24, None, 4),    # routing, bf16 readlane form: 1 token x 1 expert lane
+    (4500, 128, 0, 128, 8, 64, "bf16", 25, 1.1, 4),   # routing, bf16 DPP form: 2 tokens x 2 expert lanes
+    (4100, 128, 0, 64, 8, 64, "bf16", 26, None, 4),   # routing, bf16 DPP form: 2 tokens x 1 lane (2 chains), ragged
     (16500, 64, 0, 130, 3, 64, "bf16", 17, None, 5),   # routing: 4 tokens per wave, 3 of 4 expert lanes
     (5000, 64, 0, 256, 16, 64, "bf16", 18, 1.1, 8),    # routing: N'=256, K'=16, skewed
     (9000, 2048, 1, 64, 6, 64, "bf16", 19, 1.1, 4),    # routing: large d, 16 chunks
