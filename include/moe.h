@@ -41,11 +41,13 @@
  *    undefined).
  *  - Expert weights, per expert, "out x in": W1 and W3 are [w, d], W2 is
  *    [d, w].  Shared experts are stacked [K_s, ...], routed [N', ...].
- *  - The workspace `ws` (size from moe_workspace_size) holds the per-block
- *    partial routing statistics, the grouping scratch and the SwiGLU
- *    activations.
- *    The calls use disjoint parts of it, so one workspace serves a whole
- *    layer pass on one stream.
+ *  - The workspace `ws` (size from moe_workspace_size, 256-byte aligned)
+ *    holds the per-block partial routing statistics, the grouping scratch,
+ *    the SwiGLU activations and the control words of the fused expert FFN
+ *    launch (cleared by moe_expert_ffn itself before each use; no
+ *    initialisation is needed).  The calls use disjoint parts of it, so one
+ *    workspace serves a whole layer pass on one stream; calls that overlap
+ *    in time (other streams) need workspaces of their own.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -180,6 +182,12 @@ int moe_permute(const moe_problem *p, const int32_t *idx, int32_t *offsets,
  * rows.  Accumulation is fp32; the SwiGLU activation is rounded to dtype
  * before the down projection.  Routed pointers may be NULL when N' == 0 and
  * shared pointers when K_s == 0.
+ *
+ * In bf16 both projections run as one persistent launch (one workgroup per
+ * CU) whose down-projection tiles wait, on counters in the workspace, for
+ * the up-projection tiles of their token rows; a small kernel clears those
+ * counters first.  The results are the same as moe_expert_up followed by
+ * moe_expert_down.  fp32 runs the two projections as two launches.
  */
 int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets,
                    const int32_t *sorted_token, const void *w1_routed,

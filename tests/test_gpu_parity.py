@@ -137,3 +137,30 @@ def test_two_runs_are_bitwise_identical():
     for k in ("idx", "gate", "probs", "counts", "prob_sum", "offsets", "sorted_token", "slot_of", "y_routed",
               "y_shared", "h", "f", "P", "f_dev", "P_dev", "exp_bal", "dev_bal"):
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("case", [
+    (4096, 256, 0, 64, 8, 256, 31),    # 256-row token tiles, many groups
+    (700, 384, 2, 16, 4, 128, 32),     # shared experts, 128-row token tiles, ragged
+    (64, 512, 1, 64, 6, 128, 33),      # decode-sized: most experts hold a few rows
+])
+def test_fused_ffn_equals_two_launches(case):
+    """moe_expert_ffn (one fused launch in bf16) and moe_expert_up + moe_expert_down (two
+    launches) run the same tile code: their outputs agree bit for bit."""
+    T, d, Ks, Nr, K, w, seed = case
+    inp = W.make_random_case(T, d, Ks, Nr, K, w, dtype="bf16", seed=seed, zipf_s=1.1, groups=1)
+    PT.say(f"[case] fused vs two launches T={T} d={d} Ks={Ks} Nr={Nr} K={K} w={w}")
+    dl = DeviceLayer(inp)
+    dl.route()
+    dl.permute()
+    dl.expert_ffn()
+    a = dl.results()
+    dl.y_routed.zero_()
+    if dl.y_shared is not None:
+        dl.y_shared.zero_()
+    dl.expert_up()
+    dl.expert_down()
+    b = dl.results()
+    assert np.array_equal(a["y_routed"], b["y_routed"])
+    if Ks:
+        assert np.array_equal(a["y_shared"], b["y_shared"])
