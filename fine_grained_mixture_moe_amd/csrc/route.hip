@@ -19,15 +19,21 @@
 //   * the centroids are staged in LDS in chunks of 32 KB (KC values of k for
 //     all experts), double-buffered, and every wave of the workgroup reads
 //     them from there: one L2 read of E per workgroup instead of one per
-//     wave.  A chunk is stored as slices of 8 k, [slice][expert][8], so a
-//     step of a wave's 64 experts is one contiguous 2 KB span; E itself is
-//     read in its natural [N'][d] layout;
-//   * the token values are the same in every lane, so they feed the fma as
-//     its scalar operand: each wave loads its RT token rows of a chunk with
-//     ordinary vector loads (one 16-byte piece per lane, a chunk ahead) and
-//     each step moves the packed values it needs to SGPRs with v_readlane.
-//     Scalar loads would save that op but return out of order, and they
-//     share their wait counter with the LDS reads.
+//     wave.  A chunk is stored as slices of 8 k, each as two halves of 4 k,
+//     [slice][half][expert][4]: a lane's 16-byte read of one half sits next
+//     to its neighbours', so the 64 lanes read one contiguous 1 KB span (a
+//     32-byte stride per lane would use half of each bank cycle); E itself
+//     is read in its natural [N'][d] layout;
+//   * the token values are the same in every lane.  Each wave loads its RT
+//     token rows of a chunk with ordinary vector loads (one 16-byte piece
+//     per lane, a chunk ahead); three forms then feed them to the fmas:
+//     several tokens per wave (bf16): a DPP row broadcast inside the fma;
+//     one token and one expert per lane: the chunk as fp32 in LDS, read by
+//     all lanes at one address, so the single chain per lane issues its
+//     fmas back to back on VGPR operands; otherwise: v_readlane to SGPRs
+//     and the fma's scalar operand.  Scalar loads would save the readlane
+//     but return out of order, and they share their wait counter with the
+//     LDS reads.
 // Selection, per token, with the wave holding every logit (bias added) of it:
 //   * softmax over the routed experts: maximum and sum by DPP row reductions
 //     (fixed order, so deterministic), fp32 exp;
@@ -266,8 +272,8 @@ __device__ __forceinline__ void for_each_step(F &&f, std::integer_sequence<int, 
 // the padded NE = 64*NJ experts (64 B per thread: 32 KB with 8 waves) are
 // double-buffered in LDS; each thread fills two 32-byte pieces (8 k of one
 // expert), the KC/8 threads of an expert row reading its KC values
-// contiguously.  Slices are NE*32+16 bytes apart, so those writes land on
-// distinct banks.
+// contiguously.  The pad after each slice puts those writes on distinct
+// banks.
 template <int RT, int NJ, int W, bool XB>
 __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int K, int skip, const void *x,
                                                         const float *E,
@@ -280,7 +286,9 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     constexpr int KC = 16 * NT / NE;         // k per chunk (two 32-byte fill pieces per thread)
     constexpr int SL = KC / 8;               // steps of 8 k per chunk
     static_assert(KC >= 8 && KC <= 128 && KC % 8 == 0, "chunk of whole steps");
-    constexpr int SS = NE * 32 + 16;         // slice pitch (bytes)
+    // slice pitch (bytes): the two halves of the slice, then a pad that puts
+    // the fill writes of each 8 lanes (rows r, slices s) on distinct banks
+    constexpr int SS = NE * 32 + 128 / (SL < 8 ? SL : 8);
     constexpr int FR = NE * SL / NT;         // 32-byte fill pieces per thread
     constexpr int ES = XB ? 2 : 4;           // token element bytes
     constexpr int PPT = KC * ES / 16;        // 16-byte token pieces per token and chunk
@@ -289,6 +297,11 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     static_assert(NE * SL % NT == 0, "whole fill rounds");
     static_assert(W * NE * (8 + 4) <= 2 * SL * SS, "statistics fit in the chunk stages");
     __shared__ __attribute__((aligned(16))) uint8_t s_e[2][SL * SS];
+    // LDS form (one token, one expert per lane): the chunk's token values as fp32, per
+    // stage and wave, read by all lanes at one address (a broadcast), so the
+    // fmas take VGPR operands and the chain has no SGPR round trip
+    constexpr bool LB = RT == 1 && NJ == 1;
+    __shared__ __attribute__((aligned(16))) float s_xf[LB ? 2 * W * KC : 4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     float4 fe0a, fe0b, fe1a, fe1b;
     const float *fs0 = fsrc[0] + 8 * fsl[0], *fs1 = fsrc[1] + 8 * fsl[1];
     const int flim0 = d - 8 - 8 * fsl[0], flim1 = d - 8 - 8 * fsl[1];
-    uint8_t *fd0 = &s_e[0][0] + fsl[0] * SS + frow[0] * 32, *fd1 = &s_e[0][0] + fsl[1] * SS + frow[1] * 32;
+    uint8_t *fd0 = &s_e[0][0] + fsl[0] * SS + frow[0] * 16, *fd1 = &s_e[0][0] + fsl[1] * SS + frow[1] * 16;
 #define MOE_FILL_LOAD(c)                                              \
     {                                                                 \
         const float *a_ = fs0 + min((c) * KC, flim0);                 \
@@ -323,9 +336,9 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     {                                                                 \
         const int o_ = (stg) * (SL * SS);                             \
         *(float4 *)(fd0 + o_) = fe0a;                                 \
-        *(float4 *)(fd0 + o_ + 16) = fe0b;                            \
+        *(float4 *)(fd0 + o_ + NE * 16) = fe0b;                       \
         *(float4 *)(fd1 + o_) = fe1a;                                 \
-        *(float4 *)(fd1 + o_ + 16) = fe1b;                            \
+        *(float4 *)(fd1 + o_ + NE * 16) = fe1b;                       \
     }
     // ---- token pieces: piece p = i*PPT + q is bytes [16q, 16q+16) of token
     //      t0+i within the chunk; lane l holds pieces l + 64u ----
@@ -346,6 +359,27 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
         xsrc[u] = (const uint8_t *)x + (size_t)max(min(t0 + i, T - 1), 0) * d * ES;
         xoff[u] = (pc % PPT) * 16;
     }
+    // LDS form: lane l < PPT converts its 16-byte piece of the token (k
+    // [l*16/ES, (l+1)*16/ES) of the chunk) to fp32 and stores it
+#define MOE_XSTORE(stg, xr)                                                               \
+    if constexpr (LB) {                                                                   \
+        if (lane < PPT) {                                                                 \
+            float *xd_ = s_xf + ((stg) * W + wave) * KC + lane * (16 / ES);               \
+            const uint4 v_ = xr[0];                                                       \
+            if constexpr (XB) {                                                           \
+                *(float4 *)xd_ = make_float4(__uint_as_float(v_.x << 16),                 \
+                                             __uint_as_float(v_.x & 0xffff0000u),         \
+                                             __uint_as_float(v_.y << 16),                 \
+                                             __uint_as_float(v_.y & 0xffff0000u));        \
+                *(float4 *)(xd_ + 4) = make_float4(__uint_as_float(v_.z << 16),           \
+                                                   __uint_as_float(v_.z & 0xffff0000u),   \
+                                                   __uint_as_float(v_.w << 16),           \
+                                                   __uint_as_float(v_.w & 0xffff0000u));  \
+            } else {                                                                      \
+                *(uint4 *)xd_ = v_;                                                       \
+            }                                                                             \
+        }                                                                                 \
+    }
 #define MOE_XLOAD(c, xr)                                                                  \
     _Pragma("unroll") for (int u = 0; u < XR; ++u)                                        \
         xr[u] = *(const uint4 *)(xsrc[u] + min((c) * KC * ES + xoff[u], d * ES - 16));
@@ -361,7 +395,7 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     // k of the step the fmas of all RT*NJ chains (independent neighbours)
     auto compute_bcast = [&](auto ns_t, int stg, const uint4 (&xc)[XR]) {
         constexpr int NS = decltype(ns_t)::value;
-        const uint8_t *eb = s_e[stg] + lane * 32;
+        const uint8_t *eb = s_e[stg] + lane * 16;
         float x8[RT][8];   // the lane's piece of each token, as fp32
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
@@ -381,8 +415,8 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
         auto eread = [&](int st, float4 (&e)[NJ][2]) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                e[j][0] = *(const float4 *)(eb + st * SS + j * 64 * 32);
-                e[j][1] = *(const float4 *)(eb + st * SS + j * 64 * 32 + 16);
+                e[j][0] = *(const float4 *)(eb + st * SS + j * 64 * 16);
+                e[j][1] = *(const float4 *)(eb + st * SS + j * 64 * 16 + NE * 16);
             }
         };
         eread(0, ev[0]);
@@ -411,15 +445,55 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     auto compute = [&](auto ns_t, int stg, const uint4 (&xc)[XR]) {
         if constexpr (BC) {
             compute_bcast(ns_t, stg, xc);
+        } else if constexpr (LB) {
+            constexpr int NS = decltype(ns_t)::value;
+            const uint8_t *eb = s_e[stg] + lane * 16;
+            const float *xb = s_xf + (stg * W + wave) * KC;
+            float4 ev[3][NJ][2], xv[3][2];   // step st in [st % 3]; steps st+1, st+2 are in flight
+            auto rd = [&](int st, float4 (&e)[NJ][2], float4 (&xx)[2]) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    e[j][0] = *(const float4 *)(eb + st * SS + j * 64 * 16);
+                    e[j][1] = *(const float4 *)(eb + st * SS + j * 64 * 16 + NE * 16);
+                }
+                xx[0] = *(const float4 *)(xb + 8 * st);
+                xx[1] = *(const float4 *)(xb + 8 * st + 4);
+            };
+            rd(0, ev[0], xv[0]);
+            if (NS > 1) rd(1, ev[1], xv[1]);
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                if (st + 2 < NS) rd(st + 2, ev[(st + 2) % 3], xv[(st + 2) % 3]);
+                const float4 xa = xv[st % 3][0], xb4 = xv[st % 3][1];
+                const float x8[8] = {xa.x, xa.y, xa.z, xa.w, xb4.x, xb4.y, xb4.z, xb4.w};
+                float e8[NJ][8];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const float4 a = ev[st % 3][j][0], b = ev[st % 3][j][1];
+                    e8[j][0] = a.x; e8[j][1] = a.y; e8[j][2] = a.z; e8[j][3] = a.w;
+                    e8[j][4] = b.x; e8[j][5] = b.y; e8[j][6] = b.z; e8[j][7] = b.w;
+                }
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) acc[0][j] = __builtin_fmaf(x8[kk], e8[j][kk], acc[0][j]);
+                // one step at a time (bounded registers; the reads above run
+                // ahead): the empty asm takes the accumulators and clobbers
+                // memory, so neither this step's fmas nor later steps' LDS
+                // reads move across it
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[0][j]) : : "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
         } else {
         constexpr int NS = decltype(ns_t)::value;
-        const uint8_t *eb = s_e[stg] + lane * 32;
+        const uint8_t *eb = s_e[stg] + lane * 16;
         float4 ev[2][NJ][2];   // step st in ev[st & 1]; step st+1 is read while st computes
         auto eread = [&](int st, float4 (&e)[NJ][2]) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                e[j][0] = *(const float4 *)(eb + st * SS + j * 64 * 32);
-                e[j][1] = *(const float4 *)(eb + st * SS + j * 64 * 32 + 16);
+                e[j][0] = *(const float4 *)(eb + st * SS + j * 64 * 16);
+                e[j][1] = *(const float4 *)(eb + st * SS + j * 64 * 16 + NE * 16);
             }
         };
         eread(0, ev[0]);
@@ -470,6 +544,7 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     MOE_FILL_LOAD(0)
     MOE_XLOAD(0, xc)
     MOE_FILL_STORE(0)
+    MOE_XSTORE(0, xc)
     __syncthreads();
     for (int c = 0; c < nfull; ++c) {
         const int cn = min(c + 1, nchunk - 1);
@@ -479,6 +554,7 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
         __builtin_amdgcn_sched_barrier(0);
         compute(std::integral_constant<int, SL>{}, c & 1, xc);
         MOE_FILL_STORE((c + 1) & 1)
+        MOE_XSTORE((c + 1) & 1, xn)
 #pragma unroll
         for (int u = 0; u < XR; ++u) xc[u] = xn[u];
         __syncthreads();
@@ -487,6 +563,7 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
 #undef MOE_FILL_LOAD
 #undef MOE_FILL_STORE
 #undef MOE_XLOAD
+#undef MOE_XSTORE
 
     double ps[NJ];
     int cnt[NJ];
