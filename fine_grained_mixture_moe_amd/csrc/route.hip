@@ -323,23 +323,25 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     const float *fs0 = fsrc[0] + 8 * fsl[0], *fs1 = fsrc[1] + 8 * fsl[1];
     const int flim0 = d - 8 - 8 * fsl[0], flim1 = d - 8 - 8 * fsl[1];
     uint8_t *fd0 = &s_e[0][0] + fsl[0] * SS + frow[0] * 16, *fd1 = &s_e[0][0] + fsl[1] * SS + frow[1] * 16;
-#define MOE_FILL_LOAD(c)                                              \
+#define MOE_FILL_LOAD_TO(c, A0, B0, A1, B1)                           \
     {                                                                 \
         const float *a_ = fs0 + min((c) * KC, flim0);                 \
         const float *b_ = fs1 + min((c) * KC, flim1);                 \
-        fe0a = *(const float4 *)a_;                                   \
-        fe0b = *(const float4 *)(a_ + 4);                             \
-        fe1a = *(const float4 *)b_;                                   \
-        fe1b = *(const float4 *)(b_ + 4);                             \
+        A0 = *(const float4 *)a_;                                     \
+        B0 = *(const float4 *)(a_ + 4);                               \
+        A1 = *(const float4 *)b_;                                     \
+        B1 = *(const float4 *)(b_ + 4);                               \
     }
-#define MOE_FILL_STORE(stg)                                           \
+#define MOE_FILL_STORE_FROM(stg, A0, B0, A1, B1)                      \
     {                                                                 \
         const int o_ = (stg) * (SL * SS);                             \
-        *(float4 *)(fd0 + o_) = fe0a;                                 \
-        *(float4 *)(fd0 + o_ + NE * 16) = fe0b;                       \
-        *(float4 *)(fd1 + o_) = fe1a;                                 \
-        *(float4 *)(fd1 + o_ + NE * 16) = fe1b;                       \
+        *(float4 *)(fd0 + o_) = A0;                                   \
+        *(float4 *)(fd0 + o_ + NE * 16) = B0;                         \
+        *(float4 *)(fd1 + o_) = A1;                                   \
+        *(float4 *)(fd1 + o_ + NE * 16) = B1;                         \
     }
+#define MOE_FILL_LOAD(c) MOE_FILL_LOAD_TO(c, fe0a, fe0b, fe1a, fe1b)
+#define MOE_FILL_STORE(stg) MOE_FILL_STORE_FROM(stg, fe0a, fe0b, fe1a, fe1b)
     // ---- token pieces: piece p = i*PPT + q is bytes [16q, 16q+16) of token
     //      t0+i within the chunk; lane l holds pieces l + 64u ----
     //      (readlane form).  Broadcast form (bf16 tokens, RT >= 2): every
@@ -540,6 +542,60 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     // so only KC = 128 can leave a last chunk of 64 k; the last iteration
     // loads it (or re-loads the last full chunk into the idle stage).
     const int nchunk = (d + KC - 1) / KC, nfull = d / KC;
+    // One token per wave in 4-wave blocks (small batches): a chunk's compute
+    // is short, and in a layer step the centroids and tokens come from HBM
+    // (the expert weights streamed through the caches since the last
+    // routing), so with the next chunk's loads issued one chunk ahead every
+    // chunk waits out a memory latency.  Four register sets keep three
+    // chunks in flight: at chunk c the set c%4 holds c's token piece, the
+    // others chunks c+1..c+3; after c is computed, c+1 goes to the other
+    // stage and set c%4 is reloaded with chunk c+4.  Here KC <= 64 divides d
+    // (d % 64 == 0), so every chunk is full; loads past the end repeat the
+    // last chunk.  No branch in the loop skips a load and the loop has one
+    // exit (with loads issued on some paths only, or a loop left from inside
+    // the group, the wait counts before the LDS stores fall back to waiting
+    // for loads issued a step earlier); steps past the last chunk skip only
+    // their compute.  (Named registers through macros: as structs passed to
+    // lambdas the sets were kept in scratch memory.)
+    if constexpr (RT == 1 && W == 4) {
+        static_assert(64 % KC == 0, "whole chunks");
+        static_assert(XR == 1, "one token piece per lane and chunk");
+#define MOE_SET(n) float4 n##a0, n##b0, n##a1, n##b1; uint4 n##x;
+#define MOE_LD(c, n)                                                                     \
+    {                                                                                    \
+        const int cc_ = min((c), nchunk - 1);                                            \
+        MOE_FILL_LOAD_TO(cc_, n##a0, n##b0, n##a1, n##b1)                                \
+        n##x = *(const uint4 *)(xsrc[0] + min(cc_ * KC * ES + xoff[0], d * ES - 16));    \
+    }
+#define MOE_STEP(c, cur, nxt)                                                            \
+    {                                                                                    \
+        if ((c) < nchunk) {                                                              \
+            const uint4 xa_[1] = {cur##x};                                               \
+            compute(std::integral_constant<int, SL>{}, (c) & 1, xa_);                   \
+        }                                                                                \
+        MOE_FILL_STORE_FROM(((c) + 1) & 1, nxt##a0, nxt##b0, nxt##a1, nxt##b1)          \
+        MOE_XSTORE(((c) + 1) & 1, (&nxt##x))                                             \
+        MOE_LD((c) + 4, cur)                                                             \
+        __syncthreads();                                                                 \
+    }
+        MOE_SET(q0) MOE_SET(q1) MOE_SET(q2) MOE_SET(q3)
+        MOE_LD(0, q0)
+        MOE_LD(1, q1)
+        MOE_LD(2, q2)
+        MOE_LD(3, q3)
+        MOE_FILL_STORE_FROM(0, q0a0, q0b0, q0a1, q0b1)
+        MOE_XSTORE(0, (&q0x))
+        __syncthreads();
+        for (int c = 0; c < nchunk; c += 4) {
+            MOE_STEP(c, q0, q1)
+            MOE_STEP(c + 1, q1, q2)
+            MOE_STEP(c + 2, q2, q3)
+            MOE_STEP(c + 3, q3, q0)
+        }
+#undef MOE_SET
+#undef MOE_LD
+#undef MOE_STEP
+    } else {
     uint4 xc[XR], xn[XR];
     MOE_FILL_LOAD(0)
     MOE_XLOAD(0, xc)
@@ -560,8 +616,11 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
         __syncthreads();
     }
     if (nfull < nchunk) compute(std::integral_constant<int, (SL / 2 > 0 ? SL / 2 : 1)>{}, nfull & 1, xc);
+    }
 #undef MOE_FILL_LOAD
 #undef MOE_FILL_STORE
+#undef MOE_FILL_LOAD_TO
+#undef MOE_FILL_STORE_FROM
 #undef MOE_XLOAD
 #undef MOE_XSTORE
 

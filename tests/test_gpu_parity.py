@@ -55,6 +55,8 @@ SMALL = [
     (9000, 2048, 1, 64, 6, 64, "bf16", 19, 1.1, 4),    # routing: large d, 16 chunks
     (16400, 192, 0, 32, 4, 64, "f32", 20, None, 4),    # routing: fp32 tokens, 2 pieces per lane, last chunk
     (16400, 64, 0, 48, 2, 64, "f32", 21, None, 4),     # routing: d below one chunk (no full chunk)
+    (1000, 448, 0, 64, 6, 64, "bf16", 27, None, 4),    # routing, 4-set load ring: 7 chunks (a partial group)
+    (900, 320, 0, 128, 8, 64, "f32", 28, None, 4),     # routing, 4-set load ring, readlane form: 10 chunks
 ]
 
 
