@@ -43,6 +43,19 @@ namespace {
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer loads for the bf16 GEMM staging.  The range is the whole 2 GB
+// window: a chunk outside its tile's M/N bounds or past K carries the offset
+// kOob, which the hardware answers with zeros (no branch, no null pointer).
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bg_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ uint4 bg_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
     __bf16 b = (__bf16)f;
@@ -321,7 +334,107 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
 
     // ---- staging: chunk c of a tile -> (row, column) in the tile ----
     uint4 ra[RA], rb[RB];
+    // bf16 products: every chunk's byte offset is fixed per tile and a step
+    // adds a uniform scalar offset (mode 3's B rows follow the gathered
+    // tokens, loaded one step ahead); no address arithmetic, division or
+    // branch per chunk in the k loop.  Column offsets within a chunk never
+    // cross a segment or a [dp | dq] boundary: w % 64 == 0 and chunks are 8
+    // elements.  dq follows dp in the same workspace, so one window with dq
+    // at a positive byte offset covers both.
+    constexpr bool BUF = BF && MODE <= 3;
+    __amdgpu_buffer_rsrc_t rsA = bg_rsrc(A.x), rsB = rsA, rsB2 = rsA;
+    uint32_t va[RA], vb[RB], sA = 0, sB = 0, dA = 0;
+    int klA[RA], klB[RB], tkB[RB];
+    if constexpr (BUF) {
+        const size_t w = A.w, d = A.d, wg = Gr.wg, ro = Gr.roff;
+        const DT *dy = (const DT *)(Gr.sh ? A.dh : A.dy_r);
+        const DT *dp = (const DT *)(Gr.sh ? A.dp_s : A.dp_r), *dq = (const DT *)(Gr.sh ? A.dq_s : A.dq_r);
+        const uint32_t dq_off = (uint32_t)((const char *)dq - (const char *)dp);
+#pragma unroll
+        for (int i = 0; i < RA; ++i) {
+            const int c = tid + 256 * i;
+            int m, kofs;
+            if (AT) { kofs = c / (128 / EC); m = m0 + (c % (128 / EC)) * EC; }
+            else { m = m0 + c / (32 / EC); kofs = (c % (32 / EC)) * EC; }
+            size_t e = 0;
+            if (MODE == 0) e = (ro + m) * d + kofs;
+            if (MODE == 1) e = (ro + m) * wg + kofs;
+            if (MODE == 2) e = (size_t)kofs * d + m;
+            if (MODE == 3) e = (ro + kofs) * wg + (m < (int)wg ? m : m - (int)wg);
+            uint32_t off = (uint32_t)(e * ES);
+            if (MODE == 3 && m >= (int)wg) off += dq_off;
+            va[i] = m < M ? off : kOob;
+            klA[i] = K - kofs;   // the chunk is live while k0 < klA
+        }
+        if (MODE == 0) { rsA = bg_rsrc(dy); sA = 32 * ES; }
+        if (MODE == 1) { rsA = bg_rsrc(dp); dA = dq_off; }
+        if (MODE == 2) { rsA = bg_rsrc(dy + ro * d); sA = (uint32_t)(32 * d * ES); }
+        if (MODE == 3) { rsA = bg_rsrc(dp); sA = (uint32_t)(32 * wg * ES); }
+
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int c = tid + 256 * i;
+            const int kofs = c / (128 / EC), n = n0 + (c % (128 / EC)) * EC;   // B is transposed in modes 0-3
+            size_t e = 0;
+            if (MODE == 0) e = ((size_t)(n / A.w) * d + kofs) * w + n % A.w;
+            if (MODE == 1) e = (size_t)kofs * d + n;
+            if (MODE == 2) e = (size_t)kofs * wg + n;
+            if (MODE == 3) e = (size_t)n;
+            vb[i] = n < N ? (uint32_t)(e * ES) : kOob;
+            klB[i] = K - kofs;
+            tkB[i] = 0;
+        }
+        if (MODE == 0) {
+            rsB = bg_rsrc(Gr.sh ? (const DT *)A.w2_s : (const DT *)A.w2_r + (size_t)Gr.r * d * w);
+            sB = (uint32_t)(32 * w * ES);
+        }
+        if (MODE == 1) {
+            rsB = bg_rsrc(Gr.sh ? (const DT *)A.w1_s : (const DT *)A.w1_r + (size_t)Gr.r * w * d);
+            rsB2 = bg_rsrc(Gr.sh ? (const DT *)A.w3_s : (const DT *)A.w3_r + (size_t)Gr.r * w * d);
+            sB = (uint32_t)(d * ES);   // per k row
+        }
+        if (MODE == 2) { rsB = bg_rsrc((const DT *)(Gr.sh ? A.a_s : A.a_r) + ro * wg); sB = (uint32_t)(32 * wg * ES); }
+        if (MODE == 3) rsB = bg_rsrc(A.x);
+    }
+    // mode 3: token of k row k0 + kofs of chunk i (clamped into the group)
+    auto tok_of = [&](int i, int k0) -> int {
+        const int c = tid + 256 * i, k = min(k0 + c / (128 / EC), max(K - 1, 0));
+        return Gr.sh ? k : A.sorted_token[Gr.roff + k];
+    };
+    auto load_buf = [&](int k0) {
+        // A
+        uint32_t so = 0;
+        if (MODE == 1) so = k0 < Gr.wg ? (uint32_t)(k0 * ES) : dA + (uint32_t)((k0 - Gr.wg) * ES);
+        else so = (uint32_t)(k0 / 32) * sA;
+#pragma unroll
+        for (int i = 0; i < RA; ++i) {
+            const uint32_t v = (MODE >= 2 && k0 >= klA[i]) ? kOob : va[i];
+            ra[i] = bg_load(rsA, v, so);
+        }
+        // B
+        if (MODE == 3) {
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const uint32_t v = (k0 >= klB[i] || vb[i] == kOob) ? kOob : (uint32_t)(tkB[i] * A.d * ES) + vb[i];
+                rb[i] = bg_load(rsB, v, 0);
+            }
+            // tokens of the next step's rows, a step ahead of their use
+#pragma unroll
+            for (int i = 0; i < RB; ++i) tkB[i] = tok_of(i, k0 + 32);
+        } else {
+            const bool w3 = MODE == 1 && k0 >= Gr.wg;
+            const uint32_t sob = MODE == 1 ? (uint32_t)(w3 ? k0 - Gr.wg : k0) * sB : (uint32_t)(k0 / 32) * sB;
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const uint32_t v = (MODE >= 2 && k0 >= klB[i]) ? kOob : vb[i];
+                rb[i] = bg_load(w3 ? rsB2 : rsB, v, sob);
+            }
+        }
+    };
     auto load_tiles = [&](int k0) {
+      if constexpr (BUF) {
+        load_buf(k0);
+      } else {
 #pragma unroll
         for (int i = 0; i < RA; ++i) {
             const int c = tid + 256 * i;
@@ -338,6 +451,7 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
             else { const int nr = c / (32 / EC), kc = c % (32 / EC); p = b_ptr<MODE, DT>(A, Gr, n0 + nr, k0 + kc * EC, N, K); }
             rb[i] = ld16(p);
         }
+      }
     };
     auto store_tiles = [&](int stg) {
         uint8_t *s_a = s_a2[stg], *s_b = s_b2[stg];
@@ -422,6 +536,10 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
     // compute of the current one.  (Two stages with one barrier per step
     // measured slower: the extra registers cost a wave per SIMD.)
     const int nk = cdiv(K, 32);
+    if (MODE == 3 && BUF && nk > 0) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) tkB[i] = tok_of(i, 0);
+    }
     if (nk > 0) {
         load_tiles(0);
         store_tiles(0);
