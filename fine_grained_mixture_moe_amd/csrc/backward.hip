@@ -325,10 +325,21 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
         const int mid = (lo + hi) >> 1;
         if (s_pref[mid] <= bid) lo = mid; else hi = mid;
     }
+    // XCD-aware order within the group: workgroup b runs on XCD b % 8, so
+    // the group's j-th workgroup takes the tile at position j % 8 * per +
+    // j / 8 (with the ragged classes shortened): each XCD works through a
+    // contiguous eighth of every group (m fastest), so tiles that share an
+    // operand share its L2, and every XCD gets the same share of each
+    // group whatever the groups' tile costs (hot experts, shared experts).
+    int lt;
+    {
+        const int j = bid - s_pref[lo], ng = s_pref[lo + 1] - s_pref[lo];
+        const int per = (ng + 7) / 8, tall = ng % 8 == 0 ? 8 : ng % 8, x = j % 8, l = j / 8;
+        lt = x < tall ? x * per + l : tall * per + (x - tall) * (per - 1) + l;
+    }
     const Group Gr = group_of(A, lo);
     int M, N, K;
     dims<MODE>(A, Gr, M, N, K);
-    const int lt = bid - s_pref[lo];
     const int mt = cdiv(M, 128);
     const int m0 = (lt % mt) * 128, n0 = (lt / mt) * 128;
 
