@@ -15,6 +15,8 @@
 //                                    that chose it; a pair's rank inside the expert is
 //                                    popcount of the masks of earlier waves plus its
 //                                    lanes below -> stable.
+// A single block (T <= 256, decode batches) counts its own pairs and scans
+// them itself: one launch instead of two.
 // When the histogram is large (blocks x experts above kFusedScanMax) every
 // scatter block re-reading it would cost more than one more launch, so a
 // separate scan kernel <<<1, 1024>>> computes offsets and the per-(expert,
@@ -122,9 +124,13 @@ __device__ int block_exscan_experts(int *tot, int Nr, int *s_w) {
     return all;
 }
 
-// FUSED: derive offsets and this block's first slots from hist (see above);
-// else read the first slots from base (written by perm_scan_kernel).
-template <bool FUSED>
+// HM (where the counts come from): kFromHist derives offsets and this
+// block's first slots from hist (see above); kFromBase reads the first slots
+// from base (written by perm_scan_kernel); kSelf, for a single block (up to
+// 256 tokens, decode batches), counts its own pairs, so no histogram launch
+// precedes it.
+enum { kFromBase = 0, kFromHist = 1, kSelf = 2 };
+template <int HM>
 __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int Nr, int K,
                                                            const int32_t *__restrict__ idx,
                                                            const int32_t *__restrict__ hist,
@@ -138,7 +144,26 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int Nr, int K,
     __shared__ int s_w[4];
     const int nblk = gridDim.x, b = blockIdx.x;
     for (int i = threadIdx.x; i < 4 * Nr; i += 256) mask[i / Nr][i % Nr] = 0ull;
-    if (FUSED) {
+    if (HM == kSelf) {
+        for (int r = threadIdx.x; r < Nr; r += 256) s_tot[r] = 0;
+        __syncthreads();
+        const int n = min(kPermuteTokens, T) * K;
+        for (int e = threadIdx.x; e < n; e += kUnroll * 256) {
+            int v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? idx[e + u * 256] : -1;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                if ((unsigned)v[u] < (unsigned)Nr) atomicAdd(&s_tot[v[u]], 1);
+        }
+        __syncthreads();
+        const int all = block_exscan_experts(s_tot, Nr, s_w);
+        for (int r = threadIdx.x; r < Nr; r += 256) {
+            s_first[r] = s_tot[r];
+            offsets[r] = s_tot[r];
+        }
+        if (threadIdx.x == 0) offsets[Nr] = all;
+    } else if (HM == kFromHist) {
         for (int r = threadIdx.x; r < Nr; r += 256) { s_tot[r] = 0; s_first[r] = 0; }
         __syncthreads();
         // expert totals and this block's preceding counts: every (expert,
@@ -224,14 +249,19 @@ hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *off
         perm_empty_kernel<<<1, 256, 0, s>>>(p.n_routed, offsets);
         return hipGetLastError();
     }
+    if (nblk == 1) {
+        perm_scatter_kernel<kSelf><<<1, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, nullptr, nullptr, offsets,
+                                                     sorted_token, slot_of);
+        return hipGetLastError();
+    }
     perm_hist_kernel<<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist);
     if ((int64_t)nblk * p.n_routed <= kFusedScanMax) {
-        perm_scatter_kernel<true><<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist, nullptr, offsets,
-                                                       sorted_token, slot_of);
+        perm_scatter_kernel<kFromHist><<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist, nullptr, offsets,
+                                                            sorted_token, slot_of);
     } else {
         perm_scan_kernel<<<1, 1024, 0, s>>>(nblk, p.n_routed, hist, base, offsets);
-        perm_scatter_kernel<false><<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist, base, offsets,
-                                                        sorted_token, slot_of);
+        perm_scatter_kernel<kFromBase><<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist, base, offsets,
+                                                            sorted_token, slot_of);
     }
     return hipGetLastError();
 }
