@@ -1,0 +1,82 @@
+"""The routing kernel's load ring, checked in the generated gfx950 code.
+
+With one token per wave in 4-wave blocks, the route kernel keeps three
+centroid/token chunks in flight in four register sets.  That only works while
+the compiler's wait counts before the LDS stores stay partial: a branch around
+a load, or a loop left from inside the unrolled group, made it fall back to
+waiting for every load (vmcnt(0)) at each chunk, which costs a full memory
+latency per chunk.  This test compiles route.hip for gfx950 and checks, in
+every 1-token 4-wave route_kernel instantiation, the loop that stores the
+chunks to LDS: every vmcnt wait in its body must leave at least one register
+set (five loads) in flight.  No GPU needed.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "fine_grained_mixture_moe_amd", "csrc")
+RING = re.compile(r"^(_Z\S*route_kernelILi1ELi\d+ELi4ELb[01]E\S*):$")
+
+
+def ring_loops(asm: str):
+    """(kernel, [vmcnt values]) of each backward-branch loop that stores to LDS."""
+    out = []
+    lines = [l.split(";")[0].strip() for l in asm.split("\n")]
+    fn, labels, start = None, {}, 0
+    for k, line in enumerate(lines):
+        m = RING.match(line)
+        if m:
+            fn, labels, start = m.group(1), {}, k
+            continue
+        if re.match(r"^_Z\S*:$", line):
+            fn = None
+            continue
+        if fn is None:
+            continue
+        lm = re.match(r"^(\.LBB\S+):$", line)
+        if lm:
+            labels[lm.group(1)] = k
+            continue
+        bm = re.search(r"s_(?:cbranch_\w+|branch)\s+(\.LBB\S+)", line)
+        if bm and bm.group(1) in labels and labels[bm.group(1)] < k:
+            body = lines[labels[bm.group(1)]:k + 1]
+            if any(b.startswith("ds_write_b128") for b in body) and any(b.startswith("s_barrier") for b in body):
+                waits = [int(w) for b in body for w in re.findall(r"vmcnt\((\d+)\)", b)]
+                out.append((fn, waits))
+    return out
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
+def test_ring_loop_keeps_loads_in_flight(tmp_path):
+    out = tmp_path / "route.s"
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, "route.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    loops = ring_loops(out.read_text())
+    kernels = {fn for fn, _ in loops}
+    assert len(kernels) >= 6, f"expected the 1-token 4-wave instantiations, found {sorted(kernels)}"
+    bad = [(fn, w) for fn, w in loops if not w or min(w) < 5]
+    assert not bad, "\n".join(f"{fn}: vmcnt waits {w}" for fn, w in bad)
+
+
+def test_checker_flags_a_full_wait():
+    """The checker itself: a vmcnt(0) in an LDS-storing loop is reported, partial waits are not."""
+    asm = """_ZN3moe12_GLOBAL__N_112route_kernelILi1ELi1ELi4ELb1EEEviiiiiPKvPKfS5_PiPfS7_S6_Pd:
+.LBB0_1:
+\tglobal_load_dwordx4 v[2:5], v[6:7], off
+\ts_waitcnt vmcnt({n})
+\tds_write_b128 v8, v[10:13]
+\ts_barrier
+\ts_cbranch_scc1 .LBB0_1
+\ts_endpgm
+"""
+    (fn, waits), = ring_loops(asm.format(n=0))
+    assert waits == [0]
+    (fn, waits), = ring_loops(asm.format(n=15))
+    assert min(waits) >= 5
