@@ -28,6 +28,15 @@ int check_problem(const moe_problem *p) {
     if ((int64_t)p->T * p->top_k > INT32_MAX || (int64_t)p->n_shared * p->inter > INT32_MAX / 64 ||
         (int64_t)p->T * p->top_k * p->inter > (int64_t)1 << 40)
         return MOE_ERR_UNSUPPORTED;
+    // The GEMMs address whole operands through buffer resources with 32-bit
+    // offsets: x [T, d], y_routed / dy_routed [T*K', d], the routed and the
+    // shared activations (the backward's dp and dq side by side: twice that),
+    // and a shared expert stack [K_s, d, w] must each stay below 2^31 bytes.
+    const int64_t es = dtype_bytes(p->dtype), lim = (int64_t)1 << 31, tk = (int64_t)p->T * p->top_k;
+    if ((int64_t)p->T * p->d * es >= lim || tk * p->d * es >= lim || 2 * tk * p->inter * es + 256 >= lim ||
+        2 * (int64_t)p->T * p->n_shared * p->inter * es + 256 >= lim ||
+        (int64_t)p->n_shared * p->d * p->inter * es >= lim)
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 

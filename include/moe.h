@@ -34,7 +34,12 @@
  *    indices and counts are int32.
  *  - Shapes: d % 64 == 0, w % 64 == 0, T >= 0, K_s >= 0, N' >= 0;
  *    N' == 0 (a dense, shared-only layer) requires K' == 0, otherwise
- *    1 <= K' <= N'.  T*K' and T*K_s*w must fit in int32.
+ *    1 <= K' <= N'.  T*K' and T*K_s*w must fit in int32.  Each of these
+ *    stays below 2^31 bytes (the GEMMs address them with 32-bit offsets):
+ *    x [T, d], y_routed [T*K', d], twice the routed activations [T*K', w]
+ *    and twice the shared ones [T, K_s*w] (the backward keeps dp and dq side
+ *    by side), and the shared expert stack [K_s, d, w].  Every call returns
+ *    MOE_ERR_UNSUPPORTED outside this envelope.
  *  - Routing inputs must be finite.  Expert indices handed to moe_permute
  *    must lie in [0, N') and be distinct within a token; entries that are
  *    not are skipped (memory stays safe, results for that token are

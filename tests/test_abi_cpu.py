@@ -51,6 +51,10 @@ def test_workspace_size_and_shape_validation():
         M.moe_problem.make(16, 128, 0, 0, 1, 64, "f32"),    # N' = 0 needs K' = 0
         M.moe_problem.make(-1, 128, 0, 8, 2, 64, "f32"),    # T < 0
         M.moe_problem.make(16, 128, 0, 8, 2, 64, 7),        # dtype
+        M.moe_problem.make(1 << 19, 2048, 0, 8, 1, 64, "bf16"),       # x: T*d*2 = 2^31 bytes
+        M.moe_problem.make(1 << 16, 4096, 0, 8, 4, 64, "bf16"),       # y_routed: T*K'*d*2 = 2^31 bytes
+        M.moe_problem.make(1 << 16, 64, 0, 8, 8, 1024, "bf16"),       # dp and dq: 2*T*K'*w*2 = 2^31 bytes
+        M.moe_problem.make(1 << 16, 64, 2, 8, 1, 4096, "f32"),        # shared dp and dq: 2*T*K_s*w*4 > 2^31 bytes
     ]
     for q in bad:
         with pytest.raises(M.MoEError):
