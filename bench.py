@@ -116,6 +116,14 @@ def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
             "tflops": wl.flops() * n / wl.T / dt / 1e12}
 
 
+def device_info() -> dict:
+    """The GPU the line was measured on (the peaks above are MI355X's published ones)."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "cus": pr.multi_processor_count,
+            "hbm_gib": round(pr.total_memory / (1 << 30), 1)}
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -234,6 +242,7 @@ def run(args) -> dict:
         "layer_hbm_gbs": round(layer_bytes(wl, counts) / (ms * 1e-3) / 1e9, 1),
         "stage_ms": breakdown,
         "roofline": roof,
+        "device": device_info(),
     }
     if coarse is not None and name == "c2b" and not args.no_pair and not args.zero_weights:
         dc = DeviceLayer(coarse, device="cuda:0")
