@@ -135,6 +135,14 @@ def test_backward_c2b_sampled():
     run_backward(inp, tokens=tokens, weight_experts=[0, 17, 63], full_router=False, tag="c2b")
 
 
+def test_backward_skewed_shared_sampled():
+    """Zipf(1.1)-skewed routing with two shared experts at T = 4096: many tiles per group, groups
+    of very different sizes, shared dx-row tiles with twice the routed k extent."""
+    inp = W.make_random_case(4096, 512, 2, 32, 4, 256, dtype="bf16", seed=21, zipf_s=1.1, groups=4, w_std=0.05)
+    tokens = W.sample_tokens(inp.wl.T, 48)
+    run_backward(inp, tokens=tokens, weight_experts=[0, 1, 2, 33], full_router=False, tag="skewed")
+
+
 def test_backward_is_deterministic():
     inp = W.make_random_case(600, 128, 1, 32, 4, 128, dtype="bf16", seed=11)
     PT.say("[bwd] determinism")
