@@ -291,12 +291,13 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
     __shared__ __attribute__((aligned(16))) uint8_t s_a2[1][SA];
     __shared__ __attribute__((aligned(16))) uint8_t s_b2[1][SB];
     __shared__ int s_pref[BG_MAXG + 1];
+    __shared__ int s_maxg;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int G = (A.Ks > 0 ? 1 : 0) + A.Nr;
     if (wave == 0) {
-        int carry = 0;
+        int carry = 0, mx = 0;
         if (lane == 0) s_pref[0] = 0;
         for (int g0 = 0; g0 < G; g0 += 64) {
             const int g = g0 + lane;
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
                 dims<MODE>(A, Gr, M, N, K);
                 tiles = cdiv(M, 128) * cdiv(N, 128);
             }
+            mx = max(mx, tiles);
             int incl = tiles;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -316,26 +318,46 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
             if (g < G) s_pref[g + 1] = carry + incl;
             carry += __shfl(incl, 63, 64);
         }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+        if (lane == 0) s_maxg = mx;
     }
     __syncthreads();
     const int bid = blockIdx.x;
-    if (bid >= s_pref[G]) return;
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] <= bid) lo = mid; else hi = mid;
-    }
-    // XCD-aware order within the group: workgroup b runs on XCD b % 8, so
-    // the group's j-th workgroup takes the tile at position j % 8 * per +
-    // j / 8 (with the ragged classes shortened): each XCD works through a
-    // contiguous eighth of every group (m fastest), so tiles that share an
-    // operand share its L2, and every XCD gets the same share of each
-    // group whatever the groups' tile costs (hot experts, shared experts).
-    int lt;
-    {
-        const int j = bid - s_pref[lo], ng = s_pref[lo + 1] - s_pref[lo];
-        const int per = (ng + 7) / 8, tall = ng % 8 == 0 ? 8 : ng % 8, x = j % 8, l = j / 8;
-        lt = x < tall ? x * per + l : tall * per + (x - tall) * (per - 1) + l;
+    const int NT = s_pref[G];
+    if (bid >= NT) return;
+    // XCD-aware order.  Workgroup b runs on XCD b % 8; spread(j, n) gives the
+    // j-th of n workgroups the position j % 8 * per + j / 8 (ragged classes
+    // shortened), so each XCD works through a contiguous eighth of the range
+    // and tiles that share an operand share its L2.  The range is the whole
+    // tile list (whole groups on one XCD: each operand read into one L2) when
+    // every tile costs the same and no group holds more than an eighth of the
+    // tiles: da (k = d), and the dx rows with at most one shared expert
+    // (k = 2 K_s w vs 2 w).  Otherwise each group is spread over all XCDs, so
+    // every XCD gets the same share of it whatever it costs (hot experts
+    // under skewed routing, several shared experts, the weight gradients'
+    // k = the group's rows).
+    auto spread = [](int j, int n) {
+        const int per = (n + 7) / 8, tall = n % 8 == 0 ? 8 : n % 8, x = j % 8, l = j / 8;
+        return x < tall ? x * per + l : tall * per + (x - tall) * (per - 1) + l;
+    };
+    auto group_at = [&](int v) {
+        int lo = 0, hi = G;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pref[mid] <= v) lo = mid; else hi = mid;
+        }
+        return lo;
+    };
+    const bool whole = (MODE == 0 || (MODE == 1 && A.Ks <= 1)) && s_maxg * 8 <= NT;
+    int lo, lt;
+    if (whole) {
+        const int v = spread(bid, NT);
+        lo = group_at(v);
+        lt = v - s_pref[lo];
+    } else {
+        lo = group_at(bid);
+        lt = spread(bid - s_pref[lo], s_pref[lo + 1] - s_pref[lo]);
     }
     const Group Gr = group_of(A, lo);
     int M, N, K;
