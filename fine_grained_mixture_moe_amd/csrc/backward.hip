@@ -21,7 +21,12 @@
 //      2  dW2  = dy^T . a             (A and B transposed; k runs over the group's rows)
 //      3  dW13 = [dp|dq]^T . x        (A and B transposed; x rows gathered)
 //      4  p, q = x . [W1;W3]^T, then the SwiGLU backward in the epilogue:
-//         reads da, writes dp, dq and a (A and B k-contiguous)
+//         reads da, writes dp, dq and a (A and B k-contiguous); fp32 layers
+//         only: bf16 layers recompute p, q on the forward up kernel with its
+//         backward epilogue (expert_ffn.hip)
+//      bf16 operands come in through raw buffer loads whose offsets are fixed
+//      per tile (a chunk out of range reads zeros), and the tile order is
+//      XCD-aware (see the kernel)
 //   gather_dx_kernel     dx_ffn[t] = dxs[t] + sum_k dxr[slot_of[t,k]] (k order)
 //   router_dz_kernel     ds, dz per token (wave per token, lane = expert)
 //   router_dx_kernel     dx = dh + dx_ffn + dz E (LDS-tiled, 64 tokens x 64 columns)
