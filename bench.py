@@ -213,10 +213,12 @@ def run(args) -> dict:
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     tr = load_traffic("ffn", name)
     roof["traffic"] = None if tr is None else tr["bytes_per_launch"]
-    avg_rows = wl.T * wl.top_k / wl.n_routed if wl.n_routed else wl.T
+    avg_rows = wl.T * wl.top_k // wl.n_routed if wl.n_routed else wl.T
     # the events bracket the whole moe_expert_ffn call: for bf16 the fused launch
-    # plus the 1-block kernel that clears its control words before it
-    roof["kernel"] = (f"grouped_ffn_fused_kernel<{256 if avg_rows >= 256 else 128}> (up + down)" if wl.dtype == "bf16"
+    # plus the 1-block kernel that clears its control words before it; the template
+    # arguments are the token-tile rows and the weight loads' cache policy (2: nt)
+    form = "256, 0" if avg_rows >= 256 else ("128, 2" if avg_rows <= 64 else "128, 0")
+    roof["kernel"] = (f"grouped_ffn_fused_kernel<{form}> (up + down)" if wl.dtype == "bf16"
                       else "grouped_ffn_kernel<f32, up> + grouped_ffn_kernel<f32, down>")
     roof["kernel_ms"] = round(ffn_ms, 4)
     roof["algorithmic"] = {"flops": ffn["flops"], "bytes": ffn["bytes"], "pairs": ffn["pairs"],

@@ -334,7 +334,9 @@ struct TileDesc {
     int r, row_off, m0, nr, n_tile;
 };
 
-template <int BM, bool UP, bool BWD, bool FUSED>
+// WAUX: cache policy of the weight loads (0, or kNonTemporal when every expert's weights are
+// read by a single token tile).
+template <int BM, bool UP, bool BWD, bool FUSED, int WAUX = 0>
 __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDesc td, uint8_t (&s_w)[2][256 * 128],
                                               uint8_t (&s_x)[2][BM * 128], int (&s_src)[BM],
                                               int *head = nullptr, int *next = nullptr) {
@@ -407,19 +409,13 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
         }
         return (uint32_t)kt * RB;
     };
-    // part ph (0..3) of a k step: weight chunks [ph*CW/4, (ph+1)*CW/4), token chunks likewise.
-    // 128-row token tiles (decode batches) read each expert's weights once: those loads carry
-    // the non-temporal hint (nt), so the streamed weights do not displace the token rows and
-    // activations that are read again (c5a expert FFN 207.5 -> 193.2 us, c5c 548 -> 510 us).
-    // 256-row tiles (prefill batches) read an expert's weights again for each of its token
-    // tiles, so there the default policy keeps them in L2.
-    constexpr int kWeightAux = BM == 128 ? kNonTemporal : 0;
+    // part ph (0..3) of a k step: weight chunks [ph*CW/4, (ph+1)*CW/4), token chunks likewise
     auto gload_part = [&](int kt, int ph, bool wts = true, bool toks = true) {
         const uint32_t kw = kw_of(kt), kx = (uint32_t)kt * RB;
         if (wts) {
 #pragma unroll
             for (int i = 0; i < CW; ++i)
-                if (i * 4 / CW == ph) sw[i] = bload<kWeightAux>((UP && i >= CW / 2) ? rw_b : rw_a, ow[i], kw);
+                if (i * 4 / CW == ph) sw[i] = bload<WAUX>((UP && i >= CW / 2) ? rw_b : rw_a, ow[i], kw);
         }
         if (toks) {
 #pragma unroll
@@ -829,7 +825,7 @@ struct FusedCtl {
     int *done;   // [runs] finished up tiles of each token run
 };
 
-template <int BM>
+template <int BM, int WAUX>
 __global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, GemmParams Pd, FusedCtl C) {
     __shared__ __attribute__((aligned(16))) uint8_t s_w[2][256 * 128];
     __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * 128];
@@ -937,12 +933,12 @@ __global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, G
             }
             int next = 0;
             if (up) {
-                ffn_tile_bf16<BM, true, false, true>(Pu, td, s_w, s_x, s_src, &C.head[q], &next);
+                ffn_tile_bf16<BM, true, false, true, WAUX>(Pu, td, s_w, s_x, s_src, &C.head[q], &next);
                 __builtin_amdgcn_s_waitcnt(0);   // this thread's activation stores are complete
                 __syncthreads();
                 if (tid == 0) __hip_atomic_fetch_add(&C.done[run], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else {
-                ffn_tile_bf16<BM, false, false, true>(Pd, td, s_w, s_x, s_src, &C.head[q], &next);
+                ffn_tile_bf16<BM, false, false, true, WAUX>(Pd, td, s_w, s_x, s_src, &C.head[q], &next);
             }
             if (tid == 0) s_ticket = next;
             __syncthreads();
@@ -1022,8 +1018,14 @@ hipError_t launch_fused(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hi
     const GemmParams Pu = make_params(p, a, true), Pd = make_params(p, a, false);
     const FusedCtl C{ctl, ctl + kQueues, ctl + kQueues + 1};
     const int64_t avg = p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / p.n_routed : (int64_t)p.T;
-    if (avg >= 256) grouped_ffn_fused_kernel<256><<<ncu, 512, 0, s>>>(Pu, Pd, C);
-    else grouped_ffn_fused_kernel<128><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+    // Decode batches (at most 64 rows per expert on average) read each expert's weights with a
+    // single token tile: there the weight loads are non-temporal, so the streamed weights leave L2
+    // to the token rows and activations that are read again (c5a expert FFN 207.5 -> 193.2 us,
+    // c5c 548 -> 510 us). With more rows an expert's second tile re-reads its weights from L2, and
+    // the hint costs 4-13% (192 rows per expert on average: 491 -> 555 us).
+    if (avg >= 256) grouped_ffn_fused_kernel<256, 0><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+    else if (avg <= 64) grouped_ffn_fused_kernel<128, kNonTemporal><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+    else grouped_ffn_fused_kernel<128, 0><<<ncu, 512, 0, s>>>(Pu, Pd, C);
     return hipGetLastError();
 }
 
