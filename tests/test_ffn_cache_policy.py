@@ -1,0 +1,62 @@
+"""Cache policy of the expert-FFN weight loads, checked in the generated gfx950 code.
+
+Only the fused kernel for decode-sized batches (128-row token tiles, weight
+policy 2) streams the expert weights with non-temporal (nt) buffer loads.
+Every other instantiation re-reads an expert's weights for each of its token
+tiles from L2 and must keep the default policy.  No GPU needed.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "fine_grained_mixture_moe_amd", "csrc")
+
+
+def nt_loads_per_kernel(asm: str):
+    """{kernel symbol: (nt dwordx4 buffer loads, all dwordx4 buffer loads)}"""
+    out, fn = {}, None
+    for line in asm.split("\n"):
+        m = re.match(r"^\s*\.type\s+(\S+),@function", line)
+        if m:
+            fn = m.group(1)
+            out.setdefault(fn, [0, 0])
+            continue
+        code = line.split(";")[0]
+        if fn and re.match(r"^\s*buffer_load_dwordx4\b", code):
+            out[fn][1] += 1
+            if re.search(r"\bnt\b", code):
+                out[fn][0] += 1
+    return {k: tuple(v) for k, v in out.items()}
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
+def test_only_decode_fused_kernel_streams_weights(tmp_path):
+    out = tmp_path / "expert_ffn.s"
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, "expert_ffn.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    counts = nt_loads_per_kernel(out.read_text())
+    fused = {k: v for k, v in counts.items() if "grouped_ffn_fused_kernel" in k}
+    decode = [k for k in fused if "ILi128ELi2E" in k]
+    assert len(decode) == 1 and len(fused) == 3, sorted(fused)
+    nt, total = counts[decode[0]]
+    assert total > 0 and nt > 0, (nt, total)
+    for k, (nt, total) in counts.items():
+        if k not in decode:
+            assert nt == 0, f"{k}: {nt} nt loads"
+
+
+def test_counter_reads_policy_bits():
+    asm = """\t.type\t_Zk1,@function
+\tbuffer_load_dwordx4 v[0:3], v4, s[0:3], 0 offen nt
+\tbuffer_load_dwordx4 v[0:3], v4, s[0:3], 0 offen
+\t.type\t_Zk2,@function
+\tbuffer_load_dwordx4 v[0:3], v4, s[0:3], 0 offen sc1
+"""
+    assert nt_loads_per_kernel(asm) == {"_Zk1": (1, 2), "_Zk2": (0, 1)}
