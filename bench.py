@@ -5,15 +5,22 @@ already resident in HBM: moe_route -> moe_permute -> moe_expert_ffn (bf16: the
 up and down projections in one fused launch) -> moe_combine ->
 moe_balance_stats.  Prints ONE JSON line.
 
-Default workload: the fine-grained half of the granularity-equivalence pair
-(T=4096, d=1280, 64 routed experts of width 512, top-8, bf16); the
-coarse GShard-style half (16 experts of width 2048, top-2, same weights) is
-timed alongside for the fine/coarse ratio.  Other workloads: --config.
+Default workload: the largest single-GPU prefill layer, a 145B-style layer
+(T=8192 tokens, d=4096, 4 shared + 128 routed experts of width 1024, top-12,
+bf16).  The granularity-equivalence pair (fine-grained: 64 experts of width
+512, top-8; coarse GShard-style: 16 experts of width 2048, top-2; T=4096,
+d=1280, same weights) is timed alongside under "pair" (--no-pair skips it).
+Other workloads: --config.  --accumulate runs moe_expert_ffn in its
+accumulating mode (gate-weighted sum inside the down projection, no y_routed).
+
+Timing: W warm-up steps, then K steps between two device synchronisations
+(value, ms_per_step); then a separate loop of max(K, 50) steps (200 for
+decode batches) with an event pair around each step gives the median and the
+minimum step time.  The dominant kernel's time is the mean of event pairs
+around every moe_expert_ffn call of the K timed steps.
 
 Extra modes (used to produce the committed profile summaries):
   --copy-probe       also run a plain device copy of known size (counter calibration)
-  --zero-weights     zero every expert weight after upload (power probe: the same launches
-                     on operands that do not toggle; never a bench line of the workload)
   --backward         time the backward pass instead (moe_combine_backward ->
                      moe_expert_ffn_backward -> moe_route_backward after one forward);
                      prints its own JSON line
@@ -38,8 +45,8 @@ METRIC = "MoE-layer tokens/s + active TFLOP/s (% MFMA/HBM peak) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-KERNEL_SOURCES = ["fine_grained_mixture_moe_amd/csrc/expert_ffn.hip",
-                  "fine_grained_mixture_moe_amd/csrc/moe_internal.h"]
+# the source of the dominant kernel: a traffic record measured on other sources is not reported
+KERNEL_SOURCES = ["fine_grained_mixture_moe_amd/csrc/expert_ffn.hip"]
 COPY_BYTES = 1 << 30
 
 
@@ -60,17 +67,17 @@ def ffn_algorithmic(wl, counts) -> dict:
 
     Per (token, expert) pair: 6*d*w FLOPs (gate and up: 2 x 2*d*w, down: 2*d*w).
     Bytes: W1, W3 and W2 of every touched expert (all shared + routed experts with
-    tokens), the token rows read once, the routed outputs written once (dtype) and
-    the shared output (fp32).  The SwiGLU activations are an intermediate: their
-    round trip through HBM is implementation traffic (it shows in the measured
-    FETCH/WRITE counters), not part of the algorithmic minimum.
+    tokens), the token rows read once and the expert sum y written once (fp32).
+    The SwiGLU activations and the per-pair rows y_routed are intermediates of an
+    implementation (the gather mode writes y_routed, the accumulating mode does
+    not): their HBM traffic shows in the measured FETCH/WRITE counters, and is
+    not part of the algorithmic minimum.
     """
     es = 2 if wl.dtype == "bf16" else 4
     pairs = wl.T * (wl.top_k + wl.n_shared)
     flops = 6.0 * wl.d * wl.inter * pairs
     touched = wl.n_shared + int((counts > 0).sum())
-    byts = (3.0 * wl.inter * wl.d * es * touched + wl.T * wl.d * es
-            + wl.T * wl.top_k * wl.d * es + (wl.T * wl.d * 4 if wl.n_shared else 0))
+    byts = 3.0 * wl.inter * wl.d * es * touched + wl.T * wl.d * es + wl.T * wl.d * 4
     return dict(flops=flops, bytes=byts, pairs=pairs, touched=touched)
 
 
@@ -94,13 +101,35 @@ def load_traffic(kernel_tag: str, workload: str):
     return rec
 
 
-def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
-    """The oracle (plain C, fp64 FFN, OpenMP over tokens) on a bounded sample of the workload."""
-    from oracle import oracle as O
+def host_info() -> dict:
+    """CPU model and core counts of the host the oracle runs on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def _oracle_args(inp):
     wl = inp.wl
     sh, ro = inp.shared, inp.routed
-    args = (inp.x.f32, inp.centroids, inp.bias, wl.top_k, max(wl.groups, 1), sh(inp.w1).f32, sh(inp.w3).f32,
+    return (inp.x.f32, inp.centroids, inp.bias, wl.top_k, max(wl.groups, 1), sh(inp.w1).f32, sh(inp.w3).f32,
             sh(inp.w2).f32, ro(inp.w1).f32, ro(inp.w3).f32, ro(inp.w2).f32)
+
+
+def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
+    """The oracle (plain C, fp64 FFN, OpenMP over tokens) on a bounded sample of the workload,
+    plus the whole tiny c1 layer on one thread."""
+    from oracle import oracle as O
+    from fine_grained_mixture_moe_amd import workloads as W
+    wl = inp.wl
+    args = _oracle_args(inp)
     n0 = min(wl.T, 64)
     t0 = time.perf_counter()
     O.forward(n0, *args)
@@ -110,10 +139,27 @@ def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
     t0 = time.perf_counter()
     O.forward(n, *args)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"first {n} of {wl.T} tokens of the same workload, whole layer pass "
-                      f"(route, group, fp64 expert FFNs, combine, stats); {dt:.1f} s",
-            "tflops": wl.flops() * n / wl.T / dt / 1e12}
+    threads = O.num_threads()
+    out = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {n} of {wl.T} tokens of the same workload, whole layer pass "
+                     f"(route, group, fp64 expert FFNs, combine, stats); {dt:.1f} s on {threads} OpenMP threads",
+           "tflops": wl.flops() * n / wl.T / dt / 1e12, "threads": threads}
+    out.update(host_info())
+    # the whole tiny fp32 layer (T=512, d=256, 1+63 experts, top-7, width 128) on one thread
+    c1 = W.make_inputs(W.WORKLOADS["c1"])
+    O.set_num_threads(1)
+    try:
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.forward(c1.wl.T, *_oracle_args(c1))
+            times.append(time.perf_counter() - t0)
+    finally:
+        O.set_num_threads(threads)
+    t1 = sorted(times)[1]
+    out["c1_one_thread"] = {"tokens_per_s": round(c1.wl.T / t1, 1), "seconds": round(t1, 4),
+                            "runs": "median of 3", "threads": 1}
+    return out
 
 
 def device_info() -> dict:
@@ -142,13 +188,7 @@ def run(args) -> dict:
         inp = W.make_inputs(W.WORKLOADS[name])
     wl = inp.wl
     log(f"[bench] {name}: {wl.description} (inputs in {time.perf_counter() - t_gen:.1f}s)")
-    dl = DeviceLayer(inp, device="cuda:0")
-    if args.zero_weights:
-        for t in (dl.w1_r, dl.w3_r, dl.w2_r, dl.w1_s, dl.w3_s, dl.w2_s):
-            if t is not None:
-                t.zero_()
-        torch.cuda.synchronize()
-        log("[bench] expert weights zeroed (power probe)")
+    dl = DeviceLayer(inp, device="cuda:0", accumulate=args.accumulate)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -176,6 +216,20 @@ def run(args) -> dict:
     ffn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     ms = elapsed * 1e3 / args.steps
     counts = dl.counts.cpu().numpy()[:wl.n_routed]
+    dl.check_status()     # a stalled wait inside the fused launch would have poisoned the outputs
+
+    # per-step distribution: an event pair around every step
+    decode = wl.T * max(wl.top_k, 1) <= 64 * max(wl.n_routed, 1)
+    reps = max(args.steps, 200 if decode else 50)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in sev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in sev)
+    step_stats = {"reps": reps, "median_ms": round(per[len(per) // 2], 4), "min_ms": round(per[0], 4),
+                  "max_ms": round(per[-1], 4)}
 
     # per-stage breakdown (separate, untimed-for-value loop)
     stages = ["route", "permute", "expert_ffn", "combine", "balance_stats"]
@@ -213,14 +267,13 @@ def run(args) -> dict:
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     tr = load_traffic("ffn", name)
     roof["traffic"] = None if tr is None else tr["bytes_per_launch"]
-    avg_rows = wl.T * wl.top_k // wl.n_routed if wl.n_routed else wl.T
-    # the events bracket the whole moe_expert_ffn call: for bf16 the fused launch
-    # plus the 1-block kernel that clears its control words before it; the template
-    # arguments are the token-tile rows and the weight loads' cache policy (2: nt)
-    form = "256, 0" if avg_rows >= 256 else ("128, 2" if avg_rows <= 64 else "128, 0")
-    roof["kernel"] = (f"grouped_ffn_fused_kernel<{form}> (up + down)" if wl.dtype == "bf16"
-                      else "grouped_ffn_kernel<f32, up> + grouped_ffn_kernel<f32, down>")
+    # the kernel the launcher picks (template arguments: token-tile rows, weight-load cache
+    # policy (2: nt), accumulating down projection); the events bracket the whole
+    # moe_expert_ffn call: the fused launch plus the small preparation kernel before it
+    from fine_grained_mixture_moe_amd import moe as M
+    roof["kernel"] = M.moe_expert_ffn_kernel(dl.prob, dl.accumulate)
     roof["kernel_ms"] = round(ffn_ms, 4)
+    roof["kernel_ms_includes"] = "ffn_prep_kernel + " + roof["kernel"]
     roof["algorithmic"] = {"flops": ffn["flops"], "bytes": ffn["bytes"], "pairs": ffn["pairs"],
                            "touched_experts": ffn["touched"]}
 
@@ -237,8 +290,10 @@ def run(args) -> dict:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{name}: {wl.description}" + (" [power probe: expert weights zeroed]" if args.zero_weights else ""), "T": wl.T, "d": wl.d, "n_shared": wl.n_shared,
-                   "n_routed": wl.n_routed, "top_k": wl.top_k, "inter": wl.inter, "parallelism": "none (1 GPU)"},
+        "config": {"workload": f"{name}: {wl.description}", "T": wl.T, "d": wl.d, "n_shared": wl.n_shared,
+                   "n_routed": wl.n_routed, "top_k": wl.top_k, "inter": wl.inter, "parallelism": "none (1 GPU)",
+                   "expert_ffn_mode": "accumulating" if dl.accumulate else "gather"},
+        "step_ms": step_stats,
         "active_tflops": round(tflops, 2),
         "active_mfma_frac": round(tflops / mfma_peak, 4),
         "layer_hbm_gbs": round(layer_bytes(wl, counts) / (ms * 1e-3) / 1e9, 1),
@@ -246,21 +301,38 @@ def run(args) -> dict:
         "roofline": roof,
         "device": device_info(),
     }
-    if coarse is not None and name == "c2b" and not args.no_pair and not args.zero_weights:
-        dc = DeviceLayer(coarse, device="cuda:0")
-        for _ in range(args.warmup):
-            dc.forward()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            dc.forward()
-        torch.cuda.synchronize()
-        ms_a = (time.perf_counter() - t0) * 1e3 / args.steps
-        out["pair"] = {"c2a_gshard_ms_per_step": round(ms_a, 4), "fine_over_coarse_time": round(ms / ms_a, 3)}
-        del dc
-    if not args.no_cpu and not args.zero_weights:
+    if not args.no_pair:
+        out["pair"] = time_pair(args, ms if name == "c2b" else None)
+    if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     return out
+
+
+def time_pair(args, ms_b=None) -> dict:
+    """The granularity-equivalence pair: fine-grained (64 x 512, top-8) and coarse (16 x 2048, top-2)
+    layers on the same weights and tokens, equal active FLOPs; whole-layer step times."""
+    import torch
+    from fine_grained_mixture_moe_amd import workloads as W
+    from fine_grained_mixture_moe_amd.layer import DeviceLayer
+    coarse = W.make_c2_coarse()
+    res = {}
+    for key, inp in (("c2a", coarse), ("c2b", W.make_c2_fine(independent_centroids=True, coarse=coarse))):
+        if key == "c2b" and ms_b is not None:
+            res["c2b_ms_per_step"] = round(ms_b, 4)
+            continue
+        dl = DeviceLayer(inp, device="cuda:0", accumulate=args.accumulate)
+        for _ in range(args.warmup):
+            dl.forward()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = max(args.steps, 20)
+        for _ in range(n):
+            dl.forward()
+        torch.cuda.synchronize()
+        res[f"{key}_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / n, 4)
+        del dl
+    res["fine_over_coarse_time"] = round(res["c2b_ms_per_step"] / res["c2a_ms_per_step"], 3)
+    return res
 
 
 def run_backward(args) -> dict:
@@ -397,12 +469,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2b", help="c1 c2a c2b c3 c4 c5a c5b c5c")
+    ap.add_argument("--config", default="c5b", help="c1 c2a c2b c3 c4 c5a c5b c5c")
+    ap.add_argument("--accumulate", action="store_true",
+                    help="accumulating expert FFN (gate-weighted sum inside the down projection)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--no-pair", action="store_true", help="skip timing the coarse c2a half")
+    ap.add_argument("--no-pair", action="store_true", help="skip timing the c2a/c2b granularity pair")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--zero-weights", action="store_true", help="power probe: zero the expert weights")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (own JSON line)")
     ap.add_argument("--ingest-pmc", default=None)
     ap.add_argument("--summarize-trace", default=None, help="rocprofv3 output dir to summarize")

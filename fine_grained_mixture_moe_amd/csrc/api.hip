@@ -62,11 +62,13 @@ const char *moe_status_str(int status) {
         case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside the supported envelope";
         case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch or runtime error";
+        case MOE_ERR_STALLED:
+            return "MOE_ERR_STALLED: a wait inside the fused expert FFN launch gave up; its outputs hold NaN";
         default: return "unknown moe status";
     }
 }
 
-const char *moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+const char *moe_version(void) { return "moe-mi355x 0.2 (gfx950)"; }
 
 int moe_workspace_size(const moe_problem *p, size_t *bytes) {
     if (!bytes) return MOE_ERR_INVALID_ARG;
@@ -126,10 +128,13 @@ namespace {
 
 // Validation shared by the expert-FFN calls.  `up` / `down` select which
 // weights and outputs the call touches.
+// accum: the accumulating form of the down projection (y_routed == NULL with
+// routed pairs present; gate, slot_of and y_shared = y_acc required).
 int check_ffn(const moe_problem *p, bool up, bool down, const void *x, const int32_t *offsets,
               const int32_t *sorted_token, const void *w1_routed, const void *w3_routed, const void *w2_routed,
               const void *w1_shared, const void *w3_shared, const void *w2_shared, const void *y_routed,
-              const float *y_shared, const void *ws, size_t ws_bytes, WsLayout *L, bool *routed, bool *shared) {
+              const float *y_shared, const void *ws, size_t ws_bytes, WsLayout *L, bool *routed, bool *shared,
+              bool accum = false, const float *gate = nullptr, const int32_t *slot_of = nullptr) {
     int rc = check_problem(p);
     if (rc != MOE_OK) return rc;
     *routed = p->n_routed > 0 && (int64_t)p->T * p->top_k > 0;
@@ -137,7 +142,9 @@ int check_ffn(const moe_problem *p, bool up, bool down, const void *x, const int
     if (*routed) {
         if (!offsets) return MOE_ERR_INVALID_ARG;
         if (up && (!x || !sorted_token || !w1_routed || !w3_routed)) return MOE_ERR_INVALID_ARG;
-        if (down && (!w2_routed || !y_routed)) return MOE_ERR_INVALID_ARG;
+        if (down && !w2_routed) return MOE_ERR_INVALID_ARG;
+        if (down && !accum && !y_routed) return MOE_ERR_INVALID_ARG;
+        if (accum && (!gate || !slot_of || !y_shared || !sorted_token)) return MOE_ERR_INVALID_ARG;
         if ((w1_routed && !aligned16(w1_routed)) || (w3_routed && !aligned16(w3_routed)) ||
             (w2_routed && !aligned16(w2_routed)) || (y_routed && !aligned16(y_routed)))
             return MOE_ERR_INVALID_ARG;
@@ -149,7 +156,7 @@ int check_ffn(const moe_problem *p, bool up, bool down, const void *x, const int
             (w2_shared && !aligned16(w2_shared)) || (y_shared && !aligned16(y_shared)))
             return MOE_ERR_INVALID_ARG;
     }
-    if (x && !aligned16(x)) return MOE_ERR_INVALID_ARG;
+    if ((x && !aligned16(x)) || (y_shared && !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
     return check_ws(p, ws, ws_bytes, L);
 }
 
@@ -209,18 +216,47 @@ int moe_expert_down(const moe_problem *p, const int32_t *offsets, const void *w2
 
 int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets, const int32_t *sorted_token,
                    const void *w1_routed, const void *w3_routed, const void *w2_routed, const void *w1_shared,
-                   const void *w3_shared, const void *w2_shared, void *y_routed, float *y_shared, void *ws,
-                   size_t ws_bytes, void *stream) {
+                   const void *w3_shared, const void *w2_shared, void *y_routed, float *y_acc, const float *gate,
+                   const int32_t *slot_of, void *ws, size_t ws_bytes, void *stream) {
     WsLayout L;
     bool routed, shared;
+    const bool accum = y_routed == nullptr && p && p->n_routed > 0 && (int64_t)p->T * p->top_k > 0;
     int rc = check_ffn(p, true, true, x, offsets, sorted_token, w1_routed, w3_routed, w2_routed, w1_shared,
-                       w3_shared, w2_shared, y_routed, y_shared, ws, ws_bytes, &L, &routed, &shared);
+                       w3_shared, w2_shared, y_routed, y_acc, ws, ws_bytes, &L, &routed, &shared, accum, gate,
+                       slot_of);
     if (rc != MOE_OK) return rc;
-    if (!routed && !shared) return MOE_OK;
-    const FfnArgs a = ffn_args(x, offsets, sorted_token, w1_routed, w3_routed, w2_routed, w1_shared, w3_shared,
-                               w2_shared, y_routed, y_shared, ws, L);
+    FfnArgs a = ffn_args(x, offsets, sorted_token, w1_routed, w3_routed, w2_routed, w1_shared, w3_shared,
+                         w2_shared, y_routed, y_acc, ws, L);
+    if (accum) {
+        a.y_acc = y_acc;
+        a.gate = gate;
+        a.slot_of = slot_of;
+        a.gate_sorted = (float *)at(ws, L.gate_sorted);
+    }
+    // always launched (the preparation kernel clears the error flag of moe_expert_ffn_status)
     const moe_problem q = active_part(*p, routed, shared);
     return hip_status(launch_expert_ffn(q, a, (int32_t *)at(ws, L.ffn_ctl), (hipStream_t)stream));
+}
+
+int moe_expert_ffn_status(const moe_problem *p, const void *ws, size_t ws_bytes, void *stream) {
+    WsLayout L;
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+    int32_t err = 0;
+    if (hipMemcpy(&err, (const uint8_t *)ws + L.ffn_ctl + kFfnCtlErr * sizeof(int32_t), sizeof(err),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return MOE_ERR_HIP;
+    return err ? MOE_ERR_STALLED : MOE_OK;
+}
+
+const char *moe_expert_ffn_kernel(const moe_problem *p, int accumulate) {
+    if (check_problem(p) != MOE_OK) return nullptr;
+    const bool routed = p->n_routed > 0 && (int64_t)p->T * p->top_k > 0;
+    const bool shared = p->n_shared > 0 && p->T > 0;
+    if (!routed && !shared) return "";
+    return expert_ffn_kernel_name(active_part(*p, routed, shared), accumulate && routed);
 }
 
 int moe_combine(const moe_problem *p, const void *x, const void *y_routed, const float *y_shared,
@@ -229,7 +265,7 @@ int moe_combine(const moe_problem *p, const void *x, const void *y_routed, const
     if (rc != MOE_OK) return rc;
     if (p->T == 0) return MOE_OK;
     if (!x || !h) return MOE_ERR_INVALID_ARG;
-    if (p->top_k > 0 && (!y_routed || !gate || !slot_of)) return MOE_ERR_INVALID_ARG;
+    if (p->top_k > 0 && y_routed && (!gate || !slot_of)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(h) || (y_routed && !aligned16(y_routed)) ||
         (y_shared && !aligned16(y_shared)))
         return MOE_ERR_INVALID_ARG;

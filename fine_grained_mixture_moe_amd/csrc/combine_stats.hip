@@ -162,12 +162,14 @@ hipError_t launch_combine(const moe_problem &p, const void *x, const void *y_rou
     const int64_t n = (int64_t)p.T * (p.d / 8);
     if (n == 0) return hipSuccess;
     const int grid = (int)((n + 255) / 256);
+    // no y_routed: the accumulating expert FFN already added the routed terms into y_shared
+    const int K = y_routed ? p.top_k : 0;
     if (p.dtype == MOE_BF16)
-        combine_kernel<uint16_t><<<grid, 256, 0, s>>>(p.T, p.d, p.top_k, (const uint16_t *)x,
+        combine_kernel<uint16_t><<<grid, 256, 0, s>>>(p.T, p.d, K, (const uint16_t *)x,
                                                       (const uint16_t *)y_routed, y_shared, gate, slot_of,
                                                       (uint16_t *)h);
     else
-        combine_kernel<float><<<grid, 256, 0, s>>>(p.T, p.d, p.top_k, (const float *)x, (const float *)y_routed,
+        combine_kernel<float><<<grid, 256, 0, s>>>(p.T, p.d, K, (const float *)x, (const float *)y_routed,
                                                    y_shared, gate, slot_of, (float *)h);
     return hipGetLastError();
 }

@@ -24,6 +24,8 @@
 // Every workgroup derives its (group, row-tile, column-tile) from the
 // device-side offsets, so no host round trip sizes the grid: the grid is an
 // upper bound and surplus workgroups exit at once.
+#include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -86,7 +88,16 @@ struct GemmParams {
     // (act_* above take the recomputed activations a)
     const uint8_t *da_shared, *da_routed;
     uint8_t *dp_shared, *dp_routed, *dq_shared, *dq_routed;
+    // accumulating down projection: y_acc[t] += gate * y for every grouped row
+    // of token t (gate_sorted in grouped order), y_acc[t] += y for the shared rows
+    const float *gate_sorted;
+    float *y_acc;
 };
+
+// fp32 add into y, performed in memory (no return value): the hardware float
+// atomic, coherent across the XCDs' L2s (agent scope); the order of the adds
+// into one element is not fixed
+__device__ __forceinline__ void acc_add(float *dst, float v) { unsafeAtomicAdd(dst, v); }
 
 // UP: true for the gate/up projection with SwiGLU epilogue, false for the down projection.
 template <typename DT, bool UP>
@@ -278,8 +289,17 @@ __global__ __launch_bounds__(256) void grouped_ffn_kernel(GemmParams P) {
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = acc[ni][mi][4 * q + e];
-                    if (shared) store4((float *)P.out_shared + (size_t)row * P.d + col, v);
-                    else store4((DT *)P.out_routed + (size_t)(row_off + row) * P.d + col, v);
+                    if (P.y_acc) {
+                        // accumulating mode: y_acc[t] += gate * y (gate 1 for the shared rows)
+                        const int t = shared ? row : P.sorted_token[row_off + row];
+                        const float g = shared ? 1.0f : P.gate_sorted[row_off + row];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc_add(P.y_acc + (size_t)t * P.d + col + e, g * v[e]);
+                    } else if (shared) {
+                        store4((float *)P.out_shared + (size_t)row * P.d + col, v);
+                    } else {
+                        store4((DT *)P.out_routed + (size_t)(row_off + row) * P.d + col, v);
+                    }
                 }
         }
     }
@@ -335,12 +355,14 @@ struct TileDesc {
 };
 
 // WAUX: cache policy of the weight loads (0, or kNonTemporal when every expert's weights are
-// read by a single token tile).
-template <int BM, bool UP, bool BWD, bool FUSED, int WAUX = 0>
+// read by a single token tile).  ACC (down projection only): instead of writing y per grouped
+// row, add gate * y into the fp32 rows of y_acc of the rows' tokens.
+template <int BM, bool UP, bool BWD, bool FUSED, int WAUX = 0, bool ACC = false>
 __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDesc td, uint8_t (&s_w)[2][256 * 128],
                                               uint8_t (&s_x)[2][BM * 128], int (&s_src)[BM],
                                               int *head = nullptr, int *next = nullptr) {
     static_assert(!BWD || UP, "the backward epilogue belongs to the up projection");
+    static_assert(!ACC || !UP, "only the down projection accumulates");
     constexpr int NT = 512;          // threads: 8 waves, 2 per SIMD
     constexpr int BN = 256;          // weight rows per tile
     constexpr int RB = 128;          // LDS row bytes
@@ -558,6 +580,53 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
     }
     // ---- epilogue: lane owns token column l32 of each block; register quad q
     //      holds weight rows 8q + 4*lhi + {0..3} of the block ----
+    if constexpr (ACC) {
+        // Accumulating form.  The fp32 tile goes through LDS 64 token rows at
+        // a time (the two 32-row blocks of pass pb, 64 KB in the weight
+        // stages): row lr (0..63) holds the 256 output columns as 64 chunks of
+        // 16 B, chunk c stored at c ^ lr, so the fragment writes (16 rows of a
+        // fragment per LDS cycle) and the row reads (one row per wave, 64
+        // consecutive floats) are both conflict-free.  Then each wave adds
+        // whole row segments (64 consecutive floats per instruction) into the
+        // rows of y_acc of the tile rows' tokens, scaled by the row's gate.
+        float *stage = (float *)&s_w[0][0];
+        auto sidx = [](int lr, int col) { return lr * 256 + (((col >> 2) ^ lr) << 2) + (col & 3); };
+        const int ncol = min(BN, P.d - n_tile * BN);
+        const int npass = cdiv(nr, 64);
+#pragma unroll
+        for (int pb = 0; pb < MB; ++pb) {
+            if (pb >= npass) break;
+            const int lr = wm * 32 + l32;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = wn * 64 + nb * 32 + 8 * q + 4 * lhi;
+                    *(float4 *)(stage + sidx(lr, col)) =
+                        make_float4(acc[nb][pb][4 * q], acc[nb][pb][4 * q + 1], acc[nb][pb][4 * q + 2],
+                                    acc[nb][pb][4 * q + 3]);
+                }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int lrow = __builtin_amdgcn_readfirstlane(wave + 8 * i);
+                const int r = pb * 64 + lrow;          // tile row
+                if (r < nr) {
+                    const int j = row_off + m0 + r;     // grouped row
+                    const int t = shared ? m0 + r : P.sorted_token[j];
+                    const float g = shared ? 1.0f : P.gate_sorted[j];
+                    float *dst = P.y_acc + (size_t)t * P.d + n_tile * BN;
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4) {
+                        const int col = c4 * 64 + lane;
+                        if (col < ncol) acc_add(dst + col, g * stage[sidx(lrow, col)]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    } else {
     if (!UP && shared) {
         // fp32 output of the shared experts: stored straight from registers
 #pragma unroll
@@ -722,6 +791,7 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
         }
     }
     }
+    }
 }
 
 template <int BM, bool UP, bool BWD = false>
@@ -814,18 +884,42 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
 // No wait can deadlock: a ticket is only ever held by a running workgroup,
 // up tiles never wait, a down tile's up tiles precede it in its queue, and a
 // workgroup takes its next ticket only after the current tile's wait is
-// over.  The wait is still bounded (kSpinLimit sleeps, then an error flag).
+// over.  The wait is still bounded (spin_limit sleeps): a down tile whose
+// wait gives up sets the error flag, skips its GEMM and writes NaN over its
+// outputs instead (so no output is ever computed from partial activations),
+// and the launch goes on; the host reads the flag through
+// moe_expert_ffn_status.
 // ---------------------------------------------------------------------------
-constexpr int kQueues = 8;
+constexpr int kQueues = kFfnQueues;
 constexpr int kSpinLimit = 1 << 22;
 
 struct FusedCtl {
-    int *head;   // [kQueues] next ticket of each queue
-    int *err;    // [1] set when a wait ran out of its budget
-    int *done;   // [runs] finished up tiles of each token run
+    int *head;        // [kQueues] next ticket of each queue
+    int *err;         // [1] set when a wait ran out of its budget
+    int *done;        // [runs] finished up tiles of each token run
+    int spin_limit;   // sleeps before a wait gives up
+    int need_extra;   // added to every wait's target (0; 1 makes every wait unmeetable, for tests)
 };
 
-template <int BM, int WAUX>
+// NaN over the outputs of a down tile whose wait gave up.
+template <bool ACC>
+__device__ void poison_down_tile(const GemmParams &P, const TileDesc &td) {
+    const int c0 = td.n_tile * 256, nc = min(256, P.d - c0);
+    const float qnan = __builtin_nanf("");
+    for (int i = threadIdx.x; i < td.nr * nc; i += 512) {
+        const int r = i / nc, c = c0 + i % nc;
+        if constexpr (ACC) {
+            const int t = td.shared ? td.m0 + r : P.sorted_token[td.row_off + td.m0 + r];
+            acc_add(P.y_acc + (size_t)t * P.d + c, qnan);
+        } else if (td.shared) {
+            ((float *)P.out_shared)[(size_t)(td.m0 + r) * P.d + c] = qnan;
+        } else {
+            ((uint16_t *)P.out_routed)[(size_t)(td.row_off + td.m0 + r) * P.d + c] = 0x7fc0;
+        }
+    }
+}
+
+template <int BM, int WAUX, bool ACC>
 __global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, GemmParams Pd, FusedCtl C) {
     __shared__ __attribute__((aligned(16))) uint8_t s_w[2][256 * 128];
     __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * 128];
@@ -833,6 +927,7 @@ __global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, G
     __shared__ int s_runp[MAXG + 1];   // prefix of the token runs over the groups
     __shared__ int s_offs[MAXG + 1];   // the routed group offsets
     __shared__ int s_ticket;
+    __shared__ int s_met;              // the down tile's wait was met
 
     const GemmParams &P = Pu;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -917,19 +1012,23 @@ __global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, G
             td.m0 = (run - rp) * rl;
             td.nr = min(rl, rows - td.m0);
             td.n_tile = n;
+            int met = 1;
             if (!up) {
-                const int need = td.shared ? nus : nur;
+                const int need = (td.shared ? nus : nur) + C.need_extra;
                 if (tid == 0) {
-                    int spins = 0;
+                    int spins = 0, ok = 1;
                     while (__hip_atomic_load(&C.done[run], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-                        if (++spins > kSpinLimit) {
+                        if (++spins > C.spin_limit) {
                             __hip_atomic_store(C.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            ok = 0;
                             break;
                         }
                         __builtin_amdgcn_s_sleep(4);
                     }
+                    s_met = ok;
                 }
                 __syncthreads();
+                met = uni(s_met);
             }
             int next = 0;
             if (up) {
@@ -937,8 +1036,11 @@ __global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, G
                 __builtin_amdgcn_s_waitcnt(0);   // this thread's activation stores are complete
                 __syncthreads();
                 if (tid == 0) __hip_atomic_fetch_add(&C.done[run], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else if (met) {
+                ffn_tile_bf16<BM, false, false, true, WAUX, ACC>(Pd, td, s_w, s_x, s_src, &C.head[q], &next);
             } else {
-                ffn_tile_bf16<BM, false, false, true, WAUX>(Pd, td, s_w, s_x, s_src, &C.head[q], &next);
+                poison_down_tile<ACC>(Pd, td);
+                if (tid == 0) next = atomicAdd(&C.head[q], 1);
             }
             if (tid == 0) s_ticket = next;
             __syncthreads();
@@ -948,8 +1050,23 @@ __global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, G
     }
 }
 
-__global__ __launch_bounds__(256) void ffn_ctl_zero_kernel(int *ctl, int n) {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) ctl[i] = 0;
+// Runs before every moe_expert_ffn: clears the control words of the fused
+// launch (queue heads, error flag, run counters) and, in accumulating mode,
+// zeroes y_acc [T, d] and writes the gates in grouped order
+// (gate_sorted[slot_of[t,k]] = gate[t,k]; slots of skipped pairs are -1).
+__global__ __launch_bounds__(256) void ffn_prep_kernel(int *ctl, int n, float *y_acc, int64_t n4,
+                                                       const float *gate, const int32_t *slot_of,
+                                                       float *gate_sorted, int npairs) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (int64_t i = i0; i < n; i += stride) ctl[i] = 0;
+    if (y_acc) {
+        for (int64_t i = i0; i < n4; i += stride) ((float4 *)y_acc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int64_t i = i0; i < npairs; i += stride) {
+            const int j = slot_of[i];
+            if (j >= 0 && j < npairs) gate_sorted[j] = gate[i];
+        }
+    }
 }
 
 GemmParams make_params(const moe_problem &p, const FfnArgs &a, bool up) {
@@ -960,6 +1077,8 @@ GemmParams make_params(const moe_problem &p, const FfnArgs &a, bool up) {
     P.x = (const uint8_t *)a.x;
     P.act_shared = (const uint8_t *)a.act_shared;
     P.act_routed = (const uint8_t *)a.act_routed;
+    P.gate_sorted = a.gate_sorted;
+    P.y_acc = up ? nullptr : a.y_acc;
     if (up) {
         P.wa_r = (const uint8_t *)a.w1_r; P.wb_r = (const uint8_t *)a.w3_r;
         P.wa_s = (const uint8_t *)a.w1_s; P.wb_s = (const uint8_t *)a.w3_s;
@@ -1008,24 +1127,72 @@ hipError_t launch_bf16(const moe_problem &p, const FfnArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_fused(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s) {
+// The preparation kernel of every moe_expert_ffn call (see ffn_prep_kernel).
+hipError_t launch_prep(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s) {
     const int n = ffn_ctl_ints(p);
-    ffn_ctl_zero_kernel<<<min(cdiv(n, 256), 64), 256, 0, s>>>(ctl, n);
+    const bool accum = a.y_acc != nullptr && p.T > 0;
+    const int64_t n4 = accum ? (int64_t)p.T * p.d / 4 : 0;
+    const int npairs = accum ? p.T * p.top_k : 0;
+    const int64_t work = std::max<int64_t>(std::max<int64_t>(n, n4), npairs);
+    const int grid = (int)std::min<int64_t>(std::max<int64_t>((work + 255) / 256, 1), 2048);
+    ffn_prep_kernel<<<grid, 256, 0, s>>>(ctl, n, accum ? a.y_acc : nullptr, n4, a.gate, a.slot_of,
+                                         a.gate_sorted, npairs);
+    return hipGetLastError();
+}
+
+// Which fused instantiation a problem takes: the token tile (256 rows when the routed experts
+// average at least 256 rows, else 128) and the weight loads' cache policy. Decode batches (at
+// most 64 rows per expert on average, no shared group or at most 128 tokens) read each
+// expert's weights with a single token tile: there the weight loads are non-temporal, so the
+// streamed weights leave L2 to the token rows and activations that are read again (c5a expert
+// FFN 207.5 -> 193.2 us, c5c 548 -> 510 us). With more rows an expert's second tile re-reads
+// its weights from L2, and the hint costs 4-13% (192 rows per expert on average: 491 ->
+// 555 us); a shared group over more than 128 tokens is such a case too.
+enum class FusedForm { k256, k128nt, k128 };
+FusedForm fused_form(const moe_problem &p) {
+    const int64_t avg = p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / p.n_routed : (int64_t)p.T;
+    if (avg >= 256) return FusedForm::k256;
+    if (avg <= 64 && (p.n_shared == 0 || p.T <= 128)) return FusedForm::k128nt;
+    return FusedForm::k128;
+}
+
+// Test hook: MOE_DEBUG_FFN_STALL=<n> (n > 0) makes every wait of the fused launch unmeetable and
+// gives up after n sleeps, so the error path runs with every kernel exiting normally.
+void stall_hook(int *spin_limit, int *need_extra) {
+    *spin_limit = kSpinLimit;
+    *need_extra = 0;
+    if (const char *e = getenv("MOE_DEBUG_FFN_STALL")) {
+        const int n = atoi(e);
+        if (n > 0) {
+            *spin_limit = n;
+            *need_extra = 1;
+        }
+    }
+}
+
+hipError_t launch_fused(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s) {
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     const GemmParams Pu = make_params(p, a, true), Pd = make_params(p, a, false);
-    const FusedCtl C{ctl, ctl + kQueues, ctl + kQueues + 1};
-    const int64_t avg = p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / p.n_routed : (int64_t)p.T;
-    // Decode batches (at most 64 rows per expert on average) read each expert's weights with a
-    // single token tile: there the weight loads are non-temporal, so the streamed weights leave L2
-    // to the token rows and activations that are read again (c5a expert FFN 207.5 -> 193.2 us,
-    // c5c 548 -> 510 us). With more rows an expert's second tile re-reads its weights from L2, and
-    // the hint costs 4-13% (192 rows per expert on average: 491 -> 555 us).
-    if (avg >= 256) grouped_ffn_fused_kernel<256, 0><<<ncu, 512, 0, s>>>(Pu, Pd, C);
-    else if (avg <= 64) grouped_ffn_fused_kernel<128, kNonTemporal><<<ncu, 512, 0, s>>>(Pu, Pd, C);
-    else grouped_ffn_fused_kernel<128, 0><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+    FusedCtl C{ctl, ctl + kQueues, ctl + kQueues + 1, 0, 0};
+    stall_hook(&C.spin_limit, &C.need_extra);
+    const bool accum = a.y_acc != nullptr;
+    switch (fused_form(p)) {
+        case FusedForm::k256:
+            if (accum) grouped_ffn_fused_kernel<256, 0, true><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+            else grouped_ffn_fused_kernel<256, 0, false><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+            break;
+        case FusedForm::k128nt:
+            if (accum) grouped_ffn_fused_kernel<128, kNonTemporal, true><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+            else grouped_ffn_fused_kernel<128, kNonTemporal, false><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+            break;
+        case FusedForm::k128:
+            if (accum) grouped_ffn_fused_kernel<128, 0, true><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+            else grouped_ffn_fused_kernel<128, 0, false><<<ncu, 512, 0, s>>>(Pu, Pd, C);
+            break;
+    }
     return hipGetLastError();
 }
 
@@ -1066,10 +1233,25 @@ hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_
 }
 
 hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s) {
+    hipError_t e = launch_prep(p, a, ctl, s);
+    const bool active = p.T > 0 && (p.n_shared > 0 || (p.n_routed > 0 && p.top_k > 0));
+    if (e != hipSuccess || !active) return e;
     if (p.dtype == MOE_BF16) return launch_fused(p, a, ctl, s);
-    hipError_t e = launch_typed<float, true>(p, a, s);
+    e = launch_typed<float, true>(p, a, s);
     if (e == hipSuccess) e = launch_typed<float, false>(p, a, s);
     return e;
+}
+
+const char *expert_ffn_kernel_name(const moe_problem &p, bool accum) {
+    if (p.dtype != MOE_BF16) return "grouped_ffn_kernel<float, true> + grouped_ffn_kernel<float, false>";
+    switch (fused_form(p)) {
+        case FusedForm::k256:
+            return accum ? "grouped_ffn_fused_kernel<256, 0, true>" : "grouped_ffn_fused_kernel<256, 0, false>";
+        case FusedForm::k128nt:
+            return accum ? "grouped_ffn_fused_kernel<128, 2, true>" : "grouped_ffn_fused_kernel<128, 2, false>";
+        default:
+            return accum ? "grouped_ffn_fused_kernel<128, 0, true>" : "grouped_ffn_fused_kernel<128, 0, false>";
+    }
 }
 
 }  // namespace moe

@@ -35,17 +35,21 @@ struct WsLayout {
     size_t perm_base;      // int32  [N', perm_blocks]   first slot of each (expert, block)
     size_t act_shared;     // dtype  [T, K_s*w]          SwiGLU activations, shared experts
     size_t act_routed;     // dtype  [T*K', w]           SwiGLU activations, grouped order
+    size_t gate_sorted;    // fp32   [T*K']              gates in grouped order (accumulating expert FFN)
     size_t ffn_ctl;        // int32  [ffn_ctl_ints]      fused expert FFN: queue heads, error flag, per-run counters
     size_t total;
 };
 
-// Control words of the fused expert FFN launch: 8 queue heads, an error
-// flag, and one counter per token run; a group of c rows has ceil(c/128)
-// runs at most, so sum_g ceil(c_g/128) <= T K'/128 + N' (+ T/128 shared).
+// Control words of the fused expert FFN launch: kFfnQueues queue heads, an
+// error flag (index kFfnCtlErr), and one counter per token run; a group of c
+// rows has ceil(c/128) runs at most, so sum_g ceil(c_g/128) <= T K'/128 + N'
+// (+ T/128 shared).
+constexpr int kFfnQueues = 8;
+constexpr int kFfnCtlErr = kFfnQueues;
 inline int ffn_ctl_ints(const moe_problem &p) {
     const int64_t runs = (p.n_shared > 0 ? cdiv(p.T, 128) : 0) +
                          (p.n_routed > 0 ? ((int64_t)p.T * p.top_k) / 128 + p.n_routed : 0);
-    return (int)(8 + 1 + runs);
+    return (int)(kFfnQueues + 1 + runs);
 }
 
 // Routing workgroups for T tokens (route.hip).
@@ -65,6 +69,7 @@ inline WsLayout ws_layout(const moe_problem &p) {
     L.perm_base = take(pb * nr * sizeof(int32_t));
     L.act_shared = take((size_t)p.T * p.n_shared * p.inter * es);
     L.act_routed = take((size_t)p.T * p.top_k * p.inter * es);
+    L.gate_sorted = take((size_t)p.T * p.top_k * sizeof(float));
     L.ffn_ctl = take((size_t)ffn_ctl_ints(p) * sizeof(int32_t));
     L.total = off;
     return L;
@@ -93,14 +98,28 @@ struct FfnArgs {
     void *act_shared, *act_routed;
     void *y_routed;
     float *y_shared;
+    // accumulating mode (moe_expert_ffn with y_routed == NULL): y_acc [T, d]
+    // receives the whole expert sum (zeroed first); the gates and slots of
+    // the (t, k) pairs and the workspace's grouped-order gate array.
+    // Null outside that mode.
+    float *y_acc;
+    const float *gate;
+    const int32_t *slot_of;
+    float *gate_sorted;
 };
 
 // up: act = SiLU(X W1^T) * (X W3^T) into the workspace; down: y = act W2^T.
 hipError_t launch_expert_up(const moe_problem &p, const FfnArgs &a, hipStream_t s);
 hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_t s);
 // both projections: bf16 as one fused persistent launch (ctl: the workspace's
-// control words), fp32 as the two launches above
+// control words), fp32 as the two launches above.  A preparation kernel
+// always runs first: it clears the control words (so the error flag reports
+// this call only) and, in accumulating mode, zeroes y_acc and writes the
+// gates in grouped order.  p may have no active part (then only the
+// preparation runs).
 hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s);
+// name of the kernel (template instantiation) launch_expert_ffn runs for p
+const char *expert_ffn_kernel_name(const moe_problem &p, bool accum);
 // backward: the up projection recomputed, with a = SiLU(p) q written to act_*
 // and dp, dq formed from da in the epilogue (bf16 only)
 hipError_t launch_expert_up_backward(const moe_problem &p, const FfnArgs &a, const void *da_shared,

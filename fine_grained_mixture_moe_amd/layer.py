@@ -42,7 +42,9 @@ class DeviceLayer:
     """Inputs resident in HBM plus every output buffer of one layer pass."""
 
     def __init__(self, inp: LayerInputs, device="cuda", want_probs: bool = False, groups: Optional[int] = None,
-                 top_k: Optional[int] = None):
+                 top_k: Optional[int] = None, accumulate: bool = False):
+        """accumulate: run moe_expert_ffn in its accumulating mode (no y_routed; the gate-weighted
+        expert outputs are added into y_acc inside the down projection, not bitwise reproducible)."""
         torch = _torch()
         wl = inp.wl
         self.inp = inp
@@ -76,9 +78,13 @@ class DeviceLayer:
         self.offsets = torch.empty(Nr + 1, dtype=i32, device=dev)
         self.sorted_token = torch.empty(max(TK, 1), dtype=i32, device=dev)
         self.slot_of = torch.empty((T, K), dtype=i32, device=dev)
-        self.y_routed = torch.empty((max(TK, 1), d), dtype=tdt, device=dev)
-        self.y_shared = torch.empty((T, d), dtype=f32, device=dev) if Ks else None
+        self.accumulate = bool(accumulate) and TK > 0
+        self.y_routed = None if self.accumulate else torch.empty((max(TK, 1), d), dtype=tdt, device=dev)
+        # y_acc: the shared experts' sum (gather mode) or the whole expert sum (accumulating mode)
+        self.y_acc = torch.empty((T, d), dtype=f32, device=dev) if (Ks or self.accumulate) else None
         self.h = torch.empty((T, d), dtype=tdt, device=dev)
+        self.x_zero = None     # zero residual and output of expert_sum()
+        self.y_sum = None
         D = max(self.groups, 1)
         self.f = torch.empty(max(Nr, 1), dtype=f32, device=dev)
         self.P = torch.empty(max(Nr, 1), dtype=f32, device=dev)
@@ -88,6 +94,7 @@ class DeviceLayer:
         self.dev_bal = torch.empty(1, dtype=f32, device=dev)
         self.ws_bytes = M.moe_workspace_size(self.prob)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.ffn_called = False   # the workspace's status word is defined only after moe_expert_ffn
 
     # -- the five calls ----------------------------------------------------
     def route(self, stream=None):
@@ -107,19 +114,34 @@ class DeviceLayer:
 
     def expert_ffn(self, stream=None):
         M.moe_expert_ffn(self.prob, self.x, self.offsets, self.sorted_token, self.w1_r, self.w3_r, self.w2_r,
-                         self.w1_s, self.w3_s, self.w2_s, self.y_routed, self.y_shared, self.ws, self.ws_bytes,
-                         stream)
+                         self.w1_s, self.w3_s, self.w2_s, self.y_routed, self.y_acc, self.gate, self.slot_of,
+                         self.ws, self.ws_bytes, stream)
+        self.ffn_called = True
+
+    def ffn_status(self, stream=None) -> int:
+        """Status of the last moe_expert_ffn (synchronises the stream)."""
+        return M.moe_expert_ffn_status(self.prob, self.ws, self.ws_bytes, stream)
 
     def expert_up(self, stream=None):
         M.moe_expert_up(self.prob, self.x, self.offsets, self.sorted_token, self.w1_r, self.w3_r, self.w1_s,
                         self.w3_s, self.ws, self.ws_bytes, stream)
 
     def expert_down(self, stream=None):
-        M.moe_expert_down(self.prob, self.offsets, self.w2_r, self.w2_s, self.y_routed, self.y_shared, self.ws,
+        M.moe_expert_down(self.prob, self.offsets, self.w2_r, self.w2_s, self.y_routed, self.y_acc, self.ws,
                           self.ws_bytes, stream)
 
     def combine(self, stream=None):
-        M.moe_combine(self.prob, self.x, self.y_routed, self.y_shared, self.gate, self.slot_of, self.h, stream)
+        M.moe_combine(self.prob, self.x, self.y_routed, self.y_acc, self.gate, self.slot_of, self.h, stream)
+
+    def expert_sum(self, stream=None):
+        """y = sum of the shared and gate-weighted routed expert outputs, as the GPU combine forms it:
+        moe_combine with an all-zero residual, into a separate buffer (h stays as it is)."""
+        torch = _torch()
+        if self.x_zero is None:
+            self.x_zero = torch.zeros_like(self.x)
+            self.y_sum = torch.empty_like(self.h)
+        M.moe_combine(self.prob, self.x_zero, self.y_routed, self.y_acc, self.gate, self.slot_of, self.y_sum,
+                      stream)
 
     def balance_stats(self, stream=None):
         M.moe_balance_stats(self.prob, self.groups, self.counts, self.prob_sum, self.f, self.P, self.f_dev,
@@ -143,6 +165,14 @@ class DeviceLayer:
         self.permute(stream)
         self.expert_ffn(stream)
         self.combine(stream)
+
+    def check_status(self) -> None:
+        """Raise if the last moe_expert_ffn reported a stalled wait (its outputs hold NaN)."""
+        if not self.ffn_called:
+            return
+        st = self.ffn_status()
+        if st != M.MOE_OK:
+            raise M.MoEError("moe_expert_ffn", st)
 
     # -- backward pass -----------------------------------------------------
     def backward(self, dh: np.ndarray, alpha1: float, alpha2: float, stream=None):
@@ -180,6 +210,8 @@ class DeviceLayer:
             self.dh = to_device(bf16_bits_from_f32(np.ascontiguousarray(dh, np.float32)), "bf16", dev)
         else:
             self.dh = to_device(np.ascontiguousarray(dh, np.float32), "f32", dev)
+        if self.accumulate:
+            raise ValueError("the backward pass needs y_routed: build the layer in gather mode")
         if Nr:
             M.moe_combine_backward(p, self.dh, self.y_routed, self.gate, self.slot_of, self.dy_routed, self.dgate,
                                    stream)
@@ -202,18 +234,23 @@ class DeviceLayer:
                     dw2_s=g(self.dw2_s), dcent=g(self.dcent)[:Nr], dbias=g(self.dbias)[:Nr])
 
     # -- readback ----------------------------------------------------------
-    def results(self) -> dict:
+    def results(self, check: bool = True) -> dict:
+        """Read every output back (after checking the expert FFN's status word unless check=False)."""
         torch = _torch()
         torch.cuda.synchronize(self.device)
+        if check:
+            self.check_status()
         Nr = self.prob.n_routed
         TK = self.prob.T * self.prob.top_k
+        y_acc = None if self.y_acc is None else self.y_acc.cpu().numpy()
         out = dict(
             idx=self.idx.cpu().numpy(), gate=self.gate.cpu().numpy(),
             counts=self.counts.cpu().numpy()[:Nr], prob_sum=self.prob_sum.cpu().numpy()[:Nr],
             offsets=self.offsets.cpu().numpy(), sorted_token=self.sorted_token.cpu().numpy()[:TK],
             slot_of=self.slot_of.cpu().numpy(),
-            y_routed=to_numpy_f32(self.y_routed)[:TK],
-            y_shared=None if self.y_shared is None else self.y_shared.cpu().numpy(),
+            y_routed=None if self.y_routed is None else to_numpy_f32(self.y_routed)[:TK],
+            y_shared=None if self.accumulate else y_acc,
+            y_acc=y_acc,
             h=to_numpy_f32(self.h),
             f=self.f.cpu().numpy()[:Nr], P=self.P.cpu().numpy()[:Nr],
             f_dev=self.f_dev.cpu().numpy(), P_dev=self.P_dev.cpu().numpy(),
@@ -221,4 +258,6 @@ class DeviceLayer:
         )
         if self.probs is not None:
             out["probs"] = self.probs.cpu().numpy()
+        if self.y_sum is not None:
+            out["y"] = to_numpy_f32(self.y_sum)
         return out

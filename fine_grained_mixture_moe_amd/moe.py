@@ -15,7 +15,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_STALLED = 0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16 = 0, 1
 
 
@@ -59,7 +59,11 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_size.argtypes = [_pp, ctypes.POINTER(_sz)]
         L.moe_route.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_permute.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
-        L.moe_expert_ffn.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_expert_ffn.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _sz, _vp]
+        L.moe_expert_ffn_status.argtypes = [_pp, _vp, _sz, _vp]
+        L.moe_expert_ffn_kernel.argtypes = [_pp, ctypes.c_int]
+        L.moe_expert_ffn_kernel.restype = ctypes.c_char_p
         L.moe_expert_up.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_expert_down.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_combine.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -70,7 +74,8 @@ def lib() -> ctypes.CDLL:
         L.moe_combine_backward.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_expert_ffn_backward.argtypes = [_pp] + [_vp] * 20 + [_sz, _vp]
         L.moe_route_backward.argtypes = [_pp, ctypes.c_int32, ctypes.c_float, ctypes.c_float] + [_vp] * 13 + [_sz, _vp]
-        for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_up",
+        for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_status",
+                   "moe_expert_up",
                    "moe_expert_down", "moe_combine", "moe_balance_stats", "moe_backward_workspace_size",
                    "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward", "moe_route_ablate",
                    "moe_route_hash"):
@@ -137,11 +142,23 @@ def moe_permute(p, idx, offsets, sorted_token, slot_of, ws, ws_bytes, stream=Non
 
 
 def moe_expert_ffn(p, x, offsets, sorted_token, w1_routed, w3_routed, w2_routed, w1_shared, w3_shared,
-                   w2_shared, y_routed, y_shared, ws, ws_bytes, stream=None):
+                   w2_shared, y_routed, y_acc, gate, slot_of, ws, ws_bytes, stream=None):
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         ctypes.byref(p), _ptr(x), _ptr(offsets), _ptr(sorted_token), _ptr(w1_routed), _ptr(w3_routed),
-        _ptr(w2_routed), _ptr(w1_shared), _ptr(w3_shared), _ptr(w2_shared), _ptr(y_routed), _ptr(y_shared),
-        _ptr(ws), ws_bytes, _stream(stream)))
+        _ptr(w2_routed), _ptr(w1_shared), _ptr(w3_shared), _ptr(w2_shared), _ptr(y_routed), _ptr(y_acc),
+        _ptr(gate), _ptr(slot_of), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_expert_ffn_status(p, ws, ws_bytes, stream=None) -> int:
+    """Status word of the last moe_expert_ffn on ws (synchronises the stream); returned, not raised."""
+    return lib().moe_expert_ffn_status(ctypes.byref(p), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_expert_ffn_kernel(p, accumulate: bool = False) -> str:
+    name = lib().moe_expert_ffn_kernel(ctypes.byref(p), int(bool(accumulate)))
+    if name is None:
+        raise MoEError("moe_expert_ffn_kernel", MOE_ERR_INVALID_ARG)
+    return name.decode()
 
 
 def moe_expert_up(p, x, offsets, sorted_token, w1_routed, w3_routed, w1_shared, w3_shared, ws, ws_bytes,
@@ -157,8 +174,8 @@ def moe_expert_down(p, offsets, w2_routed, w2_shared, y_routed, y_shared, ws, ws
         _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def moe_combine(p, x, y_routed, y_shared, gate, slot_of, h, stream=None):
-    _check("moe_combine", lib().moe_combine(ctypes.byref(p), _ptr(x), _ptr(y_routed), _ptr(y_shared),
+def moe_combine(p, x, y_routed, y_acc, gate, slot_of, h, stream=None):
+    _check("moe_combine", lib().moe_combine(ctypes.byref(p), _ptr(x), _ptr(y_routed), _ptr(y_acc),
                                             _ptr(gate), _ptr(slot_of), _ptr(h), _stream(stream)))
 
 

@@ -48,9 +48,10 @@
  *    [d, w].  Shared experts are stacked [K_s, ...], routed [N', ...].
  *  - The workspace `ws` (size from moe_workspace_size, 256-byte aligned)
  *    holds the per-block partial routing statistics, the grouping scratch,
- *    the SwiGLU activations and the control words of the fused expert FFN
- *    launch (cleared by moe_expert_ffn itself before each use; no
- *    initialisation is needed).  The calls use disjoint parts of it, so one
+ *    the SwiGLU activations, the gates in grouped order (accumulating
+ *    expert FFN) and the control words of the fused expert FFN launch
+ *    (cleared by moe_expert_ffn itself before each use; no initialisation
+ *    is needed).  The calls use disjoint parts of it, so one
  *    workspace serves a whole layer pass on one stream; calls that overlap
  *    in time (other streams) need workspaces of their own.
  */
@@ -70,6 +71,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2)  /* outside the supported envelope (see each call) */
 #define MOE_ERR_WORKSPACE   (-3)  /* workspace missing or smaller than required    */
 #define MOE_ERR_HIP         (-4)  /* a HIP launch or runtime call failed           */
+#define MOE_ERR_STALLED     (-5)  /* a device-side wait gave up (moe_expert_ffn_status) */
 
 /* element types of x, weights, y_routed and h */
 #define MOE_F32  0
@@ -171,17 +173,34 @@ int moe_permute(const moe_problem *p, const int32_t *idx, int32_t *offsets,
  * moe_expert_ffn -- the expert FFNs (SwiGLU, no biases) on MFMA.
  * Source: "[ACL 2024] DeepSeekMoE ..." sections "Two core strategies" (m
  * fine-grained experts of width 1/m; K_s shared experts always active) and
- * "Method details" (FFN_i terms of the layer output).
+ * "Method details" (FFN_i terms of the layer output and their gate-weighted
+ * sum).
  *
  *   x            [T, d]         dtype in
  *   offsets      [N'+1]         int32 in   from moe_permute
  *   sorted_token [T*K']         int32 in   from moe_permute
  *   w1_routed, w3_routed [N', w, d]  dtype;  w2_routed [N', d, w]  dtype
  *   w1_shared, w3_shared [K_s, w, d] dtype;  w2_shared [K_s, d, w] dtype
- *   y_routed     [T*K', d]      dtype out  y_routed[j] = FFN_{e(j)}(u_{sorted_token[j]})
- *                                          (unweighted, in grouped order)
- *   y_shared     [T, d]         fp32  out  sum_{i < K_s} FFN_i(u_t)
- *                                          (may be NULL when K_s == 0)
+ *   y_routed     [T*K', d]      dtype out  (nullable, selects the mode below)
+ *   y_acc        [T, d]         fp32  out
+ *   gate         [T, K']        fp32  in   from moe_route (accumulating mode only)
+ *   slot_of      [T, K']        int32 in   from moe_permute (accumulating mode only)
+ *
+ * Two modes:
+ *  - gather (y_routed != NULL, the default of the layer pass):
+ *      y_routed[j] = FFN_{e(j)}(u_{sorted_token[j]})   unweighted, grouped order
+ *      y_acc[t]    = sum_{i < K_s} FFN_i(u_t)           (y_acc may be NULL when K_s == 0)
+ *    moe_combine then sums the gate-weighted rows of each token in k order:
+ *    bitwise reproducible.
+ *  - accumulating (y_routed == NULL and T*K' > 0): the down projection adds
+ *    gate[t,k] * FFN_{idx[t,k]}(u_t) of every routed pair, and every shared
+ *    FFN_i(u_t), straight into y_acc (zeroed by the call first), so
+ *      y_acc[t] = sum_{i < K_s} FFN_i(u_t) + sum_k gate[t,k] FFN_{idx[t,k]}(u_t)
+ *    and moe_combine (with y_routed = NULL) only adds the residual.  This
+ *    saves the round trip of y_routed through HBM.  The adds are fp32
+ *    atomics in memory: their order, and so the last bits of y_acc, vary
+ *    from run to run (NOT bitwise reproducible).  gate and slot_of are
+ *    required; the gates are copied into grouped order in the workspace.
  *
  * The K_s shared experts run as one dense expert of width K_s*w over all T
  * rows.  Accumulation is fp32; the SwiGLU activation is rounded to dtype
@@ -191,15 +210,40 @@ int moe_permute(const moe_problem *p, const int32_t *idx, int32_t *offsets,
  * In bf16 both projections run as one persistent launch (one workgroup per
  * CU) whose down-projection tiles wait, on counters in the workspace, for
  * the up-projection tiles of their token rows; a small kernel clears those
- * counters first.  The results are the same as moe_expert_up followed by
+ * counters first (it runs on every call, also when there is no work).  In
+ * gather mode the results are the same as moe_expert_up followed by
  * moe_expert_down.  fp32 runs the two projections as two launches.
  */
 int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets,
                    const int32_t *sorted_token, const void *w1_routed,
                    const void *w3_routed, const void *w2_routed,
                    const void *w1_shared, const void *w3_shared,
-                   const void *w2_shared, void *y_routed, float *y_shared,
+                   const void *w2_shared, void *y_routed, float *y_acc,
+                   const float *gate, const int32_t *slot_of,
                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_expert_ffn_status -- error word of the most recent moe_expert_ffn
+ * enqueued with this workspace.  Waits for `stream` to finish, then reads
+ * the word.  Returns MOE_OK, or MOE_ERR_STALLED when a down-projection tile
+ * of the fused launch gave up waiting for the up-projection tiles of its
+ * token rows (bounded wait of about 2^22 sleeps).  Such a tile computes
+ * nothing and writes NaN over its outputs, so no result is silently built
+ * from partial activations.  MOE_ERR_HIP if the stream or the read fails.
+ * Must be called before the next moe_expert_ffn with the same workspace
+ * (which clears the word).  Test hook: with the environment variable
+ * MOE_DEBUG_FFN_STALL=<n> (n > 0) set when moe_expert_ffn is called, every
+ * such wait is made unmeetable and gives up after n sleeps.
+ */
+int moe_expert_ffn_status(const moe_problem *p, const void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_expert_ffn_kernel -- name of the GPU kernel (template instantiation)
+ * that moe_expert_ffn launches for `p` (accumulate != 0: accumulating
+ * mode), as it appears in a kernel trace; "" when the call has no work;
+ * NULL for an invalid problem.  Static storage.
+ */
+const char *moe_expert_ffn_kernel(const moe_problem *p, int accumulate);
 
 /*
  * moe_expert_up / moe_expert_down -- the two halves of moe_expert_ffn, for
@@ -208,7 +252,8 @@ int moe_expert_ffn(const moe_problem *p, const void *x, const int32_t *offsets,
  * shared row and grouped routed row into the workspace; moe_expert_down
  * reads them from the same workspace (same problem, same ws, same stream, in
  * that order) and writes y_routed and y_shared exactly as moe_expert_ffn
- * does.  Arguments have the meanings given above.
+ * does in gather mode (y_shared: the y_acc of that mode).  Arguments have
+ * the meanings given above.
  */
 int moe_expert_up(const moe_problem *p, const void *x, const int32_t *offsets,
                   const int32_t *sorted_token, const void *w1_routed,
@@ -222,14 +267,17 @@ int moe_expert_down(const moe_problem *p, const int32_t *offsets,
 /*
  * moe_combine -- layer output, "[ACL 2024] DeepSeekMoE ..." section "Method
  * details" (output formula):
- *   h_t = u_t + y_shared_t + sum_{k < K'} gate[t,k] * y_routed[slot_of[t,k]]
+ *   h_t = u_t + y_acc_t + sum_{k < K'} gate[t,k] * y_routed[slot_of[t,k]]
  * summed in k order in fp32 (deterministic), written as dtype.
  *
- *   x [T, d] dtype, y_routed [T*K', d] dtype, y_shared [T, d] fp32 (NULL =
+ *   x [T, d] dtype, y_routed [T*K', d] dtype, y_acc [T, d] fp32 (NULL =
  *   zero), gate [T, K'] fp32, slot_of [T, K'] int32, h [T, d] dtype out.
+ * With y_routed == NULL (after the accumulating moe_expert_ffn, whose y_acc
+ * already holds the whole expert sum) h_t = u_t + y_acc_t and gate/slot_of
+ * are not read.  With x all zero, h is the expert sum y itself.
  */
 int moe_combine(const moe_problem *p, const void *x, const void *y_routed,
-                const float *y_shared, const float *gate, const int32_t *slot_of,
+                const float *y_acc, const float *gate, const int32_t *slot_of,
                 void *h, void *stream);
 
 /*

@@ -34,9 +34,26 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert M.moe_status_str(0) == "MOE_OK"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert M.moe_status_str(code).startswith("MOE_ERR")
     assert "gfx950" in M.moe_version()
+
+
+def test_expert_ffn_kernel_names():
+    """The launcher's own choice of fused instantiation: token tile and weight cache policy."""
+    name = M.moe_expert_ffn_kernel
+    mk = M.moe_problem.make
+    assert name(mk(4096, 1280, 0, 64, 8, 512, "bf16")) == "grouped_ffn_fused_kernel<256, 0, false>"
+    assert name(mk(4096, 1280, 0, 64, 8, 512, "bf16"), True) == "grouped_ffn_fused_kernel<256, 0, true>"
+    assert name(mk(64, 2048, 2, 64, 6, 1408, "bf16")) == "grouped_ffn_fused_kernel<128, 2, false>"
+    # 48 rows per routed expert on average, but a shared group of 1024 tokens re-reads its weights: no nt
+    assert name(mk(1024, 2048, 2, 128, 6, 1408, "bf16")) == "grouped_ffn_fused_kernel<128, 0, false>"
+    assert name(mk(1024, 2048, 0, 128, 6, 1408, "bf16")) == "grouped_ffn_fused_kernel<128, 2, false>"
+    assert name(mk(2048, 2048, 2, 64, 6, 1408, "bf16")) == "grouped_ffn_fused_kernel<128, 0, false>"
+    assert name(mk(512, 256, 1, 63, 7, 128, "f32")).startswith("grouped_ffn_kernel<float")
+    assert name(mk(0, 256, 1, 63, 7, 128, "bf16")) == ""
+    with pytest.raises(M.MoEError):
+        name(mk(16, 100, 0, 8, 2, 64, "f32"))
 
 
 def test_workspace_size_and_shape_validation():
@@ -94,15 +111,31 @@ def test_other_calls_reject_bad_arguments_before_launch():
     with pytest.raises(M.MoEError) as e:
         M.moe_permute(p, None, FAKE, FAKE, FAKE, FAKE, ws, 0)
     assert e.value.status == M.MOE_ERR_INVALID_ARG
-    with pytest.raises(M.MoEError) as e:   # shared experts present but y_shared missing
-        M.moe_expert_ffn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, 0)
+    with pytest.raises(M.MoEError) as e:   # shared experts present but y_acc missing
+        M.moe_expert_ffn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
+                         ws, 0)
     assert e.value.status == M.MOE_ERR_INVALID_ARG
     with pytest.raises(M.MoEError) as e:
-        M.moe_expert_ffn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0)
+        M.moe_expert_ffn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                         0, 0)
     assert e.value.status == M.MOE_ERR_WORKSPACE
-    with pytest.raises(M.MoEError) as e:
+    for gate, slot in ((None, FAKE), (FAKE, None)):   # accumulating mode (y_routed NULL) needs gate and slot_of
+        with pytest.raises(M.MoEError) as e:
+            M.moe_expert_ffn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, gate, slot,
+                             FAKE, ws, 0)
+        assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:   # accumulating mode needs y_acc
+        M.moe_expert_ffn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, ws,
+                         0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:   # gather form without gates
         M.moe_combine(p, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0)
     assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoEError) as e:   # status of a workspace that is too small
+        st = M.moe_expert_ffn_status(p, FAKE, ws - 1, 0)
+        if st != M.MOE_OK:
+            raise M.MoEError("moe_expert_ffn_status", st)
+    assert e.value.status == M.MOE_ERR_WORKSPACE
     with pytest.raises(M.MoEError) as e:   # D does not divide N'
         M.moe_balance_stats(p, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
     assert e.value.status == M.MOE_ERR_INVALID_ARG

@@ -16,12 +16,13 @@ import parity as PT
 pytestmark = pytest.mark.gpu
 
 
-def run_case(inp: W.LayerInputs, sample: int = 0, tag: str = ""):
+def run_case(inp: W.LayerInputs, sample: int = 0, tag: str = "", accumulate: bool = False):
     wl = inp.wl
     PT.say(f"[case] {tag} {wl.name} T={wl.T} d={wl.d} Ks={wl.n_shared} Nr={wl.n_routed} K={wl.top_k} "
-           f"w={wl.inter} {wl.dtype} groups={wl.groups}")
-    dl = DeviceLayer(inp, want_probs=wl.T * wl.n_routed <= (1 << 24))
+           f"w={wl.inter} {wl.dtype} groups={wl.groups}" + (" accumulating" if accumulate else ""))
+    dl = DeviceLayer(inp, want_probs=wl.T * wl.n_routed <= (1 << 24), accumulate=accumulate)
     dl.forward()
+    dl.expert_sum()
     g = dl.results()
     o = PT.oracle_routing(inp)
     PT.check_routing(g, o, wl)
@@ -94,6 +95,7 @@ def test_shared_only_dense_layer():
     PT.say("[case] shared-only")
     dl = DeviceLayer(inp)
     dl.forward()
+    dl.expert_sum()
     g = dl.results()
     tokens = np.arange(300, dtype=np.int32)
     ref = PT.oracle_outputs(inp, np.zeros((300, 0), np.int32), np.zeros((300, 0), np.float32), tokens)
@@ -119,6 +121,7 @@ def test_permute_every_expert_active():
     gate = np.ones((T, 64), np.float32)
     dl = DeviceLayer(inp)
     dl.forward_with_routing(idx, gate)
+    dl.expert_sum()
     g = dl.results()
     from oracle import oracle as O
     p = O.permute(idx, 64)
@@ -158,8 +161,8 @@ def test_fused_ffn_equals_two_launches(case):
     dl.expert_ffn()
     a = dl.results()
     dl.y_routed.zero_()
-    if dl.y_shared is not None:
-        dl.y_shared.zero_()
+    if dl.y_acc is not None:
+        dl.y_acc.zero_()
     dl.expert_up()
     dl.expert_down()
     b = dl.results()

@@ -26,6 +26,7 @@ def check_layer_on(dl: DeviceLayer, inp: W.LayerInputs, o_route: dict, tag: str,
     dl.combine()
     if stats:
         dl.balance_stats()
+    dl.expert_sum()
     g = dl.results()
     assert np.array_equal(g["idx"], o_route["idx"]), "expert indices differ"
     assert np.array_equal(g["counts"], o_route["counts"]), "per-expert counts differ"

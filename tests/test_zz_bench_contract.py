@@ -42,5 +42,10 @@ def test_bench_json_line():
     assert roof["bound"] in ("hbm", "mfma", "alu") and roof["unit"] in ("GB/s", "TFLOP/s")
     assert roof["peak"] > 0 and 0 < roof["achieved"] and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert "traffic" in roof
+    assert roof["kernel"].startswith("grouped_ffn_kernel<float")
+    st = out["step_ms"]
+    assert st["reps"] >= 50 and 0 < st["min_ms"] <= st["median_ms"] <= st["max_ms"]
     cpu = out["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    assert cpu["usable_cpus"] >= 1 and "cpu_model" in cpu
+    assert cpu["c1_one_thread"]["threads"] == 1 and cpu["c1_one_thread"]["tokens_per_s"] > 0
