@@ -101,6 +101,24 @@ int moe_route(const moe_problem *p, const void *x, const float *centroids, const
     return moe_route_ablate(p, 0, x, centroids, bias, idx, gate, probs, counts, prob_sum, ws, ws_bytes, stream);
 }
 
+int moe_route_noalloc(const moe_problem *p, const void *x, const float *centroids, const float *bias, int32_t *idx,
+                      float *gate, float *probs, int32_t *counts, float *prob_sum, void *stream) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (p->n_routed < 1) return MOE_ERR_INVALID_ARG;
+    if (p->n_routed > kRouteMaxExperts || p->top_k > kRouteMaxTopK) return MOE_ERR_UNSUPPORTED;
+    if (!centroids || !counts || !prob_sum) return MOE_ERR_INVALID_ARG;
+    if (p->T > 0 && (!x || !idx || !gate)) return MOE_ERR_INVALID_ARG;
+    if ((x && !aligned16(x)) || !aligned16(centroids)) return MOE_ERR_INVALID_ARG;
+    if (route_partial_bytes(*p) > kRouteScratchBytes) return MOE_ERR_UNSUPPORTED;
+    void *sp = nullptr;
+    if (route_scratch_ptr(&sp) != hipSuccess) return MOE_ERR_HIP;
+    uint8_t *base = (uint8_t *)sp;
+    return hip_status(launch_route(*p, 0, x, centroids, bias, idx, gate, probs, (int32_t *)base,
+                                   (double *)(base + route_psum_offset(*p)), counts, prob_sum,
+                                   (hipStream_t)stream));
+}
+
 int moe_route_hash(const moe_problem *p, const int32_t *token_ids, int32_t *idx, float *gate, int32_t *counts,
                    void *stream) {
     int rc = check_problem(p);

@@ -82,6 +82,22 @@ hipError_t launch_route(const moe_problem &p, int skip, const void *x, const flo
                         int32_t *part_counts, double *part_psum,
                         int32_t *counts, float *prob_sum, hipStream_t s);
 
+// Allocation-free routing: bytes of the static device scratch that holds the
+// routing partials, and its address on the current device (taken once per
+// device).
+constexpr size_t kRouteScratchBytes = (size_t)4 << 20;
+hipError_t route_scratch_ptr(void **ptr);
+// Bytes of the routing partials (counts, then fp64 sums) for p, laid out as
+// in the workspace: counts at 0, sums at route_psum_offset(p).
+inline size_t route_psum_offset(const moe_problem &p) {
+    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T) : 0;
+    return align_up(rb * (size_t)p.n_routed * sizeof(int32_t), 256);
+}
+inline size_t route_partial_bytes(const moe_problem &p) {
+    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T) : 0;
+    return route_psum_offset(p) + rb * (size_t)p.n_routed * sizeof(double);
+}
+
 hipError_t launch_route_hash(const moe_problem &p, const int32_t *token_ids, int32_t *idx, float *gate,
                              int32_t *counts, hipStream_t s);
 

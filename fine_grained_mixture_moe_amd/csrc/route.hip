@@ -45,6 +45,7 @@
 // The per-expert counts and fp64 affinity sums run over the wave's tokens in
 // order, then over the 4 waves in order.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -723,6 +724,39 @@ void launch_route_typed(const moe_problem &p, int skip, int nblk, const void *x,
 }  // namespace
 
 int route_blocks(int T) { return cdiv(T, route_waves(T) * route_tokens_per_wave(T)); }
+
+// ---------------------------------------------------------------------------
+// Allocation-free routing (moe_route_noalloc): the per-workgroup partial
+// statistics live in a file-scope device array instead of the caller's
+// workspace.  Each device holds its own copy of the array until the process
+// ends; its device address is taken once per device with hipGetSymbolAddress
+// (the host-side name is only a stand-in and is never passed to a kernel).
+// Every call on a device shares that device's array: each routing workgroup
+// overwrites its own partials before the reduction reads them, so nothing
+// needs clearing, but calls that overlap in time on one device race.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t route_scratch_ptr(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = q;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_route(const moe_problem &p, int skip, const void *x, const float *centroids, const float *bias,
                         int32_t *idx, float *gate, float *probs, int32_t *part_counts, double *part_psum,

@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.moe_version.restype = ctypes.c_char_p
         L.moe_workspace_size.argtypes = [_pp, ctypes.POINTER(_sz)]
         L.moe_route.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_route_noalloc.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_permute.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_expert_ffn.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _sz, _vp]
@@ -74,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.moe_combine_backward.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_expert_ffn_backward.argtypes = [_pp] + [_vp] * 20 + [_sz, _vp]
         L.moe_route_backward.argtypes = [_pp, ctypes.c_int32, ctypes.c_float, ctypes.c_float] + [_vp] * 13 + [_sz, _vp]
-        for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_status",
+        for fn in ("moe_workspace_size", "moe_route", "moe_route_noalloc", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_status",
                    "moe_expert_up",
                    "moe_expert_down", "moe_combine", "moe_balance_stats", "moe_backward_workspace_size",
                    "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward", "moe_route_ablate",
@@ -122,6 +123,12 @@ def moe_route(p, x, centroids, bias, idx, gate, probs, counts, prob_sum, ws, ws_
     _check("moe_route", lib().moe_route(ctypes.byref(p), _ptr(x), _ptr(centroids), _ptr(bias), _ptr(idx),
                                         _ptr(gate), _ptr(probs), _ptr(counts), _ptr(prob_sum), _ptr(ws),
                                         ws_bytes, _stream(stream)))
+
+
+def moe_route_noalloc(p, x, centroids, bias, idx, gate, probs, counts, prob_sum, stream=None):
+    _check("moe_route_noalloc", lib().moe_route_noalloc(ctypes.byref(p), _ptr(x), _ptr(centroids), _ptr(bias),
+                                                        _ptr(idx), _ptr(gate), _ptr(probs), _ptr(counts),
+                                                        _ptr(prob_sum), _stream(stream)))
 
 
 def moe_route_ablate(p, disabled_top, x, centroids, bias, idx, gate, probs, counts, prob_sum, ws, ws_bytes,

@@ -125,6 +125,23 @@ int moe_route(const moe_problem *p, const void *x, const float *centroids,
               void *stream);
 
 /*
+ * moe_route_noalloc -- moe_route for callers that cannot allocate or manage
+ * a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as moe_route, without
+ * ws: the per-workgroup partial statistics live in a static device array of
+ * the library (4 MiB per GPU, held until the process ends; its address is
+ * looked up once per device, with that device current, on the first call).
+ * The call itself allocates nothing.  Problems whose partials need more
+ * than 4 MiB (ceil(T / tokens per routing workgroup) * N' * 12 bytes, about
+ * 43 K tokens at N' = 256) return MOE_ERR_UNSUPPORTED.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ */
+int moe_route_noalloc(const moe_problem *p, const void *x, const float *centroids,
+                      const float *bias, int32_t *idx, float *gate, float *probs,
+                      int32_t *counts, float *prob_sum, void *stream);
+
+/*
  * moe_route_ablate -- moe_route with each token's `disabled_top` highest
  * ranked routed experts disabled: the token takes the experts of ranks
  * disabled_top .. disabled_top+K'-1 in the order (z desc, r asc).  This is the
