@@ -652,6 +652,136 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
     }
 }
 
+// Decode batches (few tokens): one workgroup per token and NW = ceil(N'/64)
+// waves, wave w running the chains of experts 64w + lane.  Every lane's
+// chain is sequential in k (the fixed fma order), so with few tokens the
+// work is T*N' chains of d dependent fmas and the time is the chain length:
+// each chain should own a SIMD slot and never wait for operands.  The
+// centroid row of the lane's expert streams straight from global memory into
+// registers (a ring of NBUF chunks of CK values, NBUF-1 chunks in flight), so
+// no LDS bandwidth is shared between waves; the token row is converted to
+// fp32 once into LDS and each step's 4 values are read at one address by all
+// lanes (a broadcast), one chunk ahead.  The logits of the NW waves meet in
+// LDS and wave 0 runs the same softmax and Top-K' as the batched kernel.  The
+// partial statistics go to row `token` of the partials (nblk = T).
+constexpr int kRouteDecodeMaxD = 16384;
+template <int NW, bool XB>
+__global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int Nr, int K, int skip, const void *x,
+                                                               const float *__restrict__ E,
+                                                               const float *__restrict__ bias,
+                                                               int32_t *__restrict__ idx, float *__restrict__ gate,
+                                                               float *__restrict__ probs,
+                                                               int32_t *__restrict__ part_counts,
+                                                               double *__restrict__ part_psum) {
+    constexpr int CK = 32;          // k per chunk: 8 float4 per lane
+    constexpr int NQ = CK / 4;
+    constexpr int NBUF = 4;
+    extern __shared__ __attribute__((aligned(16))) float s_x[];   // [d], dynamic
+    __shared__ float s_z[NW * 64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t = blockIdx.x;
+    const int r = wave * 64 + lane;
+    const float4 *er = (const float4 *)(E + (size_t)min(r, Nr - 1) * d);   // absent experts repeat row N'-1
+    const int nch = d / CK;          // d % 64 == 0
+    float4 e0[NQ], e1[NQ], e2[NQ], e3[NQ], xc[NQ], xn[NQ];
+#define MOE_DLD(c, b)                                                         \
+    {                                                                         \
+        const float4 *p_ = er + (size_t)min((c), nch - 1) * NQ;               \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q) b[q] = p_[q];          \
+    }
+#define MOE_XRD(c, b)                                                         \
+    {                                                                         \
+        const float *p_ = s_x + min((c), nch - 1) * CK;                       \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q) b[q] = *(const float4 *)(p_ + 4 * q); \
+    }
+    // the token row, as fp32, into LDS: the first batch of its 16-byte pieces
+    // is loaded before the first centroid chunks go out (loads complete in
+    // order, so the stores wait for the token pieces only), further batches
+    // (long rows) afterwards
+    {
+        constexpr int NT = NW * 64, SB = 8;
+        const int n16 = d * (XB ? 2 : 4) / 16;     // 16-byte pieces of the row
+        const uint4 *xr = (const uint4 *)((const uint8_t *)x + (size_t)t * d * (XB ? 2 : 4));
+        auto put = [&](int i, const uint4 v) {
+            if constexpr (XB) {
+                *(float4 *)(s_x + 8 * i) = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                                                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+                *(float4 *)(s_x + 8 * i + 4) =
+                    make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
+                                __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+            } else {
+                *(uint4 *)(s_x + 4 * i) = v;
+            }
+        };
+        uint4 v[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+            if (tid + u * NT < n16) v[u] = xr[tid + u * NT];
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_DLD(0, e0)
+        MOE_DLD(1, e1)
+        MOE_DLD(2, e2)
+        MOE_DLD(3, e3)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+            if (tid + u * NT < n16) put(tid + u * NT, v[u]);
+        for (int i = tid + SB * NT; i < n16; i += NT) put(i, xr[i]);
+    }
+    __syncthreads();
+    MOE_XRD(0, xc)
+    float acc = 0.0f;
+    // one chunk: the next chunk's token values are read from LDS first, then
+    // this chunk's fmas in k order, then the register set is refilled with
+    // the chunk NBUF ahead; the empty asm orders the phases
+#define MOE_DSTEP(c, b)                                                        \
+    {                                                                          \
+        MOE_XRD((c) + 1, xn)                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                     \
+        if ((c) < nch) {                                                       \
+            _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                   \
+                acc = __builtin_fmaf(xc[q].x, b[q].x, acc);                    \
+                acc = __builtin_fmaf(xc[q].y, b[q].y, acc);                    \
+                acc = __builtin_fmaf(xc[q].z, b[q].z, acc);                    \
+                acc = __builtin_fmaf(xc[q].w, b[q].w, acc);                    \
+            }                                                                  \
+        }                                                                      \
+        asm volatile("" : "+v"(acc));                                          \
+        __builtin_amdgcn_sched_barrier(0);                                     \
+        MOE_DLD((c) + NBUF, b)                                                 \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q) xc[q] = xn[q];          \
+    }
+    for (int c = 0; c < nch; c += NBUF) {
+        MOE_DSTEP(c, e0)
+        MOE_DSTEP(c + 1, e1)
+        MOE_DSTEP(c + 2, e2)
+        MOE_DSTEP(c + 3, e3)
+    }
+#undef MOE_DSTEP
+#undef MOE_DLD
+#undef MOE_XRD
+    s_z[r] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    float z[1][NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) z[0][j] = s_z[lane + 64 * j];
+    double ps[NW];
+    int cnt[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) { ps[j] = 0.0; cnt[j] = 0; }
+    finish_tokens<1, NW>(t, 1, Nr, K, skip, lane, z, bias, idx, gate, probs, ps, cnt);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        const int rr = lane + 64 * j;
+        if (rr < Nr) {
+            part_psum[(size_t)t * Nr + rr] = ps[j];
+            part_counts[(size_t)t * Nr + rr] = cnt[j];
+        }
+    }
+}
+
 // One workgroup per expert: counts[r] = sum_b part_counts[b, r],
 // prob_sum[r] = sum_b part_psum[b, r] in fp64: strided per-thread sums, a
 // butterfly within each wave, then the 4 wave sums in order (fixed order).
@@ -688,6 +818,23 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(
 // two waves per SIMD).
 int route_waves(int T) { return T >= 2048 ? 8 : 4; }
 int route_tokens_per_wave(int T) { return T >= 8192 ? 4 : T >= 4096 ? 2 : 1; }
+// Batches of at most this many tokens take the decode kernel (one workgroup per token).
+constexpr int kRouteDecodeTokens = 256;
+bool route_decode_path(int T, int d) { return T <= kRouteDecodeTokens && d <= kRouteDecodeMaxD; }
+
+template <bool XB>
+void launch_route_decode(const moe_problem &p, int skip, const void *x, const float *E, const float *bias,
+                         int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
+#define MOE_L(NW) route_decode_kernel<NW, XB><<<p.T, NW * 64, (size_t)p.d * sizeof(float), s>>>( \
+        p.T, p.d, p.n_routed, p.top_k, skip, x, E, bias, idx, gate, probs, pc, pp)
+    switch (cdiv(p.n_routed, 64)) {
+        case 1: MOE_L(1); break;
+        case 2: MOE_L(2); break;
+        case 3: MOE_L(3); break;
+        default: MOE_L(4); break;
+    }
+#undef MOE_L
+}
 
 template <int RT, int W, bool XB>
 void launch_rtw(const moe_problem &p, int skip, int nblk, const void *x, const float *E, const float *bias,
@@ -723,7 +870,9 @@ void launch_route_typed(const moe_problem &p, int skip, int nblk, const void *x,
 
 }  // namespace
 
-int route_blocks(int T) { return cdiv(T, route_waves(T) * route_tokens_per_wave(T)); }
+int route_blocks(int T, int d) {
+    return route_decode_path(T, d) ? T : cdiv(T, route_waves(T) * route_tokens_per_wave(T));
+}
 
 // ---------------------------------------------------------------------------
 // Allocation-free routing (moe_route_noalloc): the per-workgroup partial
@@ -761,13 +910,19 @@ hipError_t route_scratch_ptr(void **ptr) {
 hipError_t launch_route(const moe_problem &p, int skip, const void *x, const float *centroids, const float *bias,
                         int32_t *idx, float *gate, float *probs, int32_t *part_counts, double *part_psum,
                         int32_t *counts, float *prob_sum, hipStream_t s) {
-    const int nblk = p.T > 0 ? route_blocks(p.T) : 0;
+    const int nblk = p.T > 0 ? route_blocks(p.T, p.d) : 0;
     if (nblk > 0) {
-        if (p.dtype == MOE_BF16)
+        if (route_decode_path(p.T, p.d)) {
+            if (p.dtype == MOE_BF16)
+                launch_route_decode<true>(p, skip, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
+            else
+                launch_route_decode<false>(p, skip, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
+        } else if (p.dtype == MOE_BF16) {
             launch_route_typed<true>(p, skip, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
-        else
+        } else {
             launch_route_typed<false>(p, skip, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum,
                                       s);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -51,6 +51,7 @@ ABLATE = [
     (5000, 64, 0, 256, 8, 64, "bf16", 34, 1.1, 8, 8),     # disabled + K' = 16, N' = 256
     (16400, 192, 0, 32, 4, 64, "f32", 35, None, 4, 2),    # 4 tokens per wave, ragged T
     (200, 128, 0, 12, 2, 64, "f32", 36, None, 3, 10),     # disabled + K' = N': the two lowest-ranked experts
+    (96, 1024, 1, 128, 6, 64, "bf16", 37, None, 4, 4),    # decode routing kernel (two waves per token)
 ]
 
 
