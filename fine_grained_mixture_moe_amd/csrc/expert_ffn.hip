@@ -75,6 +75,7 @@ __device__ __forceinline__ void mfma_k16(f32x16 &acc, const uint8_t *a, const ui
 
 struct GemmParams {
     int T, d, Ks, Nr, w;
+    int TK;                      // T*K': rows of the routed grouped arrays
     const int32_t *offsets;
     const int32_t *sorted_token;
     const uint8_t *x;            // up: [T, d]
@@ -328,9 +329,14 @@ constexpr uint32_t kOOB = 0x80000000u;   // offset beyond any buffer: reads as z
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
-// Cache policy of the loads and stores that carry data between workgroups of
-// one launch: sc1, the agent-coherent form (what the compiler emits for
-// relaxed agent-scope atomic loads and stores), visible across the XCDs' L2s.
+// Cache policy of the stores that carry data between workgroups of one
+// launch: sc1, the agent-coherent form (what the compiler emits for relaxed
+// agent-scope atomic stores), written through to memory so that every XCD
+// sees it.  The reads of that data are ordinary cached loads: a reading XCD's
+// L2 cannot hold an older copy of those lines (the kernel launch starts with
+// the L2s invalidated, and within the launch the lines are read only after
+// they are written), so the first read on an XCD fetches the written data
+// and the later ones hit in that L2.
 constexpr int kCoherent = 16;
 constexpr int kNonTemporal = 2;   // nt: a streaming access
 template <int AUX = 0>
@@ -348,7 +354,7 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // One tile of the bf16 grouped GEMM: rows [m0, m0+nr) of a group (the
 // shared experts, or routed expert r) against weight tile n_tile.  FUSED:
 // the tile runs inside the fused up+down launch, whose activations pass
-// between workgroups through agent-coherent stores and loads.
+// between workgroups through agent-coherent stores (read back as cached loads).
 struct TileDesc {
     bool shared;
     int r, row_off, m0, nr, n_tile;
@@ -405,7 +411,11 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
         rw_a = make_rsrc(b2, (uint32_t)(shared ? (size_t)P.Ks * ebytes : ebytes));
         rw_b = rw_a;
         const uint8_t *xb = shared ? P.act_shared : P.act_routed;
-        const size_t xrows = shared ? (size_t)P.T : (size_t)(P.offsets[P.Nr]);
+        // the routed activations' region holds T*K' rows (a bound known without a
+        // load: read from memory, the descriptor was built from a vector register,
+        // every buffer load got a waterfall loop, and the k loop's first wait covered
+        // that load's register)
+        const size_t xrows = shared ? (size_t)P.T : (size_t)P.TK;
         rx = make_rsrc(xb, (uint32_t)(xrows * xpitch));
     }
 #pragma unroll
@@ -422,18 +432,49 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
     const int swz = part ^ (rsub & 7) ^ ((rsub >> 3) & 1);
 
     uint4 sw[CW], sx[CX];
-    auto kw_of = [&](int kt) -> uint32_t {
-        if (!UP && shared) {
-            // W2 of the shared experts: k runs over K_s segments [d, w]
-            const int k_el = kt * 64;
-            const int seg = k_el / P.w;
-            return (uint32_t)(((size_t)seg * P.d * P.w + (k_el - seg * P.w)) * 2);
+    // Byte offsets of k step kt in the weight rows and the token rows.  In the
+    // down projection of the shared experts, k runs over the K_s segments
+    // [d, w] of the stacked W2, w/64 steps per segment.  The k loop advances
+    // them by one step at a time (a scalar add, and a segment jump every w/64
+    // steps); a division per step, if-converted by the compiler into every
+    // down tile, cost the down k loop about 80 scalar instructions per step
+    // and wave on the CU's one scalar unit.
+    const bool segd = !UP && shared;
+    const int spw = P.w / 64;
+    const uint32_t sstr = (uint32_t)((size_t)P.d * P.w * 2);
+    struct KOff {
+        uint32_t kw, kx, kseg;
+        int kin;
+    };
+    auto koff = [&](int kt) -> KOff {
+        KOff o;
+        o.kx = (uint32_t)kt * RB;
+        if (segd) {
+            o.kseg = (uint32_t)(kt / spw) * sstr;
+            o.kin = kt % spw;
+            o.kw = o.kseg + (uint32_t)o.kin * RB;
+        } else {
+            o.kseg = 0;
+            o.kin = 0;
+            o.kw = o.kx;
         }
-        return (uint32_t)kt * RB;
+        return o;
+    };
+    auto kadvance = [&](KOff &o) {
+        o.kx += RB;
+        if (segd) {
+            if (++o.kin == spw) {
+                o.kin = 0;
+                o.kseg += sstr;
+            }
+            o.kw = o.kseg + (uint32_t)o.kin * RB;
+        } else {
+            o.kw = o.kx;
+        }
     };
     // part ph (0..3) of a k step: weight chunks [ph*CW/4, (ph+1)*CW/4), token chunks likewise
-    auto gload_part = [&](int kt, int ph, bool wts = true, bool toks = true) {
-        const uint32_t kw = kw_of(kt), kx = (uint32_t)kt * RB;
+    auto gload_part = [&](const KOff &o, int ph, bool wts = true, bool toks = true) {
+        const uint32_t kw = o.kw, kx = o.kx;
         if (wts) {
 #pragma unroll
             for (int i = 0; i < CW; ++i)
@@ -442,7 +483,7 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
         if (toks) {
 #pragma unroll
             for (int i = 0; i < CX; ++i)
-                if (i * 4 / CX == ph) sx[i] = bload<(FUSED && !UP) ? kCoherent : 0>(rx, ox[i], kx);
+                if (i * 4 / CX == ph) sx[i] = bload<0>(rx, ox[i], kx);
         }
     };
     auto sstore_part = [&](int stg, int ph) {
@@ -508,8 +549,9 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
         // the weight rows of step 0 depend on the tile alone: their loads go
         // out before the token sources are gathered (for the up projection a
         // dependent global read), so the two latencies overlap
+        const KOff k0 = koff(0);
 #pragma unroll
-        for (int ph = 0; ph < 4; ++ph) gload_part(0, ph, true, false);
+        for (int ph = 0; ph < 4; ++ph) gload_part(k0, ph, true, false);
         if (tid < BM) {
             const int row = m0 + tid;
             int src = -1;
@@ -526,35 +568,48 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
             ox[i] = src >= 0 ? (uint32_t)src * xpitch + part * 16 : kOOB;
         }
 #pragma unroll
-        for (int ph = 0; ph < 4; ++ph) gload_part(0, ph, false, true);
+        for (int ph = 0; ph < 4; ++ph) gload_part(k0, ph, false, true);
 #pragma unroll
         for (int ph = 0; ph < 4; ++ph) sstore_part(0, ph);
         __syncthreads();
-        if (nk > 1)
-#pragma unroll
-            for (int ph = 0; ph < 4; ++ph) gload_part(1, ph);
         // MORE: step kt+1 exists (store it), MORE2: step kt+2 exists (load it)
         auto kloop = [&](auto ml_t) {
+            // The loads of step 1 go out here, in each variant of the loop (one per count of
+            // live token blocks), in the loop's own order (weights and tokens of each quarter
+            // in turn): issued once before the variants, into registers the variants then
+            // assigned differently, they left the full-tile loop waiting at its head for
+            // nearly all loads in flight, every step.
+            if (nk > 1) {
+                const KOff k1 = koff(1);
+#pragma unroll
+                for (int ph = 0; ph < 4; ++ph) {
+                    gload_part(k1, ph);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // offsets of the step whose loads go out next (kt + 2 in the loop)
+            KOff kn = koff(2);
             auto kstep = [&](int kt, auto more_t, auto more2_t) {
                 constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
                 const int st = kt & 1;
                 bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
                 frags(ml_t, st, 0, fa0, fb0);
                 frags(ml_t, st, 1, fa1, fb1);
-                if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kt + 2, 0); }
+                if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kn, 0); }
                 __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
                 mma(ml_t, fa0, fb0);
                 frags(ml_t, st, 2, fa0, fb0);
-                if (MORE) { sstore_part(st ^ 1, 1); if (MORE2) gload_part(kt + 2, 1); }
+                if (MORE) { sstore_part(st ^ 1, 1); if (MORE2) gload_part(kn, 1); }
                 __builtin_amdgcn_sched_barrier(0);
                 mma(ml_t, fa1, fb1);
                 frags(ml_t, st, 3, fa1, fb1);
-                if (MORE) { sstore_part(st ^ 1, 2); if (MORE2) gload_part(kt + 2, 2); }
+                if (MORE) { sstore_part(st ^ 1, 2); if (MORE2) gload_part(kn, 2); }
                 __builtin_amdgcn_sched_barrier(0);
                 mma(ml_t, fa0, fb0);
-                if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kt + 2, 3); }
+                if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kn, 3); }
                 __builtin_amdgcn_sched_barrier(0);
                 mma(ml_t, fa1, fb1);
+                if (MORE2) kadvance(kn);
                 __syncthreads();
             };
             int kt = 0;
@@ -873,12 +928,14 @@ __global__ __launch_bounds__(512) void grouped_ffn_bf16_kernel(GemmParams P) {
 //   * a token run is one of the mt equal row runs of a group (as in the
 //     separate kernels); its up tiles write the run's activations, its down
 //     tiles read them;
-//   * the runs are split into kQueues contiguous ranges, one queue per XCD
-//     (workgroup b starts on queue b % 8, the XCD the hardware gives it), so
-//     the tiles of one expert stay on one XCD and share its L2;
+//   * the runs are split into kQueues contiguous ranges of equal work, one
+//     queue per XCD (workgroup b starts on queue b % 8, the XCD the hardware
+//     gives it), so the tiles of one expert stay on one XCD and share its L2;
 //   * inside a queue, tickets are taken in order from an atomic counter: all
-//     up tiles of the queue's runs (run-major), then all its down tiles; a
-//     workgroup whose queue is empty takes tickets from the other queues;
+//     up tiles of the queue's runs (the shared runs in blocks of a few runs,
+//     weight-tile-major; the routed runs run-major), then all its down tiles
+//     in the same order; a workgroup whose queue is empty takes tickets from
+//     the other queues;
 //   * a down tile waits until the up tiles of its run are done (a per-run
 //     counter, bumped after the tile's coherent activation stores complete).
 // No wait can deadlock: a ticket is only ever held by a running workgroup,
@@ -967,29 +1024,63 @@ __global__ __launch_bounds__(512) void grouped_ffn_fused_kernel(GemmParams Pu, G
     const int mts = P.Ks > 0 ? uni(s_runp[1]) : 0;                  // runs of the shared group
     const int nus = cdiv(P.Ks * P.w, 128), nur = cdiv(P.w, 128);    // up tiles per run
     const int nd = cdiv(P.d, 256);                                  // down tiles per run
-    auto upp = [&](int r) { return r * nur + min(r, mts) * (nus - nur); };   // up tiles before run r
+    // Queue q serves the runs [qstart(q), qstart(q+1)): equal shares of the work, counted in
+    // 64-wide k steps (a shared run, of width K_s*w, weighs more than a routed one), so the
+    // queues drain together and few tiles leave their XCD.
+    const int64_t ws = (int64_t)nus * (P.d / 64) + (int64_t)nd * (P.Ks * P.w / 64);
+    const int64_t wr = (int64_t)nur * (P.d / 64) + (int64_t)nd * (P.w / 64);
+    const int64_t wtot = (int64_t)mts * ws + (int64_t)(R - mts) * wr;
+    auto qstart = [&](int q) -> int {
+        const int64_t tau = wtot * q / kQueues;
+        int r;
+        if (mts > 0 && tau <= (int64_t)mts * ws) r = (int)((tau + ws - 1) / ws);
+        else r = mts + (int)((tau - (int64_t)mts * ws + wr - 1) / wr);
+        return q >= kQueues ? R : min(r, R);
+    };
+    // The shared runs of a queue go in blocks of kShBlock runs, each block weight-tile-major
+    // (tile n of every run of the block, then tile n+1): the workgroups of one XCD then work on a
+    // few runs and a few weight tiles at a time and share both in L2, where run-major order
+    // streamed the whole shared weight stack once per run.  l counts the tiles of the queue's
+    // shared runs [s0, s1), `per` tiles per run.
+    constexpr int kShBlock = 4;
+    auto blocked = [&](int l, int s0, int s1, int per, int &run, int &n) {
+        const int j = l / (kShBlock * per);
+        const int b0 = s0 + j * kShBlock;
+        const int bsz = min(kShBlock, s1 - b0);
+        const int lo = l - j * kShBlock * per;
+        n = lo / bsz;
+        run = b0 + lo % bsz;
+    };
 
     const int q0 = blockIdx.x % kQueues;
     for (int qi = 0; qi < kQueues; ++qi) {
         const int q = (q0 + qi) % kQueues;
-        const int ra = (int)((int64_t)R * q / kQueues), rb = (int)((int64_t)R * (q + 1) / kQueues);
-        const int u0 = upp(ra), nU = upp(rb) - u0;
-        const int len = nU + (rb - ra) * nd;
+        const int ra = qstart(q), rb = qstart(q + 1);
+        const int se = min(rb, mts), rs = max(ra, mts);    // shared runs [ra, se), routed runs [rs, rb)
+        const int nsh = max(se - ra, 0), nro = max(rb - rs, 0);
+        const int nUs = nsh * nus, nU = nUs + nro * nur, nDs = nsh * nd;
+        const int len = nU + (nsh + nro) * nd;
         if (len == 0) continue;
         if (tid == 0) s_ticket = atomicAdd(&C.head[q], 1);
         __syncthreads();
         int t = uni(s_ticket);
         __syncthreads();   // every wave has read the ticket before it is rewritten
         while (t < len) {
+            // tickets: the up tiles (shared blocks, then routed runs run-major), then the down
+            // tiles in the same order
             const bool up = t < nU;
             int run, n;
-            if (up) {
-                const int u = u0 + t;
-                if (u < mts * nus) { run = u / nus; n = u % nus; }
-                else { const int v = u - mts * nus; run = mts + v / nur; n = v % nur; }
+            if (t < nUs) {
+                blocked(t, ra, se, nus, run, n);
+            } else if (up) {
+                const int v = t - nUs;
+                run = rs + v / nur;
+                n = v % nur;
+            } else if (t < nU + nDs) {
+                blocked(t - nU, ra, se, nd, run, n);
             } else {
-                const int v = t - nU;
-                run = ra + v / nd;
+                const int v = t - nU - nDs;
+                run = rs + v / nd;
                 n = v % nd;
             }
             // group of the run: the number of prefix entries s_runp[1..G] <= run,
@@ -1072,6 +1163,7 @@ __global__ __launch_bounds__(256) void ffn_prep_kernel(int *ctl, int n, float *y
 GemmParams make_params(const moe_problem &p, const FfnArgs &a, bool up) {
     GemmParams P{};
     P.T = p.T; P.d = p.d; P.Ks = p.n_shared; P.Nr = p.n_routed; P.w = p.inter;
+    P.TK = p.T * p.top_k;
     P.offsets = a.offsets;
     P.sorted_token = a.sorted_token;
     P.x = (const uint8_t *)a.x;

@@ -656,15 +656,25 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
 // waves, wave w running the chains of experts 64w + lane.  Every lane's
 // chain is sequential in k (the fixed fma order), so with few tokens the
 // work is T*N' chains of d dependent fmas and the time is the chain length:
-// each chain should own a SIMD slot and never wait for operands.  The
-// centroid row of the lane's expert streams straight from global memory into
-// registers (a ring of NBUF chunks of CK values, NBUF-1 chunks in flight), so
-// no LDS bandwidth is shared between waves; the token row is converted to
-// fp32 once into LDS and each step's 4 values are read at one address by all
-// lanes (a broadcast), one chunk ahead.  The logits of the NW waves meet in
-// LDS and wave 0 runs the same softmax and Top-K' as the batched kernel.  The
-// partial statistics go to row `token` of the partials (nblk = T).
+// each chain should own a SIMD slot and never wait for operands.
+//   * Centroids: each wave streams its 64 expert rows in chunks of CK = 32 k
+//     (8 KB).  A chunk is loaded with row-contiguous 16-byte pieces (one
+//     load instruction covers 8 whole 128-byte row segments, so the vector
+//     cache sees 8 lines per instruction instead of 64 for a lane-per-row
+//     load), kept NBUF - 1 chunks ahead in a ring of registers, and passed
+//     through a private two-stage LDS buffer of the wave, rows 144 bytes
+//     apart, from which each lane reads its own row (16 lanes of a read hit
+//     16 distinct 4-bank groups).  The stages belong to one wave, whose LDS
+//     operations run in order, so no barrier is needed.
+//   * Token: the row is converted to fp32 once into LDS and each step's 4
+//     values are read at one address by all lanes (a broadcast).
+// The logits of the NW waves meet in LDS and wave 0 runs the same softmax
+// and Top-K' as the batched kernel.  The partial statistics go to row
+// `token` of the partials (nblk = T).
 constexpr int kRouteDecodeMaxD = 16384;
+constexpr int kDecodeCK = 32;                       // k per chunk
+constexpr int kDecodePitch = kDecodeCK * 4 + 16;    // LDS row pitch (bytes)
+constexpr int kDecodeStage = 64 * kDecodePitch;     // one chunk of one wave
 template <int NW, bool XB>
 __global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int Nr, int K, int skip, const void *x,
                                                                const float *__restrict__ E,
@@ -673,28 +683,37 @@ __global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int
                                                                float *__restrict__ probs,
                                                                int32_t *__restrict__ part_counts,
                                                                double *__restrict__ part_psum) {
-    constexpr int CK = 32;          // k per chunk: 8 float4 per lane
-    constexpr int NQ = CK / 4;
-    constexpr int NBUF = 4;
-    extern __shared__ __attribute__((aligned(16))) float s_x[];   // [d], dynamic
+    constexpr int CK = kDecodeCK;
+    constexpr int NQ = CK / 4;       // 16-byte pieces of a row segment; also load instructions per chunk
+    // dynamic LDS: [NW waves][2 stages][64 rows][kDecodePitch bytes], then the token row [d] fp32
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
     __shared__ float s_z[NW * 64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = blockIdx.x;
-    const int r = wave * 64 + lane;
-    const float4 *er = (const float4 *)(E + (size_t)min(r, Nr - 1) * d);   // absent experts repeat row N'-1
+    float *s_x = (float *)(s_dyn + NW * 2 * kDecodeStage);
+    uint8_t *stg0 = s_dyn + wave * 2 * kDecodeStage;
     const int nch = d / CK;          // d % 64 == 0
-    float4 e0[NQ], e1[NQ], e2[NQ], e3[NQ], xc[NQ], xn[NQ];
-#define MOE_DLD(c, b)                                                         \
-    {                                                                         \
-        const float4 *p_ = er + (size_t)min((c), nch - 1) * NQ;               \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q) b[q] = p_[q];          \
-    }
-#define MOE_XRD(c, b)                                                         \
-    {                                                                         \
-        const float *p_ = s_x + min((c), nch - 1) * CK;                       \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q) b[q] = *(const float4 *)(p_ + 4 * q); \
-    }
+    // load piece (lane & 7) of row 8i + (lane >> 3) of the wave's 64 rows: rows past N' repeat row N'-1
+    const int prow = lane >> 3, ppc = lane & 7;
+    // (a native vector type: copies of the HIP uint4 struct become memcpys that
+    // kept the ring in scratch memory)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 r0[NQ], r1[NQ], r2[NQ], r3[NQ];
+    auto dld = [&](int c, u32x4 (&b)[NQ]) {
+        const int o = min(c, nch - 1) * CK + 4 * ppc;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i)
+            b[i] = *(const u32x4 *)(E + (size_t)min(wave * 64 + 8 * i + prow, Nr - 1) * d + o);
+    };
+    uint8_t *const dst0 = stg0 + prow * kDecodePitch + ppc * 16;
+    auto dst = [&](int stg, const u32x4 (&b)[NQ]) {
+        uint8_t *dd = dst0 + stg * kDecodeStage;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) *(u32x4 *)(dd + 8 * i * kDecodePitch) = b[i];
+    };
+#define MOE_DLD(c, b) dld((c), b);
+#define MOE_DST(stg, b) dst((stg), b);
     // the token row, as fp32, into LDS: the first batch of its 16-byte pieces
     // is loaded before the first centroid chunks go out (loads complete in
     // order, so the stores wait for the token pieces only), further batches
@@ -719,49 +738,61 @@ __global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int
         for (int u = 0; u < SB; ++u)
             if (tid + u * NT < n16) v[u] = xr[tid + u * NT];
         __builtin_amdgcn_sched_barrier(0);
-        MOE_DLD(0, e0)
-        MOE_DLD(1, e1)
-        MOE_DLD(2, e2)
-        MOE_DLD(3, e3)
+        MOE_DLD(0, r0)
+        MOE_DLD(1, r1)
+        MOE_DLD(2, r2)
+        MOE_DLD(3, r3)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < SB; ++u)
             if (tid + u * NT < n16) put(tid + u * NT, v[u]);
         for (int i = tid + SB * NT; i < n16; i += NT) put(i, xr[i]);
     }
+    MOE_DST(0, r0)
     __syncthreads();
-    MOE_XRD(0, xc)
     float acc = 0.0f;
-    // one chunk: the next chunk's token values are read from LDS first, then
-    // this chunk's fmas in k order, then the register set is refilled with
-    // the chunk NBUF ahead; the empty asm orders the phases
-#define MOE_DSTEP(c, b)                                                        \
-    {                                                                          \
-        MOE_XRD((c) + 1, xn)                                                   \
-        __builtin_amdgcn_sched_barrier(0);                                     \
-        if ((c) < nch) {                                                       \
-            _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                   \
-                acc = __builtin_fmaf(xc[q].x, b[q].x, acc);                    \
-                acc = __builtin_fmaf(xc[q].y, b[q].y, acc);                    \
-                acc = __builtin_fmaf(xc[q].z, b[q].z, acc);                    \
-                acc = __builtin_fmaf(xc[q].w, b[q].w, acc);                    \
-            }                                                                  \
-        }                                                                      \
-        asm volatile("" : "+v"(acc));                                          \
-        __builtin_amdgcn_sched_barrier(0);                                     \
-        MOE_DLD((c) + NBUF, b)                                                 \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q) xc[q] = xn[q];          \
+    // chunk c: stage c & 1 holds it; the ring register set (c+1) % 4 holds
+    // chunk c+1, the others chunks c+2, c+3; the free set takes chunk c+4.
+    // The lane's row of the chunk and the token values are read from LDS,
+    // the fmas run in k order, then chunk c+1 goes to the other stage.
+    const uint8_t *myrow = stg0 + lane * kDecodePitch;
+    auto chunk = [&](int c) {
+        float4 e[NQ], xv[NQ];
+        const uint8_t *er = myrow + (c & 1) * kDecodeStage;
+        const float *xs = s_x + c * CK;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            e[q] = *(const float4 *)(er + 16 * q);
+            xv[q] = *(const float4 *)(xs + 4 * q);
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            acc = __builtin_fmaf(xv[q].x, e[q].x, acc);
+            acc = __builtin_fmaf(xv[q].y, e[q].y, acc);
+            acc = __builtin_fmaf(xv[q].z, e[q].z, acc);
+            acc = __builtin_fmaf(xv[q].w, e[q].w, acc);
+        }
+    };
+#define MOE_DSTEP(c, cur, nxt)                          \
+    {                                                   \
+        MOE_DLD((c) + 4, cur)                           \
+        __builtin_amdgcn_sched_barrier(0);              \
+        if ((c) < nch) chunk(c);                        \
+        asm volatile("" : "+v"(acc));                   \
+        __builtin_amdgcn_sched_barrier(0);              \
+        MOE_DST(((c) + 1) & 1, nxt)                     \
+        __builtin_amdgcn_sched_barrier(0);              \
     }
-    for (int c = 0; c < nch; c += NBUF) {
-        MOE_DSTEP(c, e0)
-        MOE_DSTEP(c + 1, e1)
-        MOE_DSTEP(c + 2, e2)
-        MOE_DSTEP(c + 3, e3)
+    for (int c = 0; c < nch; c += 4) {
+        MOE_DSTEP(c, r0, r1)
+        MOE_DSTEP(c + 1, r1, r2)
+        MOE_DSTEP(c + 2, r2, r3)
+        MOE_DSTEP(c + 3, r3, r0)
     }
 #undef MOE_DSTEP
 #undef MOE_DLD
-#undef MOE_XRD
-    s_z[r] = acc;
+#undef MOE_DST
+    s_z[wave * 64 + lane] = acc;
     __syncthreads();
     if (wave != 0) return;
     float z[1][NW];
@@ -825,7 +856,7 @@ bool route_decode_path(int T, int d) { return T <= kRouteDecodeTokens && d <= kR
 template <bool XB>
 void launch_route_decode(const moe_problem &p, int skip, const void *x, const float *E, const float *bias,
                          int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
-#define MOE_L(NW) route_decode_kernel<NW, XB><<<p.T, NW * 64, (size_t)p.d * sizeof(float), s>>>( \
+#define MOE_L(NW) route_decode_kernel<NW, XB><<<p.T, NW * 64, (size_t)NW * 2 * kDecodeStage + (size_t)p.d * sizeof(float), s>>>( \
         p.T, p.d, p.n_routed, p.top_k, skip, x, E, bias, idx, gate, probs, pc, pp)
     switch (cdiv(p.n_routed, 64)) {
         case 1: MOE_L(1); break;
