@@ -355,7 +355,7 @@ int moe_expert_ffn_backward(const moe_problem *p, const void *x, const int32_t *
     a.w1_s = w1_shared; a.w3_s = w3_shared; a.w2_s = w2_shared;
     a.da_r = at(ws, L.da_r); a.dp_r = at(ws, L.dp_r); a.dq_r = at(ws, L.dq_r); a.a_r = at(ws, L.a_r);
     a.da_s = at(ws, L.da_s); a.dp_s = at(ws, L.dp_s); a.dq_s = at(ws, L.dq_s); a.a_s = at(ws, L.a_s);
-    a.dxr = (float *)at(ws, L.dxr); a.dxs = (float *)at(ws, L.dxs); a.dx_ffn = dx_ffn;
+    a.dxr = at(ws, L.dxr); a.dxs = (float *)at(ws, L.dxs); a.dx_ffn = dx_ffn;
     a.dw1_r = dw1_routed; a.dw3_r = dw3_routed; a.dw2_r = dw2_routed;
     a.dw1_s = dw1_shared; a.dw3_s = dw3_shared; a.dw2_s = dw2_shared;
     return hip_status(launch_expert_backward(*p, a, (hipStream_t)stream));

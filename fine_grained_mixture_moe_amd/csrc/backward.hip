@@ -15,18 +15,21 @@
 //
 // Kernels:
 //   combine_bwd_kernel   dy rows (gate * dh) and dgate (dot products), one wave per token
-//   bgemm_kernel<MODE>   one grouped GEMM on MFMA for the five products below
+//   grouped GEMMs on MFMA, five products (MODE):
 //      0  da   = dy . W2              (A rows k-contiguous, B = W2 read transposed)
-//      1  dxr  = dp . W1 + dq . W3    (A k-contiguous, B transposed)
+//      1  dxr  = dp . W1 + dq . W3    (A k-contiguous, B transposed; rows in the
+//                                      layer dtype, as the forward's y_routed)
 //      2  dW2  = dy^T . a             (A and B transposed; k runs over the group's rows)
 //      3  dW13 = [dp|dq]^T . x        (A and B transposed; x rows gathered)
 //      4  p, q = x . [W1;W3]^T, then the SwiGLU backward in the epilogue:
 //         reads da, writes dp, dq and a (A and B k-contiguous); fp32 layers
 //         only: bf16 layers recompute p, q on the forward up kernel with its
 //         backward epilogue (expert_ffn.hip)
-//      bf16 operands come in through raw buffer loads whose offsets are fixed
-//      per tile (a chunk out of range reads zeros), and the tile order is
-//      XCD-aware (see the kernel)
+//   bgemm_wide_kernel    bf16 modes 0-3 on 256 x 256 tiles (8 waves, two LDS
+//                        stages, raw buffer loads whose offsets are fixed per
+//                        tile, an LDS-staged epilogue)
+//   bgemm_kernel<MODE>   fp32 layers: all five modes on 128 x 128 tiles
+//   (both with an XCD-aware tile order, see bgemm_kernel)
 //   gather_dx_kernel     dx_ffn[t] = dxs[t] + sum_k dxr[slot_of[t,k]] (k order)
 //   router_dz_kernel     ds, dz per token (wave per token, lane = expert)
 //   router_dx_kernel     dx = dh + dx_ffn + dz E (LDS-tiled, 64 tokens x 64 columns)
@@ -171,7 +174,8 @@ struct BgArgs {
     void *da_r, *da_s;                   // [T*K', w], [T, K_s*w] dtype
     void *dp_r, *dq_r, *a_r;             // [T*K', w] dtype
     void *dp_s, *dq_s, *a_s;             // [T, K_s*w] dtype
-    float *dxr, *dxs;                    // [T*K', d], [T, d]
+    void *dxr;                           // [T*K', d] dtype: dx of every grouped row
+    float *dxs;                          // [T, d]: dx of the shared experts
     float *dw1_r, *dw3_r, *dw2_r;        // [N', w, d], [N', w, d], [N', d, w]
     float *dw1_s, *dw3_s, *dw2_s;        // [K_s, ...]
 };
@@ -277,17 +281,18 @@ __device__ __forceinline__ uint4 ld16(const void *p) {
     return p ? *(const uint4 *)p : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// 128 x 128 tile (mode 4: 128 rows x 64 units, both halves of B), 32 k per
-// step, 4 waves in 2 x 2, each 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.
-template <int MODE, typename DT>
+// fp32 layers.  128 x 128 tile (mode 4: 128 rows x 64 units, both halves of
+// B), 32 k per step, 4 waves in 2 x 2, each 64 x 64 = 2 x 2 MFMA blocks of
+// 32 x 32 (v_mfma_f32_32x32x2f32).
+template <int MODE>
 __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
-    constexpr bool BF = std::is_same<DT, uint16_t>::value;
+    using DT = float;
     constexpr int ES = sizeof(DT);
     constexpr int EC = 16 / ES;                       // elements per 16-byte chunk
     constexpr bool AT = a_transposed(MODE), BT = b_transposed(MODE);
     // LDS pitches (bytes): k-contiguous tiles [128][32], transposed tiles [32][128]
-    constexpr int PK = 32 * ES + 16;                  // 80 (bf16) / 144 (fp32): conflict-free fragment rows
-    constexpr int PT = 128 * ES + (BF ? 64 : 128);    // 320 / 640: the four rows of a transposed read hit distinct banks
+    constexpr int PK = 32 * ES + 16;                  // 144: conflict-free fragment rows
+    constexpr int PT = 128 * ES + 128;                // 640
     constexpr int SA = AT ? 32 * PT : 128 * PK;
     constexpr int SB = BT ? 32 * PT : 128 * PK;
     constexpr int CA = AT ? 32 * (128 / EC) : 128 * (32 / EC);   // chunks per A tile
@@ -372,107 +377,7 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
 
     // ---- staging: chunk c of a tile -> (row, column) in the tile ----
     uint4 ra[RA], rb[RB];
-    // bf16 products: every chunk's byte offset is fixed per tile and a step
-    // adds a uniform scalar offset (mode 3's B rows follow the gathered
-    // tokens, loaded one step ahead); no address arithmetic, division or
-    // branch per chunk in the k loop.  Column offsets within a chunk never
-    // cross a segment or a [dp | dq] boundary: w % 64 == 0 and chunks are 8
-    // elements.  dq follows dp in the same workspace, so one window with dq
-    // at a positive byte offset covers both.
-    constexpr bool BUF = BF && MODE <= 3;
-    __amdgpu_buffer_rsrc_t rsA = bg_rsrc(A.x), rsB = rsA, rsB2 = rsA;
-    uint32_t va[RA], vb[RB], sA = 0, sB = 0, dA = 0;
-    int klA[RA], klB[RB], tkB[RB];
-    if constexpr (BUF) {
-        const size_t w = A.w, d = A.d, wg = Gr.wg, ro = Gr.roff;
-        const DT *dy = (const DT *)(Gr.sh ? A.dh : A.dy_r);
-        const DT *dp = (const DT *)(Gr.sh ? A.dp_s : A.dp_r), *dq = (const DT *)(Gr.sh ? A.dq_s : A.dq_r);
-        const uint32_t dq_off = (uint32_t)((const char *)dq - (const char *)dp);
-#pragma unroll
-        for (int i = 0; i < RA; ++i) {
-            const int c = tid + 256 * i;
-            int m, kofs;
-            if (AT) { kofs = c / (128 / EC); m = m0 + (c % (128 / EC)) * EC; }
-            else { m = m0 + c / (32 / EC); kofs = (c % (32 / EC)) * EC; }
-            size_t e = 0;
-            if (MODE == 0) e = (ro + m) * d + kofs;
-            if (MODE == 1) e = (ro + m) * wg + kofs;
-            if (MODE == 2) e = (size_t)kofs * d + m;
-            if (MODE == 3) e = (ro + kofs) * wg + (m < (int)wg ? m : m - (int)wg);
-            uint32_t off = (uint32_t)(e * ES);
-            if (MODE == 3 && m >= (int)wg) off += dq_off;
-            va[i] = m < M ? off : kOob;
-            klA[i] = K - kofs;   // the chunk is live while k0 < klA
-        }
-        if (MODE == 0) { rsA = bg_rsrc(dy); sA = 32 * ES; }
-        if (MODE == 1) { rsA = bg_rsrc(dp); dA = dq_off; }
-        if (MODE == 2) { rsA = bg_rsrc(dy + ro * d); sA = (uint32_t)(32 * d * ES); }
-        if (MODE == 3) { rsA = bg_rsrc(dp); sA = (uint32_t)(32 * wg * ES); }
-
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const int c = tid + 256 * i;
-            const int kofs = c / (128 / EC), n = n0 + (c % (128 / EC)) * EC;   // B is transposed in modes 0-3
-            size_t e = 0;
-            if (MODE == 0) e = ((size_t)(n / A.w) * d + kofs) * w + n % A.w;
-            if (MODE == 1) e = (size_t)kofs * d + n;
-            if (MODE == 2) e = (size_t)kofs * wg + n;
-            if (MODE == 3) e = (size_t)n;
-            vb[i] = n < N ? (uint32_t)(e * ES) : kOob;
-            klB[i] = K - kofs;
-            tkB[i] = 0;
-        }
-        if (MODE == 0) {
-            rsB = bg_rsrc(Gr.sh ? (const DT *)A.w2_s : (const DT *)A.w2_r + (size_t)Gr.r * d * w);
-            sB = (uint32_t)(32 * w * ES);
-        }
-        if (MODE == 1) {
-            rsB = bg_rsrc(Gr.sh ? (const DT *)A.w1_s : (const DT *)A.w1_r + (size_t)Gr.r * w * d);
-            rsB2 = bg_rsrc(Gr.sh ? (const DT *)A.w3_s : (const DT *)A.w3_r + (size_t)Gr.r * w * d);
-            sB = (uint32_t)(d * ES);   // per k row
-        }
-        if (MODE == 2) { rsB = bg_rsrc((const DT *)(Gr.sh ? A.a_s : A.a_r) + ro * wg); sB = (uint32_t)(32 * wg * ES); }
-        if (MODE == 3) rsB = bg_rsrc(A.x);
-    }
-    // mode 3: token of k row k0 + kofs of chunk i (clamped into the group)
-    auto tok_of = [&](int i, int k0) -> int {
-        const int c = tid + 256 * i, k = min(k0 + c / (128 / EC), max(K - 1, 0));
-        return Gr.sh ? k : A.sorted_token[Gr.roff + k];
-    };
-    auto load_buf = [&](int k0) {
-        // A
-        uint32_t so = 0;
-        if (MODE == 1) so = k0 < Gr.wg ? (uint32_t)(k0 * ES) : dA + (uint32_t)((k0 - Gr.wg) * ES);
-        else so = (uint32_t)(k0 / 32) * sA;
-#pragma unroll
-        for (int i = 0; i < RA; ++i) {
-            const uint32_t v = (MODE >= 2 && k0 >= klA[i]) ? kOob : va[i];
-            ra[i] = bg_load(rsA, v, so);
-        }
-        // B
-        if (MODE == 3) {
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                const uint32_t v = (k0 >= klB[i] || vb[i] == kOob) ? kOob : (uint32_t)(tkB[i] * A.d * ES) + vb[i];
-                rb[i] = bg_load(rsB, v, 0);
-            }
-            // tokens of the next step's rows, a step ahead of their use
-#pragma unroll
-            for (int i = 0; i < RB; ++i) tkB[i] = tok_of(i, k0 + 32);
-        } else {
-            const bool w3 = MODE == 1 && k0 >= Gr.wg;
-            const uint32_t sob = MODE == 1 ? (uint32_t)(w3 ? k0 - Gr.wg : k0) * sB : (uint32_t)(k0 / 32) * sB;
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                const uint32_t v = (MODE >= 2 && k0 >= klB[i]) ? kOob : vb[i];
-                rb[i] = bg_load(w3 ? rsB2 : rsB, v, sob);
-            }
-        }
-    };
     auto load_tiles = [&](int k0) {
-      if constexpr (BUF) {
-        load_buf(k0);
-      } else {
 #pragma unroll
         for (int i = 0; i < RA; ++i) {
             const int c = tid + 256 * i;
@@ -489,7 +394,6 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
             else { const int nr = c / (32 / EC), kc = c % (32 / EC); p = b_ptr<MODE, DT>(A, Gr, n0 + nr, k0 + kc * EC, N, K); }
             rb[i] = ld16(p);
         }
-      }
     };
     auto store_tiles = [&](int stg) {
         uint8_t *s_a = s_a2[stg], *s_b = s_b2[stg];
@@ -518,41 +422,14 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
     const int l32 = lane & 31, lhi = lane >> 5;
-    // fragment of a 32-row block at tile row r0 for the k16 (bf16) / k2 (fp32) sub-step s
-    auto frag_bf = [&](const uint8_t *s, bool tr, int r0, int ks) -> bf16x8 {
-        if (!tr) return *(const bf16x8 *)(s + (r0 + l32) * PK + (16 * ks + 8 * lhi) * 2);
-        const int g = lane >> 4, j = lane & 15;
-        const int col = r0 + 16 * (g & 1) + 4 * (j & 3);
-        const int row = 16 * ks + 8 * (g >> 1) + (j >> 2);
-        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(s + row * PT + col * 2));
-        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(s + (row + 4) * PT + col * 2));
-        // whole-vector shuffle and bit cast (element-wise assembly of the
-        // fragment was miscompiled: the second dword of each read was lost)
-        const v8s both = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, both);
-    };
+    // fragment of a 32-row block at tile row r0 for k sub-step ks (2 k)
     auto frag_f32 = [&](const uint8_t *s, bool tr, int r0, int ks) -> float {
         const int k = 2 * ks + lhi;
         return tr ? *(const float *)(s + k * PT + (r0 + l32) * 4) : *(const float *)(s + (r0 + l32) * PK + k * 4);
     };
     auto compute = [&](int stg) {
         const uint8_t *s_a = s_a2[stg], *s_b = s_b2[stg];
-        if constexpr (BF) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 fa[2], fb[2];
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    fa[b] = frag_bf(s_a, AT, wm * 64 + b * 32, ks);
-                    fb[b] = frag_bf(s_b, BT, wn * 64 + b * 32, ks);
-                }
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
-            }
-        } else {
+        {
 #pragma unroll
             for (int ks = 0; ks < 16; ++ks) {
                 float fa[2], fb[2];
@@ -574,10 +451,6 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
     // compute of the current one.  (Two stages with one barrier per step
     // measured slower: the extra registers cost a wave per SIMD.)
     const int nk = cdiv(K, 32);
-    if (MODE == 3 && BUF && nk > 0) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i) tkB[i] = tok_of(i, 0);
-    }
     if (nk > 0) {
         load_tiles(0);
         store_tiles(0);
@@ -633,7 +506,7 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
                         DT *o = (DT *)(Gr.sh ? A.da_s : A.da_r);
                         o[(size_t)(Gr.roff + m) * Gr.wg + n] = from_f<DT>(v);
                     } else if (MODE == 1) {
-                        float *o = Gr.sh ? A.dxs : A.dxr;
+                        float *o = Gr.sh ? A.dxs : (float *)A.dxr;
                         o[(size_t)(Gr.roff + m) * A.d + n] = v;
                     } else if (MODE == 2) {
                         const int seg = n / A.w, nn = n % A.w;
@@ -652,23 +525,448 @@ __global__ __launch_bounds__(256, 4) void bgemm_kernel(BgArgs A) {
     }
 }
 
-// dx_ffn[t] = dxs[t] (shared experts, or 0) + sum_k dxr[slot_of[t,k]], k in order.
+// ---------------------------------------------------------------------------
+// bf16 grouped GEMMs of modes 0-3 on 256 x 256 tiles.
+//
+// 512 threads (8 waves, 2 per SIMD) in 2 x 4: a wave owns 4 blocks of 32 A
+// rows (tile rows (2b + wm) * 32, so the live blocks of a short tile split
+// evenly between the two wave rows) times 2 blocks of 32 B rows, 8 MFMAs of
+// 32 x 32 x 16 per 6 fragment reads (the 128 x 128 kernel above: 4 per 4).
+// 64 k per step in two LDS stages; the registers hold the step after next,
+// written into the idle stage a quarter at a time between the MFMAs of the
+// current step, so one barrier per step.
+// Stage layouts: a k-contiguous operand is 256 rows of 128 B, 16-byte chunk c
+// of row r at c ^ (r & 7) ^ ((r >> 3) & 1) (a ds_read_b128 of 32 rows hits
+// distinct banks); a transposed operand is 64 k rows of 256 values with a
+// 576-byte pitch, read through ds_read_b64_tr_b16 (the four k rows that one
+// 32-lane half reads lie 64 B apart modulo the 256-byte bank cycle).
+// Modes 1-3 share one launch (no product among them needs another's output):
+// the dx rows first (k = 2 w, the longest), then dW1/dW3, then dW2.
+// ---------------------------------------------------------------------------
+namespace wide {
+constexpr int NT = 512;
+constexpr int KC = 128;          // k-contiguous stage: bytes per row (64 k)
+constexpr int KT = 576;          // transposed stage: pitch of a k row (256 values + 64 B)
+constexpr int SKC = 256 * KC;    // 32 KB
+constexpr int STR = 64 * KT;     // 36 KB
+constexpr int SMEM = 4 * STR;    // two stages of two transposed operands (the largest)
+}  // namespace wide
+
+// The modes of one launch and their block counts in units of 8 (a mode's
+// block j runs on XCD j % 8), in block order.  (Interleaving the modes 8
+// blocks at a time measured slower: fewer co-running tiles of one expert
+// share an XCD's L2.)
+struct WideRange {
+    int mode[3];
+    int oct[3];
+};
+
+// Tile (m0, nr rows; n0) of group Gr for product MODE, K its depth.
+template <int MODE>
+__device__ __forceinline__ void wide_tile(const BgArgs &A, const Group &Gr, int m0, int nr, int n0, int M, int N,
+                                          int K, uint8_t *smem) {
+    using namespace wide;
+    constexpr bool AT = a_transposed(MODE), BT = b_transposed(MODE);
+    constexpr int SA = AT ? STR : SKC, SB = BT ? STR : SKC;
+    static_assert(2 * (SA + SB) <= SMEM, "stages fit");
+    auto stA = [&](int s) { return smem + s * (SA + SB); };
+    auto stB = [&](int s) { return smem + s * (SA + SB) + SA; };
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    // staging geometry: k-contiguous chunk i = row rsub + 64 i, 16-byte part `part`;
+    // transposed chunk i = k row kr + 16 i, values 8 mc .. 8 mc + 7
+    const int part = tid & 7, rsub = tid >> 3;
+    const int swz = part ^ (rsub & 7) ^ ((rsub >> 3) & 1);
+    const int mc = tid & 31, kr = tid >> 5;
+    auto lds_off = [&](bool tr, int i) { return tr ? (kr + 16 * i) * KT + mc * 16 : (rsub + 64 * i) * KC + swz * 16; };
+
+    const size_t d = A.d, w = A.w, wg = Gr.wg, ro = Gr.roff;
+    const uint16_t *dy = (const uint16_t *)(Gr.sh ? A.dh : A.dy_r);
+    const uint16_t *dp = (const uint16_t *)(Gr.sh ? A.dp_s : A.dp_r);
+    const uint16_t *dq = (const uint16_t *)(Gr.sh ? A.dq_s : A.dq_r);
+    const uint32_t dq_off = (uint32_t)((const char *)dq - (const char *)dp);   // dq follows dp in the workspace
+
+    // fixed byte offsets of each thread's chunks (kOob: outside the tile's rows or columns)
+    uint32_t va[4], vb[4];
+    __amdgpu_buffer_rsrc_t rsA, rsB, rsB2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (MODE == 0) {   // A = dy rows (k = d), B = W2 [seg][d][w] read along its units
+            const int m = rsub + 64 * i;
+            va[i] = m < nr ? (uint32_t)(((m0 + m) * d + part * 8) * 2) : kOob;
+            const int n = n0 + 8 * mc;
+            const size_t seg = (size_t)n / w;
+            vb[i] = n < N ? (uint32_t)((seg * d * w + (size_t)(kr + 16 * i) * w + (n - seg * w)) * 2) : kOob;
+        } else if (MODE == 1) {   // A = [dp | dq] rows (k = unit), B = [W1; W3] rows read along d
+            const int m = rsub + 64 * i;
+            va[i] = m < nr ? (uint32_t)(((m0 + m) * wg + part * 8) * 2) : kOob;
+            const int n = n0 + 8 * mc;
+            vb[i] = n < N ? (uint32_t)(((size_t)(kr + 16 * i) * d + n) * 2) : kOob;
+        } else if (MODE == 2) {   // A(m = column of dy, k = row), B(n = unit, k = row) of a
+            const int m = m0 + 8 * mc, n = n0 + 8 * mc;
+            va[i] = 8 * mc < nr ? (uint32_t)(((size_t)(kr + 16 * i) * d + m) * 2) : kOob;
+            vb[i] = n < N ? (uint32_t)(((size_t)(kr + 16 * i) * wg + n) * 2) : kOob;
+        } else {   // A(m = unit of [dp | dq], k = row), B(n = column of x, k = row: gathered token)
+            const int m = m0 + 8 * mc, n = n0 + 8 * mc;
+            const bool q = m >= (int)wg;
+            const size_t mm = q ? m - wg : m;
+            va[i] = 8 * mc < nr ? (uint32_t)(((size_t)(kr + 16 * i) * wg + mm) * 2) + (q ? dq_off : 0u) : kOob;
+            vb[i] = n < N ? (uint32_t)(n * 2) : kOob;
+        }
+    }
+    if (MODE == 0) {
+        rsA = bg_rsrc(dy + ro * d);
+        rsB = bg_rsrc(Gr.sh ? (const uint16_t *)A.w2_s : (const uint16_t *)A.w2_r + (size_t)Gr.r * d * w);
+    } else if (MODE == 1) {
+        rsA = bg_rsrc(dp + ro * wg);
+        rsB = bg_rsrc(Gr.sh ? (const uint16_t *)A.w1_s : (const uint16_t *)A.w1_r + (size_t)Gr.r * w * d);
+        rsB2 = bg_rsrc(Gr.sh ? (const uint16_t *)A.w3_s : (const uint16_t *)A.w3_r + (size_t)Gr.r * w * d);
+    } else if (MODE == 2) {
+        rsA = bg_rsrc(dy + ro * d);
+        rsB = bg_rsrc((const uint16_t *)(Gr.sh ? A.a_s : A.a_r) + ro * wg);
+    } else {
+        rsA = bg_rsrc(dp + ro * wg);
+        rsB = bg_rsrc(A.x);
+    }
+    if (MODE != 1) rsB2 = rsB;
+    // mode 3: byte offset of the token row of chunk i's k row in the step whose loads go out next
+    uint32_t tkb[4] = {0u, 0u, 0u, 0u};
+    auto tok_row = [&](int i, int k0) -> uint32_t {
+        const int k = min(k0 + kr + 16 * i, K - 1);
+        const int t = Gr.sh ? k : A.sorted_token[ro + k];
+        return (uint32_t)t * (uint32_t)(d * 2);
+    };
+
+    // offsets of k step kt: uniform (scalar) adds to the fixed chunk offsets
+    struct KS {
+        uint32_t sa, sb;
+        int k0;
+        bool b3;
+    };
+    auto kstate = [&](int kt) -> KS {
+        KS s;
+        s.k0 = kt * 64;
+        s.b3 = false;
+        if (MODE == 0) { s.sa = (uint32_t)kt * 128u; s.sb = (uint32_t)(kt * 64 * w * 2); }
+        if (MODE == 1) {
+            s.b3 = s.k0 >= (int)wg;
+            const int kk = s.b3 ? s.k0 - (int)wg : s.k0;
+            s.sa = (s.b3 ? dq_off : 0u) + (uint32_t)kk * 2u;
+            s.sb = (uint32_t)((size_t)kk * d * 2);
+        }
+        if (MODE == 2) { s.sa = (uint32_t)((size_t)s.k0 * d * 2); s.sb = (uint32_t)((size_t)s.k0 * wg * 2); }
+        if (MODE == 3) { s.sa = (uint32_t)((size_t)s.k0 * wg * 2); s.sb = 0u; }
+        return s;
+    };
+    uint4 ra[4], rb[4];
+    // quarter ph of step s: chunk ph of both operands
+    auto gload = [&](const KS &s, int ph) {
+        const bool kv = MODE < 2 || s.k0 + kr + 16 * ph < K;   // the transposed chunks' k row is inside the group
+        ra[ph] = bg_load(rsA, kv ? va[ph] : kOob, s.sa);
+        if (MODE == 3) {
+            rb[ph] = bg_load(rsB, (kv && vb[ph] != kOob) ? tkb[ph] + vb[ph] : kOob, 0u);
+            tkb[ph] = tok_row(ph, s.k0 + 64);   // the same chunk's row one step on
+        } else {
+            rb[ph] = bg_load(s.b3 ? rsB2 : rsB, kv ? vb[ph] : kOob, s.sb);
+        }
+    };
+    auto sstore = [&](int st, int ph) {
+        *(uint4 *)(stA(st) + lds_off(AT, ph)) = ra[ph];
+        *(uint4 *)(stB(st) + lds_off(BT, ph)) = rb[ph];
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+    // fragment of the 32-row block at `base` for k sub-step ks (16 k)
+    const int lsw = (l32 & 7) ^ ((l32 >> 3) & 1);
+    const int g4 = lane >> 4, j16 = lane & 15;
+    const int trow = 8 * (g4 >> 1) + (j16 >> 2), tcol = 16 * (g4 & 1) + 4 * (j16 & 3);
+    auto frag = [&](const uint8_t *s, bool tr, int base, int ks) -> bf16x8 {
+        if (!tr) return *(const bf16x8 *)(s + (base + l32) * KC + ((2 * ks + lhi) ^ lsw) * 16);
+        const uint8_t *p = s + (16 * ks + trow) * KT + (base + tcol) * 2;
+        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p);
+        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p + 4 * KT));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto frags = [&](auto ml_t, int st, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+        constexpr int ML = decltype(ml_t)::value;
+#pragma unroll
+        for (int ma = 0; ma < ML; ++ma) fa[ma] = frag(stA(st), AT, (2 * ma + wm) * 32, ks);
+        if (ML > 0) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(stB(st), BT, wn * 64 + nb * 32, ks);
+        }
+    };
+    auto mma = [&](auto ml_t, const bf16x8 (&fa)[4], const bf16x8 (&fb)[2]) {
+        constexpr int ML = decltype(ml_t)::value;
+#pragma unroll
+        for (int ma = 0; ma < ML; ++ma)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                acc[ma][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ma], fb[nb], acc[ma][nb], 0, 0, 0);
+    };
+
+    using yes = std::true_type;
+    using no = std::false_type;
+    const int nk = cdiv(K, 64);
+    const int nblk = cdiv(nr, 32);
+    const int ml = __builtin_amdgcn_readfirstlane(min(4, (nblk - wm + 1) >> 1));
+    if (nk > 0) {
+        const KS s0 = kstate(0);
+        if (MODE == 3) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tkb[i] = tok_row(i, 0);
+        }
+#pragma unroll
+        for (int ph = 0; ph < 4; ++ph) gload(s0, ph);
+#pragma unroll
+        for (int ph = 0; ph < 4; ++ph) sstore(0, ph);
+        __syncthreads();
+        auto kloop = [&](auto ml_t) {
+            if (nk > 1) {
+                const KS s1 = kstate(1);
+#pragma unroll
+                for (int ph = 0; ph < 4; ++ph) {
+                    gload(s1, ph);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            auto kstep = [&](int kt, auto more_t, auto more2_t) {
+                constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
+                const int st = kt & 1;
+                KS sn;
+                if (MORE2) sn = kstate(kt + 2);
+                bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+                frags(ml_t, st, 0, fa0, fb0);
+                frags(ml_t, st, 1, fa1, fb1);
+                if (MORE) { sstore(st ^ 1, 0); if (MORE2) gload(sn, 0); }
+                __builtin_amdgcn_sched_barrier(0);
+                mma(ml_t, fa0, fb0);
+                frags(ml_t, st, 2, fa0, fb0);
+                if (MORE) { sstore(st ^ 1, 1); if (MORE2) gload(sn, 1); }
+                __builtin_amdgcn_sched_barrier(0);
+                mma(ml_t, fa1, fb1);
+                frags(ml_t, st, 3, fa1, fb1);
+                if (MORE) { sstore(st ^ 1, 2); if (MORE2) gload(sn, 2); }
+                __builtin_amdgcn_sched_barrier(0);
+                mma(ml_t, fa0, fb0);
+                if (MORE) { sstore(st ^ 1, 3); if (MORE2) gload(sn, 3); }
+                __builtin_amdgcn_sched_barrier(0);
+                mma(ml_t, fa1, fb1);
+                __syncthreads();
+            };
+            int kt = 0;
+            for (; kt + 2 < nk; ++kt) kstep(kt, yes{}, yes{});
+            if (kt + 1 < nk) kstep(kt++, yes{}, no{});
+            kstep(kt, no{}, no{});
+        };
+        using std::integral_constant;
+        if (ml >= 4) kloop(integral_constant<int, 4>{});
+        else if (ml == 3) kloop(integral_constant<int, 3>{});
+        else if (ml == 2) kloop(integral_constant<int, 2>{});
+        else if (ml == 1) kloop(integral_constant<int, 1>{});
+        else kloop(integral_constant<int, 0>{});
+    }
+
+    // ---- epilogue: lane holds column n = l32 of each B block; register 4q + e
+    //      holds tile row (2 ma + wm) * 32 + 8q + 4 lhi + e.  The tile goes out
+    //      through the idle LDS stages as whole rows of 16-byte stores (a row
+    //      per wave instruction; bf16: two rows): stored straight from the
+    //      MFMA layout, every instruction would write 4-byte pieces of two rows,
+    //      4x the store instructions, which took 7-12 us per tile.  fp32 tiles
+    //      go in two passes of 128 rows (pitch 1056 B), bf16 tiles in one pass
+    //      (pitch 544 B); either pitch puts the rows r and r + 4 of a fragment
+    //      write on different banks.
+    const bool obf = MODE == 0 || (MODE == 1 && !Gr.sh);   // bf16 output rows
+    // element offset of columns [n, n + 8) (bf16) / [n, n + 4) (fp32) in an output
+    // row, per lane; mode 2: in its W2 segment, whose base goes in too
+    const int ncol = obf ? 8 * l32 : 4 * lane;
+    const int nabs = n0 + ncol;
+    size_t nofs = (size_t)nabs;
+    if (MODE == 2) {
+        const size_t seg = (size_t)nabs / w;
+        nofs = seg * d * w + (nabs - seg * w);
+    }
+    const bool ncol_ok = nabs < N;
+    auto row_ptr = [&](int tr) -> uint8_t * {   // output row of tile row tr (bytes; the lane's columns)
+        const size_t m = (size_t)(m0 + tr);
+        if (MODE == 0) return (uint8_t *)((uint16_t *)(Gr.sh ? A.da_s : A.da_r) + (ro + m) * wg + nofs);
+        if (MODE == 1) {
+            if (obf) return (uint8_t *)((uint16_t *)A.dxr + (ro + m) * d + nofs);
+            return (uint8_t *)(A.dxs + m * d + nofs);
+        }
+        if (MODE == 2) return (uint8_t *)((Gr.sh ? A.dw2_s : A.dw2_r + (size_t)Gr.r * d * w) + m * w + nofs);
+        const bool q = m >= wg;
+        float *o = Gr.sh ? (q ? A.dw3_s : A.dw1_s) : (q ? A.dw3_r : A.dw1_r) + (size_t)Gr.r * w * d;
+        return (uint8_t *)(o + (q ? m - wg : m) * d + nofs);
+    };
+    auto emit = [&](auto bf_t) {
+        constexpr bool BF = decltype(bf_t)::value;
+        constexpr int PR = BF ? 256 : 128;        // tile rows per pass
+        constexpr int PITCH = BF ? 544 : 1056;
+#pragma unroll
+        for (int pass = 0; pass < 256 / PR; ++pass) {
+            if (pass * PR >= nr) break;
+            if (pass > 0) __syncthreads();         // the previous pass's rows are read
+#pragma unroll
+            for (int ma = 0; ma < 4; ++ma) {
+                const int rb0 = (2 * ma + wm) * 32;
+                if (rb0 < pass * PR || rb0 >= (pass + 1) * PR || rb0 >= nr) continue;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const int c = wn * 64 + nb * 32 + l32;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int lr = rb0 - pass * PR + 8 * (e >> 2) + 4 * lhi + (e & 3);
+                        if (BF) *(uint16_t *)(smem + lr * PITCH + c * 2) = f2bf(acc[ma][nb][e]);
+                        else *(float *)(smem + lr * PITCH + c * 4) = acc[ma][nb][e];
+                    }
+                }
+            }
+            __syncthreads();
+            // wave w stores rows w, w + 8, ... of the pass (bf16: a row per half-wave)
+            constexpr int RPI = BF ? 2 : 1;       // rows per store instruction
+#pragma unroll
+            for (int i = 0; i < PR / (8 * RPI); ++i) {
+                const int lr = (i * 8 + wave) * RPI + (BF ? lhi : 0);
+                const int tr = pass * PR + lr;
+                const uint4 v = *(const uint4 *)(smem + lr * PITCH + (BF ? l32 : lane) * 16);
+                if (tr < nr && ncol_ok) *(uint4 *)row_ptr(tr) = v;
+            }
+        }
+    };
+    if (obf) emit(std::true_type{});
+    else emit(std::false_type{});
+}
+
+// Locates block lb of a mode's range and runs its tile.  The tile list is
+// ordered group by group; a group's rows (modes 0, 1) or its M (modes 2, 3)
+// are cut into mt runs of equal length rounded up to 32, as in the forward.
+// XCD-aware order: as in bgemm_kernel (a mode's range starts on XCD 0).
+template <int MODE>
+__device__ __forceinline__ void wide_run(const BgArgs &A, int lb, uint8_t *smem, int *s_pref, int &s_maxg) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = (A.Ks > 0 ? 1 : 0) + A.Nr;
+    if (wave == 0) {
+        int carry = 0, mx = 0;
+        if (lane == 0) s_pref[0] = 0;
+        for (int g0 = 0; g0 < G; g0 += 64) {
+            const int g = g0 + lane;
+            int tiles = 0;
+            if (g < G) {
+                const Group Gr = group_of(A, g);
+                int M, N, K;
+                dims<MODE>(A, Gr, M, N, K);
+                tiles = cdiv(M, 256) * cdiv(N, 256);
+            }
+            mx = max(mx, tiles);
+            int incl = tiles;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += v;
+            }
+            if (g < G) s_pref[g + 1] = carry + incl;
+            carry += __shfl(incl, 63, 64);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+        if (lane == 0) s_maxg = mx;
+    }
+    __syncthreads();
+    const int NT = s_pref[G];
+    if (lb >= NT) return;
+    auto spread = [](int j, int n) {
+        const int per = (n + 7) / 8, tall = n % 8 == 0 ? 8 : n % 8, x = j % 8, l = j / 8;
+        return x < tall ? x * per + l : tall * per + (x - tall) * (per - 1) + l;
+    };
+    auto group_at = [&](int v) {
+        int lo = 0, hi = G;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pref[mid] <= v) lo = mid; else hi = mid;
+        }
+        return lo;
+    };
+    const bool whole = (MODE == 0 || (MODE == 1 && A.Ks <= 1)) && s_maxg * 8 <= NT;
+    int g, lt;
+    if (whole) {
+        const int v = spread(lb, NT);
+        g = group_at(v);
+        lt = v - s_pref[g];
+    } else {
+        g = group_at(lb);
+        lt = spread(lb - s_pref[g], s_pref[g + 1] - s_pref[g]);
+    }
+    const Group Gr = group_of(A, g);
+    int M, N, K;
+    dims<MODE>(A, Gr, M, N, K);
+    const int mt = cdiv(M, 256);
+    const int run = (cdiv(M, mt) + 31) & ~31;
+    const int m0 = (lt % mt) * run, n0 = (lt / mt) * 256;
+    wide_tile<MODE>(A, Gr, m0, min(run, M - m0), n0, M, N, K, smem);
+}
+
+__global__ __launch_bounds__(512) void bgemm_wide_kernel(BgArgs A, WideRange R) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[wide::SMEM];
+    __shared__ int s_pref[BG_MAXG + 1];
+    __shared__ int s_maxg;
+    const int o = blockIdx.x >> 3;
+    const int slot = o < R.oct[0] ? 0 : (o < R.oct[0] + R.oct[1] ? 1 : 2);
+    const int lb = blockIdx.x - 8 * (slot == 0 ? 0 : (slot == 1 ? R.oct[0] : R.oct[0] + R.oct[1]));
+    switch (R.mode[slot]) {
+        case 0: wide_run<0>(A, lb, smem, s_pref, s_maxg); break;
+        case 1: wide_run<1>(A, lb, smem, s_pref, s_maxg); break;
+        case 2: wide_run<2>(A, lb, smem, s_pref, s_maxg); break;
+        default: wide_run<3>(A, lb, smem, s_pref, s_maxg); break;
+    }
+}
+
+// dx_ffn[t] = dxs[t] (shared experts, or 0) + sum_k dxr[slot_of[t,k]], k in
+// order.  A thread owns 8 columns of a token: its K' slots are read first,
+// then the K' row pieces go out together (4 at a time), summed in k order.
+template <typename RT>
 __global__ __launch_bounds__(256) void gather_dx_kernel(int T, int d, int K, const float *__restrict__ dxs,
-                                                        const float *__restrict__ dxr,
+                                                        const RT *__restrict__ dxr,
                                                         const int32_t *__restrict__ slot_of,
                                                         float *__restrict__ dx) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one float4 of one token
-    const int q = d / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 8 columns of one token
+    const int q = d / 8;
     if (i >= (int64_t)T * q) return;
-    const int t = (int)(i / q), c = (int)(i % q) * 4;
-    float4 acc = dxs ? *(const float4 *)(dxs + (size_t)t * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-        const int slot = slot_of[(size_t)t * K + k];
-        if (slot < 0) continue;
-        const float4 v = *(const float4 *)(dxr + (size_t)slot * d + c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    const int t = (int)(i / q), c = (int)(i % q) * 8;
+    float acc[8];
+    if (dxs) {
+        load8(dxs + (size_t)t * d + c, acc);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     }
-    *(float4 *)(dx + (size_t)t * d + c) = acc;
+    int slot[kRouteMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kRouteMaxTopK; ++k) slot[k] = k < K ? slot_of[(size_t)t * K + k] : -1;
+#pragma unroll
+    for (int k0 = 0; k0 < kRouteMaxTopK; k0 += 4) {
+        if (k0 >= K) break;
+        float v[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (slot[k0 + u] >= 0) load8(dxr + (size_t)slot[k0 + u] * d + c, v[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (slot[k0 + u] >= 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
+            }
+    }
+    store8(dx + (size_t)t * d + c, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -832,10 +1130,10 @@ __global__ __launch_bounds__(256) void router_de_sum_kernel(int nchunk, int d, i
     else if (dbias) dbias[r] = a;
 }
 
-template <int MODE, typename DT>
+template <int MODE>
 hipError_t launch_bg(const BgArgs &a, int tiles, hipStream_t s) {
     if (tiles <= 0) return hipSuccess;
-    bgemm_kernel<MODE, DT><<<tiles, 256, 0, s>>>(a);
+    bgemm_kernel<MODE><<<tiles, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -884,7 +1182,18 @@ hipError_t launch_expert_backward(const moe_problem &p, const BwdFfnArgs &b, hip
     hipError_t e;
     (void)t4;
     if (p.dtype == MOE_BF16) {
-        if ((e = launch_bg<0, uint16_t>(a, t0, s)) != hipSuccess) return e;
+        // 256 x 256 tiles: da alone, then (after the recompute) dx rows, dW1/dW3, dW2 in one launch
+        const int rw = (p.n_routed > 0 ? (int)(((int64_t)p.T * p.top_k) / 256) + p.n_routed : 0) +
+                       (p.n_shared > 0 ? cdiv(p.T, 256) : 0);
+        const int o0 = cdiv(rw * cdiv(wmax, 256), 8);
+        const int o1 = cdiv(rw * cdiv(p.d, 256), 8);
+        const int o3 = cdiv(G * cdiv(2 * wmax, 256) * cdiv(p.d, 256), 8);
+        const int o2 = cdiv(G * cdiv(p.d, 256) * cdiv(wmax, 256), 8);
+        if (o0 > 0) {
+            const WideRange r0{{0, 0, 0}, {o0, 0, 0}};
+            bgemm_wide_kernel<<<8 * o0, wide::NT, 0, s>>>(a, r0);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         // p, q recomputed by the forward up kernel, with the backward epilogue
         FfnArgs f{};
         f.x = b.x; f.offsets = b.offsets; f.sorted_token = b.sorted_token;
@@ -896,20 +1205,28 @@ hipError_t launch_expert_backward(const moe_problem &p, const BwdFfnArgs &b, hip
         if ((q.n_routed > 0 || q.n_shared > 0) &&
             (e = launch_expert_up_backward(q, f, b.da_s, b.da_r, b.dp_s, b.dp_r, b.dq_s, b.dq_r, s)) != hipSuccess)
             return e;
-        if ((e = launch_bg<1, uint16_t>(a, t1, s)) != hipSuccess) return e;
-        if ((e = launch_bg<2, uint16_t>(a, t2, s)) != hipSuccess) return e;
-        if ((e = launch_bg<3, uint16_t>(a, t3, s)) != hipSuccess) return e;
+        if (o1 + o3 + o2 > 0) {
+            const WideRange r{{1, 3, 2}, {o1, o3, o2}};
+            bgemm_wide_kernel<<<8 * (o1 + o3 + o2), wide::NT, 0, s>>>(a, r);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     } else {
-        if ((e = launch_bg<0, float>(a, t0, s)) != hipSuccess) return e;
-        if ((e = launch_bg<4, float>(a, t4, s)) != hipSuccess) return e;
-        if ((e = launch_bg<1, float>(a, t1, s)) != hipSuccess) return e;
-        if ((e = launch_bg<2, float>(a, t2, s)) != hipSuccess) return e;
-        if ((e = launch_bg<3, float>(a, t3, s)) != hipSuccess) return e;
+        if ((e = launch_bg<0>(a, t0, s)) != hipSuccess) return e;
+        if ((e = launch_bg<4>(a, t4, s)) != hipSuccess) return e;
+        if ((e = launch_bg<1>(a, t1, s)) != hipSuccess) return e;
+        if ((e = launch_bg<2>(a, t2, s)) != hipSuccess) return e;
+        if ((e = launch_bg<3>(a, t3, s)) != hipSuccess) return e;
     }
     if (p.T > 0) {
-        const int64_t n = (int64_t)p.T * (p.d / 4);
-        gather_dx_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(p.T, p.d, p.top_k, p.n_shared > 0 ? b.dxs : nullptr,
-                                                                 b.dxr, b.slot_of, b.dx_ffn);
+        const int64_t n = (int64_t)p.T * (p.d / 8);
+        const int grid = (int)((n + 255) / 256);
+        const float *dxs = p.n_shared > 0 ? b.dxs : nullptr;
+        if (p.dtype == MOE_BF16)
+            gather_dx_kernel<uint16_t><<<grid, 256, 0, s>>>(p.T, p.d, p.top_k, dxs, (const uint16_t *)b.dxr,
+                                                            b.slot_of, b.dx_ffn);
+        else
+            gather_dx_kernel<float><<<grid, 256, 0, s>>>(p.T, p.d, p.top_k, dxs, (const float *)b.dxr, b.slot_of,
+                                                         b.dx_ffn);
     }
     return hipGetLastError();
 }

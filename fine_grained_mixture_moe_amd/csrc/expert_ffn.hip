@@ -40,7 +40,6 @@ constexpr int PITCH = KB + 16; // padded LDS row pitch (bytes)
 constexpr int MAXG = 1 + kPermuteMaxExperts;
 
 template <typename DT> struct Elt;
-template <> struct Elt<uint16_t> { static constexpr int size = 2; };
 template <> struct Elt<float> { static constexpr int size = 4; };
 
 __device__ __forceinline__ uint16_t f2bf(float f) {

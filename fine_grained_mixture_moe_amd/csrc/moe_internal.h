@@ -159,7 +159,7 @@ int route_backward_chunks(int T);
 struct BwdWsLayout {
     size_t da_r, dp_r, dq_r, a_r;   // dtype [T*K', w]
     size_t da_s, dp_s, dq_s, a_s;   // dtype [T, K_s*w]
-    size_t dxr;                     // fp32  [T*K', d]   dx of every grouped row
+    size_t dxr;                     // dtype [T*K', d]   dx of every grouped row
     size_t dxs;                     // fp32  [T, d]      dx of the shared experts
     size_t dz;                      // fp32  [T, N']     router logit gradient
     size_t de_part;                 // fp32  [chunks, N', d+4] centroid-gradient partials
@@ -180,7 +180,7 @@ inline BwdWsLayout bwd_ws_layout(const moe_problem &p) {
     L.dp_s = take(ts * p.inter * es);
     L.dq_s = take(ts * p.inter * es);
     L.a_s = take(ts * p.inter * es);
-    L.dxr = take(tk * p.d * sizeof(float));
+    L.dxr = take(tk * p.d * es);
     L.dxs = take((p.n_shared > 0 ? (size_t)p.T : 0) * p.d * sizeof(float));
     L.dz = take((size_t)p.T * p.n_routed * sizeof(float));
     L.de_part = take((size_t)route_backward_chunks(p.T) * p.n_routed * (p.d + 4) * sizeof(float));
@@ -197,7 +197,8 @@ struct BwdFfnArgs {
     const int32_t *offsets, *sorted_token, *slot_of;
     const void *w1_r, *w3_r, *w2_r, *w1_s, *w3_s, *w2_s;
     void *da_r, *dp_r, *dq_r, *a_r, *da_s, *dp_s, *dq_s, *a_s;
-    float *dxr, *dxs, *dx_ffn;
+    void *dxr;
+    float *dxs, *dx_ffn;
     float *dw1_r, *dw3_r, *dw2_r, *dw1_s, *dw3_s, *dw2_s;
 };
 hipError_t launch_expert_backward(const moe_problem &p, const BwdFfnArgs &a, hipStream_t s);

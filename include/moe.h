@@ -341,7 +341,8 @@ int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *count
  *   dx_t += sum_r dz[t,r] e_r;  dcentroids = dz^T x;  dbias = column sums of dz
  * The backward workspace (moe_backward_workspace_size, 256-byte aligned) is
  * separate from the forward one; it holds the per-row intermediates (da,
- * dp, dq, a in dtype, the grouped rows' dx in fp32) and the router's dz.
+ * dp, dq, a and the grouped rows' dx, all in dtype; the shared experts' dx
+ * in fp32) and the router's dz.
  * Gradients are fp32; accumulation is fp32; the intermediates are rounded
  * to dtype as the forward rounds its activations.  Every output is
  * overwritten.  Deterministic: no atomics, fixed summation orders.
