@@ -739,13 +739,15 @@ __device__ __forceinline__ void wide_tile(const BgArgs &A, const Group &Gr, int 
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            // sub-step 0's fragments of each step are read under the last MFMAs of the
+            // step before, after its barrier (as in the forward's k loop)
+            bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+            frags(ml_t, 0, 0, fa0, fb0);
             auto kstep = [&](int kt, auto more_t, auto more2_t) {
                 constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
                 const int st = kt & 1;
                 KS sn;
                 if (MORE2) sn = kstate(kt + 2);
-                bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
-                frags(ml_t, st, 0, fa0, fb0);
                 frags(ml_t, st, 1, fa1, fb1);
                 if (MORE) { sstore(st ^ 1, 0); if (MORE2) gload(sn, 0); }
                 __builtin_amdgcn_sched_barrier(0);
@@ -760,8 +762,15 @@ __device__ __forceinline__ void wide_tile(const BgArgs &A, const Group &Gr, int 
                 mma(ml_t, fa0, fb0);
                 if (MORE) { sstore(st ^ 1, 3); if (MORE2) gload(sn, 3); }
                 __builtin_amdgcn_sched_barrier(0);
-                mma(ml_t, fa1, fb1);
-                __syncthreads();
+                if (MORE) {
+                    __syncthreads();
+                    frags(ml_t, st ^ 1, 0, fa0, fb0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma(ml_t, fa1, fb1);
+                } else {
+                    mma(ml_t, fa1, fb1);
+                    __syncthreads();
+                }
             };
             int kt = 0;
             for (; kt + 2 < nk; ++kt) kstep(kt, yes{}, yes{});

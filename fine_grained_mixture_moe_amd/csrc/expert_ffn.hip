@@ -588,11 +588,16 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
             }
             // offsets of the step whose loads go out next (kt + 2 in the loop)
             KOff kn = koff(2);
+            // The fragments of sub-step 0 of each step are read at the end of the step
+            // before, under its last group of MFMAs: the barrier goes before that group
+            // (the step's reads of its own stage are complete by then, and the stores of
+            // the next stage are), so after it the waves do not all wait on LDS at once
+            // before their first MFMA.
+            bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
+            frags(ml_t, 0, 0, fa0, fb0);
             auto kstep = [&](int kt, auto more_t, auto more2_t) {
                 constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
                 const int st = kt & 1;
-                bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
-                frags(ml_t, st, 0, fa0, fb0);
                 frags(ml_t, st, 1, fa1, fb1);
                 if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kn, 0); }
                 __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
@@ -607,9 +612,16 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
                 mma(ml_t, fa0, fb0);
                 if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kn, 3); }
                 __builtin_amdgcn_sched_barrier(0);
-                mma(ml_t, fa1, fb1);
                 if (MORE2) kadvance(kn);
-                __syncthreads();
+                if (MORE) {
+                    __syncthreads();
+                    frags(ml_t, st ^ 1, 0, fa0, fb0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma(ml_t, fa1, fb1);
+                } else {
+                    mma(ml_t, fa1, fb1);
+                    __syncthreads();
+                }
             };
             int kt = 0;
             for (; kt + 2 < nk; ++kt) kstep(kt, yes{}, yes{});

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from fine_grained_mixture_moe_amd import workloads as W
-from fine_grained_mixture_moe_amd.layer import DeviceLayer
+from fine_grained_mixture_moe_amd.layer import DeviceLayer, to_device
 import parity as PT
 
 pytestmark = pytest.mark.gpu
@@ -174,3 +174,29 @@ def test_fused_ffn_equals_two_launches(case):
     assert np.array_equal(a["y_routed"], b["y_routed"])
     if Ks:
         assert np.array_equal(a["y_shared"], b["y_shared"])
+
+
+@pytest.mark.parametrize("accumulate", [False, True], ids=["gather", "accumulating"])
+def test_second_input_over_the_same_workspace(accumulate):
+    """The fused launch hands the SwiGLU activations between workgroups through the workspace and
+    reads them back as cached loads; a second call with other tokens (other routing, other
+    activations in the same rows of the workspace) must see its own activations, not lines left
+    in some XCD's L2 by the first call."""
+    import dataclasses
+    first = W.make_random_case(3000, 256, 1, 32, 6, 256, dtype="bf16", seed=34, zipf_s=1.1, groups=4)
+    other = W.make_random_case(3000, 256, 1, 32, 6, 256, dtype="bf16", seed=35, zipf_s=1.1, groups=4)
+    second = dataclasses.replace(first, x=other.x)
+    PT.say(f"[case] second input over the same workspace, accumulate={accumulate}")
+    dl = DeviceLayer(first, accumulate=accumulate)
+    dl.forward()
+    dl.check_status()
+    dl.x.copy_(to_device(second.x.device_bits("bf16"), "bf16", dl.x.device))
+    dl.inp = second
+    dl.forward()
+    dl.expert_sum()
+    g = dl.results()
+    o = PT.oracle_routing(second)
+    PT.check_routing(g, o, second.wl)
+    tokens = np.arange(second.wl.T, dtype=np.int32)
+    ref = PT.oracle_outputs(second, o["idx"], o["gate"], tokens)
+    PT.check_outputs(g, second, tokens, ref, "second input")
