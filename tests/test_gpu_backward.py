@@ -115,6 +115,12 @@ SMALL = [
     (200, 192, 0, 200, 16, 64, "bf16", 5, None, 8),
     (1, 64, 0, 8, 1, 64, "f32", 4, None, 1),
     (130, 64, 0, 1, 1, 64, "f32", 8, None, 1),
+    # 256 x 256 bf16 tiles: most experts empty (their weight gradients must be exact zeros)
+    (40, 128, 0, 64, 2, 128, "bf16", 9, None, 4),
+    # W2 segments of width 320 straddle the 256-wide tiles of da and dW2; shared width 640
+    (600, 192, 2, 8, 2, 320, "bf16", 10, None, 2),
+    # 750 rows per expert: three row runs of 256, 256 and 238 rows for da and the dx rows
+    (1500, 128, 1, 4, 2, 128, "bf16", 12, None, 2),
 ]
 
 
