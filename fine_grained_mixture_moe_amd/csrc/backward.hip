@@ -975,6 +975,14 @@ __global__ __launch_bounds__(256) void gather_dx_kernel(int T, int d, int K, con
                 for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
             }
     }
+    for (int k = kRouteMaxTopK; k < K; ++k) {   // K' beyond the routing kernels' limit (other routers)
+        const int sl = slot_of[(size_t)t * K + k];
+        if (sl < 0) continue;
+        float v[8];
+        load8(dxr + (size_t)sl * d + c, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
     store8(dx + (size_t)t * d + c, acc);
 }
 
