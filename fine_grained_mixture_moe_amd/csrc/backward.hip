@@ -32,8 +32,9 @@
 //   (both with an XCD-aware tile order, see bgemm_kernel)
 //   gather_dx_kernel     dx_ffn[t] = dxs[t] + sum_k dxr[slot_of[t,k]] (k order)
 //   router_dz_kernel     ds, dz per token (wave per token, lane = expert)
-//   router_dx_kernel     dx = dh + dx_ffn + dz E (LDS-tiled, 64 tokens x 64 columns)
-//   router_de_part/sum   dE, dbias partials over token chunks (x read once), then a fixed-order sum
+//   router_dx_kernel     dx = dh + dx_ffn + dz E (LDS-tiled, 128 tokens x 128 columns, 8 x 8 per thread)
+//   router_de_part/sum   dE, dbias partials over token chunks (8 columns x 4 or 8 experts per thread),
+//                        then a fixed-order sum
 //
 // Operands are staged through LDS; a "transposed" operand (stored with its
 // m index contiguous) is read into MFMA fragments with ds_read_b64_tr_b16:
@@ -1032,107 +1033,167 @@ __global__ __launch_bounds__(256) void router_dz_kernel(int T, int Nr, int K, in
     }
 }
 
-// dx = dh + dx_ffn + dz E.  Workgroup tile: 64 tokens x 64 columns, thread
-// (token group tg, column group cg) owns 4 tokens x 4 columns; dz rows of the
-// tile and E columns of the tile are staged in LDS; the sum over r runs in
-// ascending order.
-template <typename DT, int NJ>
+// dx = dh + dx_ffn + dz E.  Workgroup tile: 128 tokens x 128 columns, thread
+// (token group tg, column group cg) owns 8 tokens x 8 columns (64
+// accumulators: 4 LDS reads of 16 bytes per 64 fmas).  The expert dimension
+// goes through LDS 32 at a time: dz transposed to [r][t], E as [r][c]; every
+// output's sum over r runs in ascending order.
+template <typename DT>
 __global__ __launch_bounds__(256) void router_dx_kernel(int T, int d, int Nr, const DT *__restrict__ dh,
                                                         const float *__restrict__ dx_ffn,
                                                         const float *__restrict__ dz, const float *__restrict__ E,
                                                         float *__restrict__ dx) {
-    constexpr int NE = 64 * NJ;
-    __shared__ float s_dz[64][NE + 1];
-    __shared__ __attribute__((aligned(16))) float s_e[NE][64];
-    const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < 64 * NE; i += 256) {
-        const int tt = i / NE, r = i % NE;
-        s_dz[tt][r] = (t0 + tt < T && r < Nr) ? dz[(size_t)(t0 + tt) * Nr + r] : 0.0f;
-    }
-    for (int i = tid; i < NE * 16; i += 256) {
-        const int r = i / 16, c4 = (i % 16) * 4;
-        *(float4 *)&s_e[r][c4] = (r < Nr && c0 + c4 < d) ? *(const float4 *)(E + (size_t)r * d + c0 + c4)
-                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-    const int cg = tid & 15, tg = tid >> 4;
-    float acc[4][4];
+    __shared__ __attribute__((aligned(16))) float s_z[32][128];
+    __shared__ __attribute__((aligned(16))) float s_e[32][128];
+    const int t0 = blockIdx.x * 128, c0 = blockIdx.y * 128;
+    const int tid = threadIdx.x, cg = tid & 15, tg = tid >> 4;
+    float acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-    for (int r = 0; r < Nr; ++r) {
-        const float4 e4 = *(const float4 *)&s_e[r][cg * 4];
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    for (int r0 = 0; r0 < Nr; r0 += 32) {
+        // dz[t0 + t][r0 + 4q .. 4q + 3] -> s_z[4q + e][t]; E rows r0 .. r0 + 31 -> s_e
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float z = s_dz[tg * 4 + i][r];
-            acc[i][0] = __builtin_fmaf(z, e4.x, acc[i][0]);
-            acc[i][1] = __builtin_fmaf(z, e4.y, acc[i][1]);
-            acc[i][2] = __builtin_fmaf(z, e4.z, acc[i][2]);
-            acc[i][3] = __builtin_fmaf(z, e4.w, acc[i][3]);
+            const int t = tid & 127, q = (tid >> 7) + 2 * i;   // q: 0..7
+            const int r = r0 + 4 * q;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t0 + t < T) {
+                const float *src = dz + (size_t)(t0 + t) * Nr + r;
+                if ((Nr & 3) == 0 && r + 3 < Nr) v = *(const float4 *)src;   // 16-byte aligned rows
+                else {
+                    v.x = r < Nr ? src[0] : 0.f;
+                    v.y = r + 1 < Nr ? src[1] : 0.f;
+                    v.z = r + 2 < Nr ? src[2] : 0.f;
+                    v.w = r + 3 < Nr ? src[3] : 0.f;
+                }
+            }
+            s_z[4 * q][t] = v.x;
+            s_z[4 * q + 1][t] = v.y;
+            s_z[4 * q + 2][t] = v.z;
+            s_z[4 * q + 3][t] = v.w;
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, rr = idx >> 5, c4 = (idx & 31) * 4;
+            const int r = r0 + rr, c = c0 + c4;
+            *(float4 *)&s_e[rr][c4] = (r < Nr && c < d) ? *(const float4 *)(E + (size_t)r * d + c)
+                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        __syncthreads();
+        const int nr = min(32, Nr - r0);
+        for (int r = 0; r < nr; ++r) {
+            const float4 z0 = *(const float4 *)&s_z[r][tg * 8], z1 = *(const float4 *)&s_z[r][tg * 8 + 4];
+            const float4 e0 = *(const float4 *)&s_e[r][cg * 8], e1 = *(const float4 *)&s_e[r][cg * 8 + 4];
+            const float z[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+            const float e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(z[i], e[j], acc[i][j]);
+        }
+        __syncthreads();
     }
-    const int c = c0 + cg * 4;
-    if (c >= d) return;
+    const int c = c0 + cg * 8;
+    if (c >= d) return;   // d % 64 == 0: a thread's 8 columns are all inside or all outside
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + tg * 4 + i;
+    for (int i = 0; i < 8; ++i) {
+        const int t = t0 + tg * 8 + i;
         if (t >= T) continue;
-        float o[4];
+        float hv[8], fv[8], o[8];
+        load8(dh + (size_t)t * d + c, hv);
+        if (dx_ffn) load8(dx_ffn + (size_t)t * d + c, fv);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            o[j] = to_f(dh[(size_t)t * d + c + j]) + (dx_ffn ? dx_ffn[(size_t)t * d + c + j] : 0.0f) + acc[i][j];
-        *(float4 *)(dx + (size_t)t * d + c) = make_float4(o[0], o[1], o[2], o[3]);
+        for (int j = 0; j < 8; ++j) o[j] = (hv[j] + (dx_ffn ? fv[j] : 0.0f)) + acc[i][j];
+        store8(dx + (size_t)t * d + c, o);
     }
 }
 
-// dE partials over token chunks of kDeTokens: workgroup (chunk j, 64
-// columns); thread (column col, expert group eg) accumulates, t ascending,
-// dz[t, r] x[t, c] for its 16 NJ consecutive experts r = eg * 16 NJ + i,
-// reading each x value once; dz of the chunk is staged in LDS, read as
-// 16-byte broadcasts (a wave shares eg).  part[j][r][c], row pitch d + 4;
-// column d carries sum_t dz (the bias gradient).
+// dE partials over token chunks of kDeTokens: workgroup (chunk j, 16 RT
+// experts, 128 columns); thread (expert group eg, column group cg) owns RT
+// experts x 8 columns and accumulates, t ascending, dz[t, r] x[t, c]; the
+// chunk's dz rows and x rows (as fp32) go through LDS 32 tokens at a time.
+// part[j][r][c], row pitch d + 4; column d carries sum_t dz (the bias
+// gradient), from the workgroups of the first column tile.
 constexpr int kDeTokens = 128;
-template <typename DT, int NJ>
+template <typename DT, int RT>
 __global__ __launch_bounds__(256) void router_de_part_kernel(int T, int d, int Nr, const DT *__restrict__ x,
                                                              const float *__restrict__ dz,
                                                              float *__restrict__ part) {
-    constexpr int NE = 64 * NJ, PER = 16 * NJ;
-    __shared__ __attribute__((aligned(16))) float s_dz[kDeTokens][NE];
-    const int j = blockIdx.x, c0 = blockIdx.y * 64;
-    const int tid = threadIdx.x, col = tid & 63, eg = tid >> 6;
-    const int c = c0 + col;
-    const int t0 = j * kDeTokens, n = min(kDeTokens, T - t0);
-    for (int i = tid; i < kDeTokens * NE; i += 256) {
-        const int tt = i / NE, r = i % NE;
-        s_dz[tt][r] = (tt < n && r < Nr) ? dz[(size_t)(t0 + tt) * Nr + r] : 0.0f;
-    }
-    __syncthreads();
-    float acc[PER];
-    float bsum[PER];
+    constexpr int TR = 16 * RT;   // experts of the tile
+    __shared__ __attribute__((aligned(16))) float s_z[32][TR];
+    __shared__ __attribute__((aligned(16))) float s_x[32][128];
+    const int j = blockIdx.x, rt0 = blockIdx.z * TR, c0 = blockIdx.y * 128;
+    const int tid = threadIdx.x, cg = tid & 15, eg = tid >> 4;
+    const int tc0 = j * kDeTokens, n = min(kDeTokens, T - tc0);
+    float acc[RT][8];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) { acc[i] = 0.0f; bsum[i] = 0.0f; }
-    for (int tt = 0; tt < n; ++tt) {
-        const float xv = to_f(x[(size_t)(t0 + tt) * d + c]);
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int i = 0; i < PER; i += 4) {
-            const float4 z = *(const float4 *)&s_dz[tt][eg * PER + i];
-            acc[i] = __builtin_fmaf(z.x, xv, acc[i]);
-            acc[i + 1] = __builtin_fmaf(z.y, xv, acc[i + 1]);
-            acc[i + 2] = __builtin_fmaf(z.z, xv, acc[i + 2]);
-            acc[i + 3] = __builtin_fmaf(z.w, xv, acc[i + 3]);
-            bsum[i] += z.x; bsum[i + 1] += z.y; bsum[i + 2] += z.z; bsum[i + 3] += z.w;
+        for (int k = 0; k < 8; ++k) acc[i][k] = 0.0f;
+    float bsum = 0.0f;   // thread tid < TR of the first column tile: sum over t of dz[t, rt0 + tid]
+    for (int s0 = 0; s0 < n; s0 += 32) {
+        // dz rows of 32 tokens (TR experts each), x rows (128 columns) as fp32
+        for (int i = tid; i < 32 * TR / 4; i += 256) {
+            const int tt = i / (TR / 4), r4 = (i % (TR / 4)) * 4;
+            const int t = tc0 + s0 + tt, r = rt0 + r4;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (s0 + tt < n) {
+                const float *src = dz + (size_t)t * Nr + r;
+                if ((Nr & 3) == 0 && r + 3 < Nr) v = *(const float4 *)src;   // 16-byte aligned rows
+                else {
+                    v.x = r < Nr ? src[0] : 0.f;
+                    v.y = r + 1 < Nr ? src[1] : 0.f;
+                    v.z = r + 2 < Nr ? src[2] : 0.f;
+                    v.w = r + 3 < Nr ? src[3] : 0.f;
+                }
+            }
+            *(float4 *)&s_z[tt][r4] = v;
         }
-    }
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int r = eg * PER + i;
-        if (r >= Nr) continue;
-        float *o = part + ((size_t)j * Nr + r) * (d + 4);
-        o[c] = acc[i];
-        if (blockIdx.y == 0 && col == 0) o[d] = bsum[i];
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 256 * i, tt = idx >> 4, c8 = (idx & 15) * 8;
+            float v[8];
+            if (s0 + tt < n && c0 + c8 < d) load8(x + (size_t)(tc0 + s0 + tt) * d + c0 + c8, v);
+            else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+            }
+            *(float4 *)&s_x[tt][c8] = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4 *)&s_x[tt][c8 + 4] = make_float4(v[4], v[5], v[6], v[7]);
+        }
+        __syncthreads();
+        const int m = min(32, n - s0);
+        if (blockIdx.y == 0 && tid < TR)
+            for (int tt = 0; tt < m; ++tt) bsum += s_z[tt][tid];
+        for (int tt = 0; tt < m; ++tt) {
+            float z[RT], xv[8];
+#pragma unroll
+            for (int i = 0; i < RT; i += 4) {
+                const float4 z4 = *(const float4 *)&s_z[tt][eg * RT + i];
+                z[i] = z4.x; z[i + 1] = z4.y; z[i + 2] = z4.z; z[i + 3] = z4.w;
+            }
+            const float4 x0 = *(const float4 *)&s_x[tt][cg * 8], x1 = *(const float4 *)&s_x[tt][cg * 8 + 4];
+            xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
+            xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[i][k] = __builtin_fmaf(z[i], xv[k], acc[i][k]);
+        }
+        __syncthreads();
     }
+    const int c = c0 + cg * 8;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const int r = rt0 + eg * RT + i;
+        if (r >= Nr || c >= d) continue;
+        float *o = part + ((size_t)j * Nr + r) * (d + 4) + c;
+        *(float4 *)o = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        *(float4 *)(o + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+    }
+    if (blockIdx.y == 0 && tid < TR && rt0 + tid < Nr) part[((size_t)j * Nr + rt0 + tid) * (d + 4) + d] = bsum;
 }
 
 // dE[r][c] = sum_j part[j][r][c] (j ascending); dbias[r] = sum_j part[j][r][d].
@@ -1256,26 +1317,24 @@ hipError_t launch_route_backward(const moe_problem &p, int groups, float alpha1,
     if (p.T > 0) {
         router_dz_kernel<<<cdiv(p.T, 4), 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, alpha1, alpha2, probs, idx,
                                                       dgate, f, f_dev, dz);
-        const dim3 gx(cdiv(p.T, 64), cdiv(p.d, 64));
-        const int nj = cdiv(p.n_routed, 64);
-#define MOE_DX(DT, NJ) router_dx_kernel<DT, NJ><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const DT *)dh, dx_ffn, \
-                                                                   dz, centroids, dx)
-        if (p.dtype == MOE_BF16) {
-            if (nj == 1) MOE_DX(uint16_t, 1); else if (nj == 2) MOE_DX(uint16_t, 2); else MOE_DX(uint16_t, 4);
-        } else {
-            if (nj == 1) MOE_DX(float, 1); else if (nj == 2) MOE_DX(float, 2); else MOE_DX(float, 4);
-        }
-#undef MOE_DX
+        const dim3 gx(cdiv(p.T, 128), cdiv(p.d, 128));
+        if (p.dtype == MOE_BF16)
+            router_dx_kernel<uint16_t><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const uint16_t *)dh, dx_ffn, dz,
+                                                          centroids, dx);
+        else
+            router_dx_kernel<float><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const float *)dh, dx_ffn, dz,
+                                                       centroids, dx);
     }
     const int nchunk = cdiv(p.T, kDeTokens);
     if (nchunk > 0) {
-        const dim3 g(nchunk, cdiv(p.d, 64));
-        const int nj = cdiv(p.n_routed, 64);
-#define MOE_DE(DT, NJ) router_de_part_kernel<DT, NJ><<<g, 256, 0, s>>>(p.T, p.d, p.n_routed, (const DT *)x, dz, part)
+        // 64-expert tiles up to 64 routed experts, else 128-expert tiles
+        const bool small = p.n_routed <= 64;
+        const dim3 g(nchunk, cdiv(p.d, 128), cdiv(p.n_routed, small ? 64 : 128));
+#define MOE_DE(DT, RT) router_de_part_kernel<DT, RT><<<g, 256, 0, s>>>(p.T, p.d, p.n_routed, (const DT *)x, dz, part)
         if (p.dtype == MOE_BF16) {
-            if (nj == 1) MOE_DE(uint16_t, 1); else if (nj == 2) MOE_DE(uint16_t, 2); else MOE_DE(uint16_t, 4);
+            if (small) MOE_DE(uint16_t, 4); else MOE_DE(uint16_t, 8);
         } else {
-            if (nj == 1) MOE_DE(float, 1); else if (nj == 2) MOE_DE(float, 2); else MOE_DE(float, 4);
+            if (small) MOE_DE(float, 4); else MOE_DE(float, 8);
         }
 #undef MOE_DE
     }
