@@ -32,7 +32,8 @@
 //   (both with an XCD-aware tile order, see bgemm_kernel)
 //   gather_dx_kernel     dx_ffn[t] = dxs[t] + sum_k dxr[slot_of[t,k]] (k order)
 //   router_dz_kernel     ds, dz per token (wave per token, lane = expert)
-//   router_dx_kernel     dx = dh + dx_ffn + dz E (LDS-tiled, 128 tokens x 128 columns, 8 x 8 per thread)
+//   router_dx_kernel     dx = dh + dx_ffn + dz E (LDS-tiled, 128 or 64 tokens x 128 columns, 8 or 4 x 8
+//                        per thread)
 //   router_de_part/sum   dE, dbias partials over token chunks (8 columns x 4 or 8 experts per thread),
 //                        then a fixed-order sum
 //
@@ -1033,30 +1034,32 @@ __global__ __launch_bounds__(256) void router_dz_kernel(int T, int Nr, int K, in
     }
 }
 
-// dx = dh + dx_ffn + dz E.  Workgroup tile: 128 tokens x 128 columns, thread
-// (token group tg, column group cg) owns 8 tokens x 8 columns (64
-// accumulators: 4 LDS reads of 16 bytes per 64 fmas).  The expert dimension
-// goes through LDS 32 at a time: dz transposed to [r][t], E as [r][c]; every
-// output's sum over r runs in ascending order.
-template <typename DT>
+// dx = dh + dx_ffn + dz E.  Workgroup tile: 16 TPT tokens x 128 columns,
+// thread (token group tg, column group cg) owns TPT tokens x 8 columns (TPT =
+// 8: 64 accumulators, 4 LDS reads of 16 bytes per 64 fmas; TPT = 4 for small
+// batches, twice the workgroups).  The expert dimension goes through LDS 32
+// at a time: dz transposed to [r][t], E as [r][c]; every output's sum over r
+// runs in ascending order.
+template <typename DT, int TPT>
 __global__ __launch_bounds__(256) void router_dx_kernel(int T, int d, int Nr, const DT *__restrict__ dh,
                                                         const float *__restrict__ dx_ffn,
                                                         const float *__restrict__ dz, const float *__restrict__ E,
                                                         float *__restrict__ dx) {
-    __shared__ __attribute__((aligned(16))) float s_z[32][128];
+    constexpr int TT = 16 * TPT;   // tokens of the tile
+    __shared__ __attribute__((aligned(16))) float s_z[32][TT];
     __shared__ __attribute__((aligned(16))) float s_e[32][128];
-    const int t0 = blockIdx.x * 128, c0 = blockIdx.y * 128;
+    const int t0 = blockIdx.x * TT, c0 = blockIdx.y * 128;
     const int tid = threadIdx.x, cg = tid & 15, tg = tid >> 4;
-    float acc[8][8];
+    float acc[TPT][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TPT; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
     for (int r0 = 0; r0 < Nr; r0 += 32) {
         // dz[t0 + t][r0 + 4q .. 4q + 3] -> s_z[4q + e][t]; E rows r0 .. r0 + 31 -> s_e
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = tid & 127, q = (tid >> 7) + 2 * i;   // q: 0..7
+        for (int i = 0; i < TPT / 2; ++i) {
+            const int t = tid % TT, q = tid / TT + (256 / TT) * i;   // q: 0..7
             const int r = r0 + 4 * q;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (t0 + t < T) {
@@ -1084,12 +1087,16 @@ __global__ __launch_bounds__(256) void router_dx_kernel(int T, int d, int Nr, co
         __syncthreads();
         const int nr = min(32, Nr - r0);
         for (int r = 0; r < nr; ++r) {
-            const float4 z0 = *(const float4 *)&s_z[r][tg * 8], z1 = *(const float4 *)&s_z[r][tg * 8 + 4];
+            float z[TPT];
+#pragma unroll
+            for (int i = 0; i < TPT; i += 4) {
+                const float4 z4 = *(const float4 *)&s_z[r][tg * TPT + i];
+                z[i] = z4.x; z[i + 1] = z4.y; z[i + 2] = z4.z; z[i + 3] = z4.w;
+            }
             const float4 e0 = *(const float4 *)&s_e[r][cg * 8], e1 = *(const float4 *)&s_e[r][cg * 8 + 4];
-            const float z[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
             const float e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < TPT; ++i)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(z[i], e[j], acc[i][j]);
         }
@@ -1098,8 +1105,8 @@ __global__ __launch_bounds__(256) void router_dx_kernel(int T, int d, int Nr, co
     const int c = c0 + cg * 8;
     if (c >= d) return;   // d % 64 == 0: a thread's 8 columns are all inside or all outside
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = t0 + tg * 8 + i;
+    for (int i = 0; i < TPT; ++i) {
+        const int t = t0 + tg * TPT + i;
         if (t >= T) continue;
         float hv[8], fv[8], o[8];
         load8(dh + (size_t)t * d + c, hv);
@@ -1317,13 +1324,17 @@ hipError_t launch_route_backward(const moe_problem &p, int groups, float alpha1,
     if (p.T > 0) {
         router_dz_kernel<<<cdiv(p.T, 4), 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, alpha1, alpha2, probs, idx,
                                                       dgate, f, f_dev, dz);
-        const dim3 gx(cdiv(p.T, 128), cdiv(p.d, 128));
-        if (p.dtype == MOE_BF16)
-            router_dx_kernel<uint16_t><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const uint16_t *)dh, dx_ffn, dz,
-                                                          centroids, dx);
-        else
-            router_dx_kernel<float><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const float *)dh, dx_ffn, dz,
-                                                       centroids, dx);
+        // 64-token tiles while 128-token ones would leave fewer than two workgroups per CU
+        const bool small = (int64_t)cdiv(p.T, 128) * cdiv(p.d, 128) < 512;
+        const dim3 gx(cdiv(p.T, small ? 64 : 128), cdiv(p.d, 128));
+#define MOE_DX(DT, TPT) router_dx_kernel<DT, TPT><<<gx, 256, 0, s>>>(p.T, p.d, p.n_routed, (const DT *)dh, dx_ffn, \
+                                                                     dz, centroids, dx)
+        if (p.dtype == MOE_BF16) {
+            if (small) MOE_DX(uint16_t, 4); else MOE_DX(uint16_t, 8);
+        } else {
+            if (small) MOE_DX(float, 4); else MOE_DX(float, 8);
+        }
+#undef MOE_DX
     }
     const int nchunk = cdiv(p.T, kDeTokens);
     if (nchunk > 0) {
