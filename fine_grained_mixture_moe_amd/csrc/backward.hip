@@ -917,7 +917,13 @@ __device__ __forceinline__ void wide_run(const BgArgs &A, int lb, uint8_t *smem,
         g = group_at(lb);
         lt = spread(lb - s_pref[g], s_pref[g + 1] - s_pref[g]);
     }
-    const Group Gr = group_of(A, g);
+    // the group and tile are the same in every lane: in SGPRs, the buffer descriptors built from
+    // them are too (a descriptor in VGPRs puts a waterfall loop around every load that uses it)
+    g = __builtin_amdgcn_readfirstlane(g);
+    lt = __builtin_amdgcn_readfirstlane(lt);
+    Group Gr = group_of(A, g);
+    Gr.rows = __builtin_amdgcn_readfirstlane(Gr.rows);
+    Gr.roff = __builtin_amdgcn_readfirstlane(Gr.roff);
     int M, N, K;
     dims<MODE>(A, Gr, M, N, K);
     const int mt = cdiv(M, 256);
