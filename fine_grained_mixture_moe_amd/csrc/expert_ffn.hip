@@ -309,13 +309,16 @@ __global__ __launch_bounds__(256) void grouped_ffn_kernel(GemmParams P) {
 // bf16 path: 256 weight rows x BM tokens per tile, 64 k per step.
 //
 // LDS rows are 128 bytes (64 bf16) with no padding; the 16-byte chunk c of
-// row r lives at chunk c ^ (r & 7), so the 32 rows a fragment read touches
-// spread over all banks.  Two LDS stages: while the MFMAs consume stage s,
-// the registers already hold the next k step (issued one step earlier) and
-// are written to stage s^1 afterwards; one barrier per k step.  Global reads
-// are raw buffer loads: per-thread 32-bit row offsets are fixed for the
-// whole k loop and the k position is a scalar offset; rows outside the
-// group read as zero (range-checked loads), so no masking is needed.
+// row r lives at chunk c ^ (r & 7) ^ ((r >> 3) & 1), so the 32 rows a fragment
+// read touches spread over all banks.  Two LDS stages, filled by direct-to-LDS
+// buffer loads (no registers, no LDS store instructions; on a 64 KB-per-step
+// loop the LDS stores cost about a tenth of the MFMA rate, and their power
+// the shader clock): a step reads all its weight fragments first, so its
+// stage's weight rows are refilled with the step after next from the
+// barrier after its first MFMA group, and its token rows from the barrier
+// before its last group.  Per-thread 32-bit row offsets are fixed for the
+// whole k loop and the k position is a scalar offset; rows outside the group
+// read as zero (range-checked loads), so no masking is needed.
 // 8 waves (2 per SIMD, so one wave's LDS and memory latency hides behind
 // the other's MFMAs), laid out 2 (tokens) x 4 (weights): a wave owns 64
 // weight rows (2 blocks of 32) x BM/2 tokens (BM/64 blocks of 32).  In the
@@ -342,6 +345,42 @@ template <int AUX = 0>
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Direct-to-LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane L
+// writes LDS bytes [lds_base + 16 L, +16); lanes whose offset lies past the
+// descriptor's size write zeros.  The descriptor is four dwords in SGPRs (the
+// layout __builtin_amdgcn_make_buffer_rsrc builds).  Issued from inline asm: the
+// compiler does not track these loads, which keeps it from making later LDS
+// reads of the other stage wait for them (it cannot tell the stages apart); the
+// caller orders them with s_waitcnt vmcnt and barriers, and any wait the
+// compiler places for its own loads only counts more loads than it knows of.
+// The s_nop covers the hazard between the write of M0 and its read by the load.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc4(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r.x = (int)(uint32_t)a;
+    r.y = (int)((uint32_t)(a >> 32) & 0xffffu);
+    r.z = (int)bytes;
+    r.w = 0x00020000;
+    return r;
+}
+template <int AUX>
+__device__ __forceinline__ void dma16(i32x4 r, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+    static_assert(AUX == 0 || AUX == kNonTemporal, "cache policy of a direct-to-LDS load");
+    if constexpr (AUX == kNonTemporal)
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                     :
+                     : "{m0}"(lds_base), "v"(voff), "s"(r), "s"(soff)
+                     : "memory");
+    else
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "{m0}"(lds_base), "v"(voff), "s"(r), "s"(soff)
+                     : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
 template <int AUX = 0>
 __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint4 v) {
@@ -387,9 +426,15 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
     const int K = UP ? P.d : (shared ? P.Ks * P.w : P.w);
     const uint32_t xpitch = (uint32_t)K * 2u;   // token-side row bytes
     // ---- buffer resources and fixed per-thread offsets ----
-    const int part = tid & 7;               // logical 16-byte chunk of the row
+    const int part = tid & 7;               // physical 16-byte chunk of the row in LDS
     const int rsub = tid >> 3;              // row within a group of 64
-    __amdgpu_buffer_rsrc_t rw_a, rw_b, rx;
+    // Logical chunk c of row r sits at physical chunk c ^ (r & 7) ^ ((r >> 3) & 1)
+    // (an involution): any 8 consecutive rows, and any 16 consecutive rows split by
+    // parity, land on distinct 16-byte bank groups.  The stages are filled by
+    // direct-to-LDS loads, lane L of a wave writing the L-th 16 bytes after the
+    // wave's base, so the lane at physical chunk `part` fetches logical chunk swz.
+    const int swz = part ^ (rsub & 7) ^ ((rsub >> 3) & 1);
+    i32x4 rw_a, rw_b, rx;
     uint32_t ow[CW], ox[CX];
     int n_valid;                            // weight-side rows of this group
     uint32_t wpitch;
@@ -399,15 +444,15 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
         const uint8_t *b3 = shared ? P.wb_s : P.wb_r + (size_t)r * ebytes;
         n_valid = shared ? P.Ks * P.w : P.w;
         wpitch = (uint32_t)P.d * 2u;
-        rw_a = make_rsrc(b1, (uint32_t)((size_t)n_valid * wpitch));
-        rw_b = make_rsrc(b3, (uint32_t)((size_t)n_valid * wpitch));
-        rx = make_rsrc(P.x, (uint32_t)((size_t)P.T * P.d * 2));
+        rw_a = make_rsrc4(b1, (uint32_t)((size_t)n_valid * wpitch));
+        rw_b = make_rsrc4(b3, (uint32_t)((size_t)n_valid * wpitch));
+        rx = make_rsrc4(P.x, (uint32_t)((size_t)P.T * P.d * 2));
     } else {
         const size_t ebytes = (size_t)P.d * P.w * 2;
         const uint8_t *b2 = shared ? P.wa_s : P.wa_r + (size_t)r * ebytes;
         n_valid = P.d;
         wpitch = (uint32_t)P.w * 2u;
-        rw_a = make_rsrc(b2, (uint32_t)(shared ? (size_t)P.Ks * ebytes : ebytes));
+        rw_a = make_rsrc4(b2, (uint32_t)(shared ? (size_t)P.Ks * ebytes : ebytes));
         rw_b = rw_a;
         const uint8_t *xb = shared ? P.act_shared : P.act_routed;
         // the routed activations' region holds T*K' rows (a bound known without a
@@ -415,7 +460,7 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
         // every buffer load got a waterfall loop, and the k loop's first wait covered
         // that load's register)
         const size_t xrows = shared ? (size_t)P.T : (size_t)P.TK;
-        rx = make_rsrc(xb, (uint32_t)(xrows * xpitch));
+        rx = make_rsrc4(xb, (uint32_t)(xrows * xpitch));
     }
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
@@ -423,14 +468,8 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
         int wr;
         if (UP) wr = n_tile * 128 + (j & 127);           // W1 (j < 128) or W3 row
         else wr = n_tile * BN + j;                       // W2 row = output column
-        ow[i] = wr < n_valid ? (uint32_t)wr * wpitch + part * 16 : kOOB;
+        ow[i] = wr < n_valid ? (uint32_t)wr * wpitch + swz * 16 : kOOB;
     }
-    // physical chunk of logical chunk c in row r: c ^ (r & 7) ^ ((r >> 3) & 1).
-    // Any 8 consecutive rows, and any 16 consecutive rows split by parity,
-    // land on distinct 16-byte bank groups.
-    const int swz = part ^ (rsub & 7) ^ ((rsub >> 3) & 1);
-
-    uint4 sw[CW], sx[CX];
     // Byte offsets of k step kt in the weight rows and the token rows.  In the
     // down projection of the shared experts, k runs over the K_s segments
     // [d, w] of the stacked W2, w/64 steps per segment.  The k loop advances
@@ -471,27 +510,34 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
             o.kw = o.kx;
         }
     };
-    // part ph (0..3) of a k step: weight chunks [ph*CW/4, (ph+1)*CW/4), token chunks likewise
-    auto gload_part = [&](const KOff &o, int ph, bool wts = true, bool toks = true) {
-        const uint32_t kw = o.kw, kx = o.kx;
+    // The loads of k step o into stage stg, straight into LDS: instruction i of
+    // wave wv fills tile rows 64 i + 8 wv .. +7, 1 KB contiguous from the wave's
+    // base.  Rows past the operand (offset kOOB) are filled with zeros.  They
+    // count on vmcnt like any load: a wave waits for its own with s_waitcnt
+    // vmcnt, and a barrier after that wait publishes them to the others.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto dma = [&](const KOff &o, int stg, bool wts, bool toks) {
         if (wts) {
 #pragma unroll
             for (int i = 0; i < CW; ++i)
-                if (i * 4 / CW == ph) sw[i] = bload<WAUX>((UP && i >= CW / 2) ? rw_b : rw_a, ow[i], kw);
+                dma16<WAUX>((UP && i >= CW / 2) ? rw_b : rw_a, lds_addr(s_w[stg] + (64 * i + 8 * wv) * RB), ow[i], o.kw);
         }
         if (toks) {
 #pragma unroll
-            for (int i = 0; i < CX; ++i)
-                if (i * 4 / CX == ph) sx[i] = bload<0>(rx, ox[i], kx);
+            for (int i = 0; i < CX; ++i) dma16<0>(rx, lds_addr(s_x[stg] + (64 * i + 8 * wv) * RB), ox[i], o.kx);
         }
     };
-    auto sstore_part = [&](int stg, int ph) {
-#pragma unroll
-        for (int i = 0; i < CW; ++i)
-            if (i * 4 / CW == ph) *(uint4 *)(s_w[stg] + (rsub + 64 * i) * RB + swz * 16) = sw[i];
-#pragma unroll
-        for (int i = 0; i < CX; ++i)
-            if (i * 4 / CX == ph) *(uint4 *)(s_x[stg] + (rsub + 64 * i) * RB + swz * 16) = sx[i];
+    // Barrier that waits for this wave's LDS accesses and its direct-to-LDS loads
+    // except the newest VM of them (an immediate), not for more: __syncthreads'
+    // fence would wait for every outstanding load.  The empty asm statements keep
+    // the compiler from moving LDS accesses across it.
+    auto lds_sync = [&](auto vm_t) {
+        constexpr int VM = decltype(vm_t)::value;
+        static_assert(VM < 16, "vmcnt immediate");
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0070 | VM);   // vmcnt(VM) expcnt(7) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
 
     f32x16 acc[NB][MB];
@@ -517,18 +563,8 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
     const int ml = __builtin_amdgcn_readfirstlane(min(MB, (nblk - wm + 1) >> 1));
     const int lsw = (l32 & 7) ^ ((l32 >> 3) & 1);   // swizzle of every fragment row of this lane
 
-    // ML: live token blocks of the wave, a compile-time count so that the
-    // k loop stays straight-line code
-    auto frags = [&](auto ml_t, int stg, int ks, bf16x8 (&fa)[NB], bf16x8 (&fb)[MB]) {
-        constexpr int ML = decltype(ml_t)::value;
-        const int ch = ((2 * ks + lhi) ^ lsw) * 16;
-        if (ML > 0) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) fa[nb] = *(const bf16x8 *)(s_w[stg] + wrow[nb] * RB + ch);
-        }
-#pragma unroll
-        for (int mb = 0; mb < ML; ++mb) fb[mb] = *(const bf16x8 *)(s_x[stg] + xrow[mb] * RB + ch);
-    };
+    // ML (below): live token blocks of the wave, a compile-time count so that
+    // the k loop stays straight-line code
     auto mma = [&](auto ml_t, const bf16x8 (&fa)[NB], const bf16x8 (&fb)[MB]) {
         constexpr int ML = decltype(ml_t)::value;
 #pragma unroll
@@ -542,15 +578,11 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
     using no = std::false_type;
     const int nk = K / 64;
     {
-        // Stage kt&1 holds k step kt; the registers hold step kt+1.  During
-        // the 4 sub-steps of step kt, quarter ph of the registers is written
-        // to the other stage and refilled with step kt+2, between MFMAs.
-        // the weight rows of step 0 depend on the tile alone: their loads go
-        // out before the token sources are gathered (for the up projection a
-        // dependent global read), so the two latencies overlap
+        // The weight rows of step 0 depend on the tile alone: their loads go out
+        // before the token sources are gathered (for the up projection a dependent
+        // global read), so the two latencies overlap.
         const KOff k0 = koff(0);
-#pragma unroll
-        for (int ph = 0; ph < 4; ++ph) gload_part(k0, ph, true, false);
+        dma(k0, 0, true, false);
         if (tid < BM) {
             const int row = m0 + tid;
             int src = -1;
@@ -560,66 +592,77 @@ __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDes
             }
             s_src[tid] = src;
         }
-        __syncthreads();
+        lds_sync(std::integral_constant<int, 15>{});   // s_src written; the weight loads stay in flight
 #pragma unroll
         for (int i = 0; i < CX; ++i) {
             const int src = s_src[rsub + 64 * i];
-            ox[i] = src >= 0 ? (uint32_t)src * xpitch + part * 16 : kOOB;
+            ox[i] = src >= 0 ? (uint32_t)src * xpitch + swz * 16 : kOOB;
         }
-#pragma unroll
-        for (int ph = 0; ph < 4; ++ph) gload_part(k0, ph, false, true);
-#pragma unroll
-        for (int ph = 0; ph < 4; ++ph) sstore_part(0, ph);
-        __syncthreads();
-        // MORE: step kt+1 exists (store it), MORE2: step kt+2 exists (load it)
+        dma(k0, 0, false, true);
+        // step 1 into stage 1; then stage 0 complete (step 1's loads, issued after
+        // it, may stay in flight: vmcnt counts down in issue order)
+        if (nk > 1) {
+            dma(koff(1), 1, true, true);
+            lds_sync(std::integral_constant<int, CW + CX>{});
+        } else {
+            lds_sync(std::integral_constant<int, 0>{});
+        }
+        // MORE: step kt+1 exists (wait for its stage), MORE2: step kt+2 exists (load it)
         auto kloop = [&](auto ml_t) {
-            // The loads of step 1 go out here, in each variant of the loop (one per count of
-            // live token blocks), in the loop's own order (weights and tokens of each quarter
-            // in turn): issued once before the variants, into registers the variants then
-            // assigned differently, they left the full-tile loop waiting at its head for
-            // nearly all loads in flight, every step.
-            if (nk > 1) {
-                const KOff k1 = koff(1);
+            constexpr int ML = decltype(ml_t)::value;
+            // Stage kt&1 holds step kt; step kt+1's loads into the other stage are in
+            // flight.  A step reads all four of its weight fragments up front; the
+            // barrier after its first group of MFMAs then frees the stage's weight
+            // rows, and step kt+2's weight loads go out there, two steps ahead of
+            // their use.  The barrier before the step's last group (its fragments are
+            // in registers by then) waits for step kt+1, frees the token rows (step
+            // kt+2's token loads go out), and the next step's first fragments are
+            // read under that last group.
+            KOff kn = koff(2);   // the step whose loads go out next (kt + 2 in the loop)
+            bf16x8 fw[4][NB], fx0[MB], fx1[MB];
+            auto wfr = [&](int stg, int ks, bf16x8 (&fa)[NB]) {
+                if (ML > 0) {
+                    const int ch = ((2 * ks + lhi) ^ lsw) * 16;
 #pragma unroll
-                for (int ph = 0; ph < 4; ++ph) {
-                    gload_part(k1, ph);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int nb = 0; nb < NB; ++nb) fa[nb] = *(const bf16x8 *)(s_w[stg] + wrow[nb] * RB + ch);
                 }
-            }
-            // offsets of the step whose loads go out next (kt + 2 in the loop)
-            KOff kn = koff(2);
-            // The fragments of sub-step 0 of each step are read at the end of the step
-            // before, under its last group of MFMAs: the barrier goes before that group
-            // (the step's reads of its own stage are complete by then, and the stores of
-            // the next stage are), so after it the waves do not all wait on LDS at once
-            // before their first MFMA.
-            bf16x8 fa0[NB], fb0[MB], fa1[NB], fb1[MB];
-            frags(ml_t, 0, 0, fa0, fb0);
+            };
+            auto xfr = [&](int stg, int ks, bf16x8 (&fb)[MB]) {
+                const int ch = ((2 * ks + lhi) ^ lsw) * 16;
+#pragma unroll
+                for (int mb = 0; mb < ML; ++mb) fb[mb] = *(const bf16x8 *)(s_x[stg] + xrow[mb] * RB + ch);
+            };
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) wfr(0, ks, fw[ks]);
+            xfr(0, 0, fx0);
             auto kstep = [&](int kt, auto more_t, auto more2_t) {
                 constexpr bool MORE = decltype(more_t)::value, MORE2 = decltype(more2_t)::value;
                 const int st = kt & 1;
-                frags(ml_t, st, 1, fa1, fb1);
-                if (MORE) { sstore_part(st ^ 1, 0); if (MORE2) gload_part(kn, 0); }
-                __builtin_amdgcn_sched_barrier(0);  // keep the refill loads early
-                mma(ml_t, fa0, fb0);
-                frags(ml_t, st, 2, fa0, fb0);
-                if (MORE) { sstore_part(st ^ 1, 1); if (MORE2) gload_part(kn, 1); }
-                __builtin_amdgcn_sched_barrier(0);
-                mma(ml_t, fa1, fb1);
-                frags(ml_t, st, 3, fa1, fb1);
-                if (MORE) { sstore_part(st ^ 1, 2); if (MORE2) gload_part(kn, 2); }
-                __builtin_amdgcn_sched_barrier(0);
-                mma(ml_t, fa0, fb0);
-                if (MORE) { sstore_part(st ^ 1, 3); if (MORE2) gload_part(kn, 3); }
-                __builtin_amdgcn_sched_barrier(0);
-                if (MORE2) kadvance(kn);
+                xfr(st, 1, fx1);
+                mma(ml_t, fw[0], fx0);
+                // every wave has its weight fragments of this stage
+                lds_sync(std::integral_constant<int, 15>{});
+                if (MORE2) dma(kn, st, true, false);
+                xfr(st, 2, fx0);
+                mma(ml_t, fw[1], fx1);
+                xfr(st, 3, fx1);
+                mma(ml_t, fw[2], fx0);
                 if (MORE) {
-                    __syncthreads();
-                    frags(ml_t, st ^ 1, 0, fa0, fb0);
+                    // step kt+1 complete (step kt+2's weight loads may stay in flight)
+                    if (MORE2) lds_sync(std::integral_constant<int, CW>{});
+                    else lds_sync(std::integral_constant<int, 0>{});
+                    if (MORE2) {
+                        dma(kn, st, false, true);
+                        kadvance(kn);
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < 3; ++ks) wfr(st ^ 1, ks, fw[ks]);
+                    xfr(st ^ 1, 0, fx0);
                     __builtin_amdgcn_sched_barrier(0);
-                    mma(ml_t, fa1, fb1);
+                    mma(ml_t, fw[3], fx1);
+                    wfr(st ^ 1, 3, fw[3]);
                 } else {
-                    mma(ml_t, fa1, fb1);
+                    mma(ml_t, fw[3], fx1);
                     __syncthreads();
                 }
             };
