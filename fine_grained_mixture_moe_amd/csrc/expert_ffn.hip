@@ -398,8 +398,10 @@ struct TileDesc {
     int r, row_off, m0, nr, n_tile;
 };
 
-// WAUX: cache policy of the weight loads (0, or kNonTemporal when every expert's weights are
-// read by a single token tile).  ACC (down projection only): instead of writing y per grouped
+// WAUX: cache policy of the weight loads (0, or kNonTemporal for decode-sized batches, where
+// the routed experts average at most 64 rows and the shared group, if any, is one token tile:
+// most experts' weights are then read by a single tile; a skewed expert with more than one
+// tile re-reads them from memory).  ACC (down projection only): instead of writing y per grouped
 // row, add gate * y into the fp32 rows of y_acc of the rows' tokens.
 template <int BM, bool UP, bool BWD, bool FUSED, int WAUX = 0, bool ACC = false>
 __device__ __forceinline__ void ffn_tile_bf16(const GemmParams &P, const TileDesc td, uint8_t (&s_w)[2][256 * 128],
