@@ -53,12 +53,12 @@ inline int ffn_ctl_ints(const moe_problem &p) {
 }
 
 // Routing workgroups for T tokens of hidden size d (route.hip).
-int route_blocks(int T, int d);
+int route_blocks(int T, int d, int Nr);
 
 inline WsLayout ws_layout(const moe_problem &p) {
     WsLayout L{};
     const size_t nr = (size_t)p.n_routed;
-    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T, p.d) : 0;
+    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T, p.d, p.n_routed) : 0;
     const size_t pb = (size_t)cdiv(p.T, kPermuteTokens);
     const size_t es = dtype_bytes(p.dtype);
     size_t off = 0;
@@ -90,11 +90,11 @@ hipError_t route_scratch_ptr(void **ptr);
 // Bytes of the routing partials (counts, then fp64 sums) for p, laid out as
 // in the workspace: counts at 0, sums at route_psum_offset(p).
 inline size_t route_psum_offset(const moe_problem &p) {
-    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T, p.d) : 0;
+    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T, p.d, p.n_routed) : 0;
     return align_up(rb * (size_t)p.n_routed * sizeof(int32_t), 256);
 }
 inline size_t route_partial_bytes(const moe_problem &p) {
-    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T, p.d) : 0;
+    const size_t rb = p.T > 0 ? (size_t)route_blocks(p.T, p.d, p.n_routed) : 0;
     return route_psum_offset(p) + rb * (size_t)p.n_routed * sizeof(double);
 }
 

@@ -841,6 +841,194 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Logits on the matrix cores (batches beyond the decode path, 64 < N' <= 128,
+// d a multiple of 64).  v_mfma_f32_32x32x2_f32 adds to each output the product
+// of the k pair's first value (the operands of lanes 0-31) and then that of
+// its second (lanes 32-63), as two fused multiply-adds with one rounding
+// each: measured bit-identical to fmaf chains in ascending k, subnormal
+// values included.  A run of these instructions over the k pairs in
+// ascending order is therefore the same single fma chain over k = 0..d-1
+// from +0 as route_kernel's, at the matrix cores' fp32 rate.
+//   * a workgroup takes 32 tokens and every expert; wave e computes the
+//     32 x 32 block of experts 32e .. 32e+31 (EBK waves, N' <= 32 EBK);
+//   * each 64-deep k chunk of the token rows and the centroid rows is staged
+//     in LDS, two stages filled through registers a chunk ahead, every row
+//     split into its even and its odd k (lanes 0-31 take the even k of each
+//     pair, lanes 32-63 the odd one), so one 16-byte read of a lane feeds
+//     four instructions; rows are 272 bytes apart, so the rows of a read
+//     phase hit distinct 16-byte bank groups;
+//   * the logits then go through LDS into the lane-per-expert layout of the
+//     selection (finish_tokens, 8 tokens of a wave at a time), and the
+//     statistics are combined as in route_kernel (tokens in order within a
+//     wave, then the waves in order).
+// ---------------------------------------------------------------------------
+namespace rm {
+// Range-checked 16-byte loads: an offset at or past the buffer's size reads zeros.  No branch
+// guards a load, so the compiler keeps exact wait counts for the loads in flight.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+constexpr int TB = 32;              // tokens per workgroup
+constexpr int KC = 64;              // k per stage
+constexpr int PITCH = KC * 4 + 16;  // a row's 32 even k, its 32 odd k, a pad (bytes)
+}  // namespace rm
+
+template <int EBK, bool XB>
+__global__ __launch_bounds__(EBK * 64) void route_mfma_kernel(int T, int d, int Nr, int K, int skip, const void *x,
+                                                              const float *__restrict__ E,
+                                                              const float *__restrict__ bias,
+                                                              int32_t *__restrict__ idx, float *__restrict__ gate,
+                                                              float *__restrict__ probs,
+                                                              int32_t *__restrict__ part_counts,
+                                                              double *__restrict__ part_psum) {
+    using namespace rm;
+    constexpr int W = EBK, NT = W * 64, NE = 32 * EBK, NJ = (NE + 63) / 64;
+    constexpr int STAGE = (TB + NE) * PITCH;   // token rows, then centroid rows
+    constexpr int PR = XB ? KC / 8 : KC / 4;   // 16-byte token pieces per row and chunk
+    constexpr int XPT = TB * PR / NT;          // token pieces per thread
+    constexpr int EPT = NE * (KC / 4) / NT;    // centroid pieces per thread (4)
+    static_assert(TB * PR % NT == 0 && NE * (KC / 4) % NT == 0, "whole pieces per thread");
+    constexpr int ZP = NE + 4;                 // pitch (floats) of the logits tile
+    static_assert(TB * ZP * 4 <= 2 * STAGE && W * NJ * 64 * 12 <= 2 * STAGE, "tile and statistics fit");
+    __shared__ __attribute__((aligned(16))) uint8_t s_m[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int t0 = blockIdx.x * TB;
+    const int nchunk = d / KC;
+
+    // staging: token piece p = row p / PR, piece p % PR; centroid piece p = row p / 16, piece p % 16.
+    // Piece c of a row covers k = 4c..4c+3 (fp32; 8c..8c+7 for bf16 tokens): its even k go to
+    // [8c, 8c+8) of the row's even half (bf16: [16c, 16c+16)), its odd k to the same place + 128.
+    constexpr int XE = XB ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint32_t)((size_t)T * d * XE));
+    const __amdgpu_buffer_rsrc_t re = rsrc(E, (uint32_t)((size_t)Nr * d * 4));
+    uint32_t xo[XPT], eo[EPT];   // byte offsets of the pieces in chunk 0 (kOob: a row past the end)
+    int xd[XPT], ed[EPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int pc = tid + i * NT, r = pc / PR, c = pc % PR;
+        const int t = t0 + r;
+        xo[i] = t < T ? (uint32_t)(((size_t)t * d + (size_t)c * (16 / XE)) * XE) : kOob;
+        xd[i] = r * PITCH + c * (XB ? 16 : 8);
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int pc = tid + i * NT, r = pc / 16, c = pc % 16;
+        eo[i] = r < Nr ? (uint32_t)(((size_t)r * d + 4 * c) * 4) : kOob;   // rows of absent experts read zeros
+        ed[i] = (TB + r) * PITCH + c * 8;
+    }
+    uint4 xr[XPT], er[EPT];
+    auto load = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) xr[i] = ld16(rx, xo[i], (uint32_t)(c * KC * XE));
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) er[i] = ld16(re, eo[i], (uint32_t)(c * KC * 4));
+    };
+    // the 4 fp32 values of a piece: even k at p, p + 4, odd k at p + 128, p + 132
+    auto put4 = [](uint8_t *p, const uint4 &v) {
+        *(uint2 *)p = make_uint2(v.x, v.z);
+        *(uint2 *)(p + 128) = make_uint2(v.y, v.w);
+    };
+    auto store = [&](int st) {
+        uint8_t *b = s_m + st * STAGE;
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const uint4 v = xr[i];
+            if (XB) {   // 8 bf16 -> fp32 (exact): even k, then odd k
+                *(uint4 *)(b + xd[i]) = make_uint4(v.x << 16, v.y << 16, v.z << 16, v.w << 16);
+                *(uint4 *)(b + xd[i] + 128) =
+                    make_uint4(v.x & 0xffff0000u, v.y & 0xffff0000u, v.z & 0xffff0000u, v.w & 0xffff0000u);
+            } else {
+                put4(b + xd[i], v);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) put4(b + ed[i], er[i]);
+    };
+
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    // lane (l32, hi): token row l32 and centroid row 32 wave + l32, their hi-parity k
+    const int aoff = l32 * PITCH + hi * 128, boff = (TB + 32 * wave + l32) * PITCH + hi * 128;
+    // chunk c in stage c & 1; chunk c+1's loads go out before chunk c's MFMAs and are stored
+    // into the other stage after them
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+        if (c + 1 < nchunk) load(c + 1);
+        const uint8_t *b = s_m + (c & 1) * STAGE;
+#pragma unroll
+        for (int u = 0; u < KC / 8; ++u) {   // k pairs 4u .. 4u+3 of the chunk, in order
+            const float4 a4 = *(const float4 *)(b + aoff + 16 * u);
+            const float4 b4 = *(const float4 *)(b + boff + 16 * u);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, b4.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, b4.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, b4.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, b4.w, acc, 0, 0, 0);
+        }
+        if (c + 1 < nchunk) store((c + 1) & 1);
+        __syncthreads();
+    }
+
+    // the 32 x NE logits through LDS: register e of lane (l32, hi) holds token
+    // 8 (e / 4) + 4 hi + e % 4 and expert 32 wave + l32
+    float *s_z = (float *)s_m;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s_z[((e / 4) * 8 + hi * 4 + (e % 4)) * ZP + 32 * wave + l32] = acc[e];
+    __syncthreads();
+
+    constexpr int TPW = TB / W;               // tokens of each wave
+    constexpr int RR = TPW < 8 ? TPW : 8;     // tokens per selection round
+    double ps[NJ];
+    int cnt[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) { ps[j] = 0.0; cnt[j] = 0; }
+    for (int q = 0; q < TPW; q += RR) {
+        const int tl = wave * TPW + q;
+        const int tg = t0 + tl;
+        if (tg >= T) break;
+        float a[RR][NJ];
+#pragma unroll
+        for (int i = 0; i < RR; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int e = lane + 64 * j;
+                a[i][j] = e < NE ? s_z[(tl + i) * ZP + e] : 0.0f;
+            }
+        finish_tokens<RR, NJ>(tg, min(RR, T - tg), Nr, K, skip, lane, a, bias, idx, gate, probs, ps, cnt);
+    }
+
+    // the waves' per-expert sums, combined in wave order, at row blockIdx.x
+    __syncthreads();
+    double *s_ps = (double *)s_m;
+    int *s_cnt = (int *)(s_ps + W * NJ * 64);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        s_ps[wave * NJ * 64 + lane + 64 * j] = ps[j];
+        s_cnt[wave * NJ * 64 + lane + 64 * j] = cnt[j];
+    }
+    __syncthreads();
+    for (int r = tid; r < Nr; r += NT) {
+        double a = 0.0;
+        int cc = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) { a += s_ps[w * NJ * 64 + r]; cc += s_cnt[w * NJ * 64 + r]; }
+        part_psum[(size_t)blockIdx.x * Nr + r] = a;
+        part_counts[(size_t)blockIdx.x * Nr + r] = cc;
+    }
+}
+
 // Waves per workgroup and tokens per wave, from a sweep of (2, 4, 8) x
 // (1, 2, 4) on MI355X: 8 waves from 2048 tokens (one centroid chunk read
 // serves 8 waves), 4 below (more CUs stream the centroids for small
@@ -852,6 +1040,23 @@ int route_tokens_per_wave(int T) { return T >= 8192 ? 4 : T >= 4096 ? 2 : 1; }
 // Batches of at most this many tokens take the decode kernel (one workgroup per token).
 constexpr int kRouteDecodeTokens = 256;
 bool route_decode_path(int T, int d) { return T <= kRouteDecodeTokens && d <= kRouteDecodeMaxD; }
+// Batched tokens that take route_mfma_kernel: 65 to 128 experts (four 32-expert waves) and whole
+// 64-deep k chunks.  Measured against route_kernel (bf16 tokens, one box): T = 8192, d = 4096,
+// N' = 128: 231-255 -> 150 us.  With N' <= 64 (two waves per workgroup, less than a microsecond
+// of MFMAs per chunk) the chunk loads' latency dominates and route_kernel stays faster (T = 16384,
+// d = 1280, N' = 63: 61 -> 92 us; T = 4096, N' = 64: 25 -> 57 us).
+bool route_mfma_path(int T, int d, int Nr) {
+    return !route_decode_path(T, d) && Nr > 64 && Nr <= 128 && d % rm::KC == 0;
+}
+
+template <bool XB>
+void launch_route_mfma(const moe_problem &p, int skip, int nblk, const void *x, const float *E, const float *bias,
+                       int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
+#define MOE_L(EBK) route_mfma_kernel<EBK, XB><<<nblk, EBK * 64, 0, s>>>( \
+        p.T, p.d, p.n_routed, p.top_k, skip, x, E, bias, idx, gate, probs, pc, pp)
+    MOE_L(4);   // 65..128 experts: four waves (65..96 with a zero block: the staging splits evenly)
+#undef MOE_L
+}
 
 template <bool XB>
 void launch_route_decode(const moe_problem &p, int skip, const void *x, const float *E, const float *bias,
@@ -901,8 +1106,10 @@ void launch_route_typed(const moe_problem &p, int skip, int nblk, const void *x,
 
 }  // namespace
 
-int route_blocks(int T, int d) {
-    return route_decode_path(T, d) ? T : cdiv(T, route_waves(T) * route_tokens_per_wave(T));
+int route_blocks(int T, int d, int Nr) {
+    if (route_decode_path(T, d)) return T;
+    if (route_mfma_path(T, d, Nr)) return cdiv(T, rm::TB);
+    return cdiv(T, route_waves(T) * route_tokens_per_wave(T));
 }
 
 // ---------------------------------------------------------------------------
@@ -941,9 +1148,15 @@ hipError_t route_scratch_ptr(void **ptr) {
 hipError_t launch_route(const moe_problem &p, int skip, const void *x, const float *centroids, const float *bias,
                         int32_t *idx, float *gate, float *probs, int32_t *part_counts, double *part_psum,
                         int32_t *counts, float *prob_sum, hipStream_t s) {
-    const int nblk = p.T > 0 ? route_blocks(p.T, p.d) : 0;
+    const int nblk = p.T > 0 ? route_blocks(p.T, p.d, p.n_routed) : 0;
     if (nblk > 0) {
-        if (route_decode_path(p.T, p.d)) {
+        if (route_mfma_path(p.T, p.d, p.n_routed)) {
+            if (p.dtype == MOE_BF16)
+                launch_route_mfma<true>(p, skip, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
+            else
+                launch_route_mfma<false>(p, skip, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum,
+                                         s);
+        } else if (route_decode_path(p.T, p.d)) {
             if (p.dtype == MOE_BF16)
                 launch_route_decode<true>(p, skip, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
             else

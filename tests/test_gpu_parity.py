@@ -63,6 +63,8 @@ SMALL = [
     (256, 320, 0, 256, 16, 64, "f32", 31, 1.1, 8),     # decode routing: four waves, fp32 tokens, 10 chunks
     (33, 64, 1, 130, 5, 64, "bf16", 32, None, 5),      # decode routing: three waves, 2 chunks (< ring depth)
     (3, 8192, 0, 64, 4, 64, "bf16", 33, None, 4),      # decode routing: token row beyond one staging batch
+    (1000, 192, 0, 100, 6, 64, "bf16", 35, 1.1, 4),    # matrix-core logits: ragged T, 100 experts (partial 4th block)
+    (777, 128, 1, 96, 5, 64, "f32", 36, None, 4),      # matrix-core logits, fp32 tokens: 96 experts, empty 4th block
 ]
 
 
