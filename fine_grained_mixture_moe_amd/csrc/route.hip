@@ -11,9 +11,12 @@
 //
 // Logits.  Every z_{t,r} is ONE fused multiply-add chain over k = 0..d-1 in
 // ascending order starting from +0, so the value - and therefore the
-// selected experts - is reproducible bit for bit on any IEEE host.  No MFMA
-// and no split of k: both would change the summation order.  The work is
-// T*N' independent chains of length d:
+// selected experts - is reproducible bit for bit on any IEEE host.  No split
+// of k: it would change the summation order.  For 65 to 128 experts the
+// chains run on the matrix cores (route_mfma_kernel below: an fp32 MFMA adds
+// each product as a fused multiply-add of its own, in k order); otherwise,
+// and for decode batches, on the VALU.  The VALU work is T*N' independent
+// chains of length d:
 //   * lane = expert (l + 64 j for j < NJ), a wave owns RT consecutive tokens,
 //     so each lane runs RT*NJ independent chains;
 //   * the centroids are staged in LDS in chunks of 32 KB (KC values of k for
