@@ -658,27 +658,84 @@ __global__ __launch_bounds__(W * 64) void route_kernel(int T, int d, int Nr, int
 // Decode batches (few tokens): one workgroup per token and NW = ceil(N'/64)
 // waves, wave w running the chains of experts 64w + lane.  Every lane's
 // chain is sequential in k (the fixed fma order), so with few tokens the
-// work is T*N' chains of d dependent fmas and the time is the chain length:
-// each chain should own a SIMD slot and never wait for operands.
+// work is T*N' chains of d dependent fmas and the time is the chain length,
+// as long as a wave issues little besides its fmas and never waits for data.
 //   * Centroids: each wave streams its 64 expert rows in chunks of CK = 32 k
-//     (8 KB).  A chunk is loaded with row-contiguous 16-byte pieces (one
-//     load instruction covers 8 whole 128-byte row segments, so the vector
-//     cache sees 8 lines per instruction instead of 64 for a lane-per-row
-//     load), kept NBUF - 1 chunks ahead in a ring of registers, and passed
-//     through a private two-stage LDS buffer of the wave, rows 144 bytes
-//     apart, from which each lane reads its own row (16 lanes of a read hit
-//     16 distinct 4-bank groups).  The stages belong to one wave, whose LDS
-//     operations run in order, so no barrier is needed.
-//   * Token: the row is converted to fp32 once into LDS and each step's 4
-//     values are read at one address by all lanes (a broadcast).
+//     (8 KB) straight into LDS (buffer_load ... lds: no staging registers, no
+//     LDS stores), S stages per wave, S - 2 chunks ahead of the one being
+//     read, so that several chunks per wave are in flight against the memory
+//     latency.  Load instruction i of a chunk fills rows 8i .. 8i+7 (1 KB,
+//     lane L the 16 bytes at 16 L); the 16-byte piece q of row r sits at
+//     piece q ^ (r & 7) ^ ((r >> 3) & 1) of the row, so the 16 lanes of a
+//     row-wise read phase (rows r .. r+15 at one q) hit 16 distinct 4-bank
+//     groups.  A wave waits for its own loads only (vmcnt): the waves of a
+//     workgroup do not synchronise inside the k loop.
+//   * Token: the row is converted to fp32 once into LDS; each chunk's values
+//     are read at one address by all lanes (a broadcast).
+//   * The LDS reads of chunk c+1 are interleaved with the fmas of chunk c
+//     (after each half of them, the next chunk's pieces of that half, in
+//     descending order), so every read is a whole chunk of fmas ahead of its
+//     use, 8 reads are in flight at each wait (the counter holds 15), and a
+//     chunk takes two waits.
 // The logits of the NW waves meet in LDS and wave 0 runs the same softmax
 // and Top-K' as the batched kernel.  The partial statistics go to row
 // `token` of the partials (nblk = T).
 constexpr int kRouteDecodeMaxD = 16384;
-constexpr int kDecodeCK = 32;                       // k per chunk
-constexpr int kDecodePitch = kDecodeCK * 4 + 16;    // LDS row pitch (bytes)
-constexpr int kDecodeStage = 64 * kDecodePitch;     // one chunk of one wave
-template <int NW, bool XB>
+constexpr int kDecodeCK = 32;                          // k per chunk
+constexpr int kDecodeChunk = 64 * kDecodeCK * 4;       // bytes of one chunk of one wave
+constexpr size_t kDecodeLdsMax = 160 * 1024 - 1024;    // dynamic LDS budget (the logits take the rest)
+// dynamic LDS of the decode kernel: NW waves x S stages, then the token row as fp32 and a zero chunk
+constexpr size_t decode_lds_bytes(int NW, int S, int d) {
+    return (size_t)NW * S * kDecodeChunk + ((size_t)d + kDecodeCK) * 4;
+}
+// stages per wave: as many as fit, up to 8 (at most 6 chunks, 48 loads, in flight)
+int decode_stages(int NW, int d) {
+    for (int S = 8; S >= 4; S -= 2)
+        if (decode_lds_bytes(NW, S, d) <= kDecodeLdsMax) return S;
+    return 0;
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// Buffer descriptor (four dwords, the layout __builtin_amdgcn_make_buffer_rsrc
+// builds): base, no stride, `bytes` in range; offsets at or past it read zeros.
+__device__ __forceinline__ i32x4_t decode_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4_t r;
+    r.x = (int)(uint32_t)a;
+    r.y = (int)((uint32_t)(a >> 32) & 0xffffu);
+    r.z = (int)bytes;
+    r.w = 0x00020000;
+    return r;
+}
+// Four loads of 16 bytes per lane straight into LDS: load i (immediate offset
+// 1024 i) lane L writes LDS bytes [lds + 1024 i + 16 L, +16) and reads memory
+// at voff[i] + soff + 1024 i (the immediate offset moves both addresses, so
+// voff[i] carries -1024 i).  Inline asm, so the compiler neither tracks nor
+// waits for them; the kernel waits for its own loads with s_waitcnt vmcnt.
+// The s_nop is the wait state between the write of M0 and its first read.
+__device__ __forceinline__ void decode_dma16x4(i32x4_t rsrc, uint32_t lds, const uint32_t *voff, uint32_t soff) {
+    asm volatile("s_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+                 "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+                 :
+                 : "{m0}"(lds), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+__device__ __forceinline__ uint32_t decode_lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+// s_waitcnt vmcnt(VM), no wait on the other counters
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt immediate");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+template <int NW, int S, bool XB>
 __global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int Nr, int K, int skip, const void *x,
                                                                const float *__restrict__ E,
                                                                const float *__restrict__ bias,
@@ -686,43 +743,48 @@ __global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int
                                                                float *__restrict__ probs,
                                                                int32_t *__restrict__ part_counts,
                                                                double *__restrict__ part_psum) {
+    static_assert(S >= 4 && S % 2 == 0 && 8 * (S - 2) < 64, "stages: even, 4..8");
     constexpr int CK = kDecodeCK;
     constexpr int NQ = CK / 4;       // 16-byte pieces of a row segment; also load instructions per chunk
-    // dynamic LDS: [NW waves][2 stages][64 rows][kDecodePitch bytes], then the token row [d] fp32
+    // dynamic LDS: [NW waves][S stages][64 rows][128 bytes], then the token row [d] fp32 and CK zeros
     extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
     __shared__ float s_z[NW * 64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = blockIdx.x;
-    float *s_x = (float *)(s_dyn + NW * 2 * kDecodeStage);
-    uint8_t *stg0 = s_dyn + wave * 2 * kDecodeStage;
-    const int nch = d / CK;          // d % 64 == 0
-    // load piece (lane & 7) of row 8i + (lane >> 3) of the wave's 64 rows: rows past N' repeat row N'-1
-    const int prow = lane >> 3, ppc = lane & 7;
-    // (a native vector type: copies of the HIP uint4 struct become memcpys that
-    // kept the ring in scratch memory)
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 r0[NQ], r1[NQ], r2[NQ], r3[NQ];
-    auto dld = [&](int c, u32x4 (&b)[NQ]) {
-        const int o = min(c, nch - 1) * CK + 4 * ppc;
+    const int nch = d / CK;          // d % 64 == 0: even, at least 2
+    float *s_x = (float *)(s_dyn + (size_t)NW * S * kDecodeChunk);
+    const uint8_t *const stg0 = s_dyn + (size_t)wave * S * kDecodeChunk;   // this wave's stages
+    const uint32_t lds0 = decode_lds_addr(stg0);
+
+    // load instruction i of a chunk: row 8i + (lane >> 3) (rows past N' repeat row N'-1),
+    // physical piece lane & 7, which holds logical piece q
+    const i32x4_t re = decode_rsrc(E, (uint32_t)((size_t)Nr * d * 4));
+    uint32_t voff[NQ];
 #pragma unroll
-        for (int i = 0; i < NQ; ++i)
-            b[i] = *(const u32x4 *)(E + (size_t)min(wave * 64 + 8 * i + prow, Nr - 1) * d + o);
+    for (int i = 0; i < NQ; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const int q = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 1);
+        // less the immediate offset of load i within its group of four (row r >= 8 i, so the
+        // value stays positive)
+        voff[i] = (uint32_t)(((size_t)min(wave * 64 + r, Nr - 1) * d + 4 * q) * 4) - 1024u * (i & 3);
+    }
+    // loads 4h .. 4h+3 of chunk c (clamped: the loads past the last chunk repeat it, so every
+    // step issues the same number of loads and the vmcnt waits stay exact) into stage stg
+    auto dma = [&](int c, int stg, int h) {
+        decode_dma16x4(re, lds0 + stg * kDecodeChunk + 4096 * h, voff + 4 * h, (uint32_t)min(c, nch - 1) * (CK * 4));
     };
-    uint8_t *const dst0 = stg0 + prow * kDecodePitch + ppc * 16;
-    auto dst = [&](int stg, const u32x4 (&b)[NQ]) {
-        uint8_t *dd = dst0 + stg * kDecodeStage;
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) *(u32x4 *)(dd + 8 * i * kDecodePitch) = b[i];
-    };
-#define MOE_DLD(c, b) dld((c), b);
-#define MOE_DST(stg, b) dst((stg), b);
-    // the token row, as fp32, into LDS: the first batch of its 16-byte pieces
-    // is loaded before the first centroid chunks go out (loads complete in
-    // order, so the stores wait for the token pieces only), further batches
-    // (long rows) afterwards
+    for (int s = 0; s < S - 1; ++s) {
+        dma(s, s, 0);
+        dma(s, s, 1);
+    }
+
+    // the token row, as fp32, into LDS (its loads go out after the chunks' and the first wait
+    // for them covers the chunks too; with SB pieces per thread at most 8 (S - 1) + SB <= 60
+    // loads are outstanding)
     {
-        constexpr int NT = NW * 64, SB = 8;
+        constexpr int NT = NW * 64, SB = 4;
         const int n16 = d * (XB ? 2 : 4) / 16;     // 16-byte pieces of the row
         const uint4 *xr = (const uint4 *)((const uint8_t *)x + (size_t)t * d * (XB ? 2 : 4));
         auto put = [&](int i, const uint4 v) {
@@ -740,61 +802,62 @@ __global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int
 #pragma unroll
         for (int u = 0; u < SB; ++u)
             if (tid + u * NT < n16) v[u] = xr[tid + u * NT];
-        __builtin_amdgcn_sched_barrier(0);
-        MOE_DLD(0, r0)
-        MOE_DLD(1, r1)
-        MOE_DLD(2, r2)
-        MOE_DLD(3, r3)
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < SB; ++u)
             if (tid + u * NT < n16) put(tid + u * NT, v[u]);
         for (int i = tid + SB * NT; i < n16; i += NT) put(i, xr[i]);
+        if (tid < CK / 4) *(float4 *)(s_x + d + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    MOE_DST(0, r0)
+    wait_vmcnt<0>();
     __syncthreads();
+
+    // the lane's row: logical piece q at physical piece q ^ sw
+    const int sw = (lane & 7) ^ ((lane >> 3) & 1);
+    uint32_t eo[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) eo[q] = (uint32_t)(lane * 128 + 16 * (q ^ sw));
+    float4 e[2][NQ], xv[2][NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        e[0][q] = *(const float4 *)(stg0 + eo[q]);
+        xv[0][q] = *(const float4 *)(s_x + 4 * q);
+    }
     float acc = 0.0f;
-    // chunk c: stage c & 1 holds it; the ring register set (c+1) % 4 holds
-    // chunk c+1, the others chunks c+2, c+3; the free set takes chunk c+4.
-    // The lane's row of the chunk and the token values are read from LDS,
-    // the fmas run in k order, then chunk c+1 goes to the other stage.
-    const uint8_t *myrow = stg0 + lane * kDecodePitch;
-    auto chunk = [&](int c) {
-        float4 e[NQ], xv[NQ];
-        const uint8_t *er = myrow + (c & 1) * kDecodeStage;
-        const float *xs = s_x + c * CK;
+    // step c (stage j = c % S, register set j & 1): chunk c+1 is in its stage once the loads
+    // after it, chunks c+2 .. c+S-2, are the only ones outstanding; its reads go out between the
+    // fma groups of chunk c; chunk c+S-1 then refills the stage of chunk c-1, read a step ago.
+    auto step = [&](auto jt, int c) {
+        constexpr int j = decltype(jt)::value, P = j & 1, N = P ^ 1;
+        constexpr int SN = (j + 1) % S, SF = (j + S - 1) % S;
+        wait_vmcnt<8 * (S - 3)>();
+        const float *xs = s_x + min(c + 1, nch) * CK;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            e[q] = *(const float4 *)(er + 16 * q);
-            xv[q] = *(const float4 *)(xs + 4 * q);
-        }
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            acc = __builtin_fmaf(xv[q].x, e[q].x, acc);
-            acc = __builtin_fmaf(xv[q].y, e[q].y, acc);
-            acc = __builtin_fmaf(xv[q].z, e[q].z, acc);
-            acc = __builtin_fmaf(xv[q].w, e[q].w, acc);
+            for (int q = 4 * h; q < 4 * h + 4; ++q) {
+                acc = __builtin_fmaf(xv[P][q].x, e[P][q].x, acc);
+                acc = __builtin_fmaf(xv[P][q].y, e[P][q].y, acc);
+                acc = __builtin_fmaf(xv[P][q].z, e[P][q].z, acc);
+                acc = __builtin_fmaf(xv[P][q].w, e[P][q].w, acc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // in descending q: the first fma of the half then waits for all of them at once
+#pragma unroll
+            for (int q = 4 * h + 3; q >= 4 * h; --q) {
+                xv[N][q] = *(const float4 *)(xs + 4 * q);
+                __builtin_amdgcn_sched_barrier(0);
+                e[N][q] = *(const float4 *)(stg0 + SN * kDecodeChunk + eo[q]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            dma(c + S - 1, SF, h);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
-#define MOE_DSTEP(c, cur, nxt)                          \
-    {                                                   \
-        MOE_DLD((c) + 4, cur)                           \
-        __builtin_amdgcn_sched_barrier(0);              \
-        if ((c) < nch) chunk(c);                        \
-        asm volatile("" : "+v"(acc));                   \
-        __builtin_amdgcn_sched_barrier(0);              \
-        MOE_DST(((c) + 1) & 1, nxt)                     \
-        __builtin_amdgcn_sched_barrier(0);              \
-    }
-    for (int c = 0; c < nch; c += 4) {
-        MOE_DSTEP(c, r0, r1)
-        MOE_DSTEP(c + 1, r1, r2)
-        MOE_DSTEP(c + 2, r2, r3)
-        MOE_DSTEP(c + 3, r3, r0)
-    }
-#undef MOE_DSTEP
-#undef MOE_DLD
-#undef MOE_DST
+    // whole rounds of S steps, no branch inside: steps past the last chunk add x = 0 (the zero
+    // chunk after the token row) times a copy of the last centroid chunk, which leaves acc as it is
+    for (int c0 = 0; c0 < nch; c0 += S)
+        for_each_step([&](auto jt) { step(jt, c0 + decltype(jt)::value); }, std::make_integer_sequence<int, S>{});
+    wait_vmcnt<0>();   // the loads past the last chunk land before the workgroup's LDS is released
     s_z[wave * 64 + lane] = acc;
     __syncthreads();
     if (wave != 0) return;
@@ -1042,14 +1105,17 @@ int route_waves(int T) { return T >= 2048 ? 8 : 4; }
 int route_tokens_per_wave(int T) { return T >= 8192 ? 4 : T >= 4096 ? 2 : 1; }
 // Batches of at most this many tokens take the decode kernel (one workgroup per token).
 constexpr int kRouteDecodeTokens = 256;
-bool route_decode_path(int T, int d) { return T <= kRouteDecodeTokens && d <= kRouteDecodeMaxD; }
+// ... and whose LDS stages fit (decode_stages); N' up to 256.
+bool route_decode_path(int T, int d, int Nr) {
+    return T <= kRouteDecodeTokens && d <= kRouteDecodeMaxD && decode_stages(cdiv(Nr, 64), d) > 0;
+}
 // Batched tokens that take route_mfma_kernel: 65 to 128 experts (four 32-expert waves) and whole
 // 64-deep k chunks.  Measured against route_kernel (bf16 tokens, one box): T = 8192, d = 4096,
 // N' = 128: 231-255 -> 150 us.  With N' <= 64 (two waves per workgroup, less than a microsecond
 // of MFMAs per chunk) the chunk loads' latency dominates and route_kernel stays faster (T = 16384,
 // d = 1280, N' = 63: 61 -> 92 us; T = 4096, N' = 64: 25 -> 57 us).
 bool route_mfma_path(int T, int d, int Nr) {
-    return !route_decode_path(T, d) && Nr > 64 && Nr <= 128 && d % rm::KC == 0;
+    return !route_decode_path(T, d, Nr) && Nr > 64 && Nr <= 128 && d % rm::KC == 0;
 }
 
 template <bool XB>
@@ -1061,16 +1127,41 @@ void launch_route_mfma(const moe_problem &p, int skip, int nblk, const void *x, 
 #undef MOE_L
 }
 
+template <int NW, int S, bool XB>
+hipError_t launch_decode_form(const moe_problem &p, int skip, const void *x, const float *E, const float *bias,
+                              int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
+    const size_t lds = decode_lds_bytes(NW, S, p.d);
+    // dynamic LDS beyond 64 KB: raise the kernel's limit (set once per form; the largest d wins)
+    static size_t granted = 0;
+    static std::mutex mu;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (lds > granted) {
+            const hipError_t e = hipFuncSetAttribute((const void *)route_decode_kernel<NW, S, XB>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            granted = lds;
+        }
+    }
+    route_decode_kernel<NW, S, XB><<<p.T, NW * 64, lds, s>>>(p.T, p.d, p.n_routed, p.top_k, skip, x, E, bias, idx,
+                                                             gate, probs, pc, pp);
+    return hipGetLastError();
+}
+
 template <bool XB>
-void launch_route_decode(const moe_problem &p, int skip, const void *x, const float *E, const float *bias,
-                         int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
-#define MOE_L(NW) route_decode_kernel<NW, XB><<<p.T, NW * 64, (size_t)NW * 2 * kDecodeStage + (size_t)p.d * sizeof(float), s>>>( \
-        p.T, p.d, p.n_routed, p.top_k, skip, x, E, bias, idx, gate, probs, pc, pp)
-    switch (cdiv(p.n_routed, 64)) {
-        case 1: MOE_L(1); break;
-        case 2: MOE_L(2); break;
-        case 3: MOE_L(3); break;
-        default: MOE_L(4); break;
+hipError_t launch_route_decode(const moe_problem &p, int skip, const void *x, const float *E, const float *bias,
+                               int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
+    const int nw = cdiv(p.n_routed, 64);
+#define MOE_L(NW, S) return launch_decode_form<NW, S, XB>(p, skip, x, E, bias, idx, gate, probs, pc, pp, s)
+    switch (nw * 16 + decode_stages(nw, p.d)) {
+        case 1 * 16 + 8: MOE_L(1, 8);
+        case 2 * 16 + 8: MOE_L(2, 8);
+        case 2 * 16 + 6: MOE_L(2, 6);
+        case 2 * 16 + 4: MOE_L(2, 4);
+        case 3 * 16 + 6: MOE_L(3, 6);
+        case 3 * 16 + 4: MOE_L(3, 4);
+        case 4 * 16 + 4: MOE_L(4, 4);
+        default: return hipErrorInvalidValue;   // route_decode_path excludes every other form
     }
 #undef MOE_L
 }
@@ -1110,7 +1201,7 @@ void launch_route_typed(const moe_problem &p, int skip, int nblk, const void *x,
 }  // namespace
 
 int route_blocks(int T, int d, int Nr) {
-    if (route_decode_path(T, d)) return T;
+    if (route_decode_path(T, d, Nr)) return T;
     if (route_mfma_path(T, d, Nr)) return cdiv(T, rm::TB);
     return cdiv(T, route_waves(T) * route_tokens_per_wave(T));
 }
@@ -1159,11 +1250,13 @@ hipError_t launch_route(const moe_problem &p, int skip, const void *x, const flo
             else
                 launch_route_mfma<false>(p, skip, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum,
                                          s);
-        } else if (route_decode_path(p.T, p.d)) {
-            if (p.dtype == MOE_BF16)
-                launch_route_decode<true>(p, skip, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
-            else
-                launch_route_decode<false>(p, skip, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
+        } else if (route_decode_path(p.T, p.d, p.n_routed)) {
+            const hipError_t e =
+                p.dtype == MOE_BF16
+                    ? launch_route_decode<true>(p, skip, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s)
+                    : launch_route_decode<false>(p, skip, x, centroids, bias, idx, gate, probs, part_counts, part_psum,
+                                                 s);
+            if (e != hipSuccess) return e;
         } else if (p.dtype == MOE_BF16) {
             launch_route_typed<true>(p, skip, nblk, x, centroids, bias, idx, gate, probs, part_counts, part_psum, s);
         } else {

@@ -58,11 +58,14 @@ SMALL = [
     (16400, 64, 0, 48, 2, 64, "f32", 21, None, 4),     # routing: d below one chunk (no full chunk)
     (1000, 448, 0, 64, 6, 64, "bf16", 27, None, 4),    # routing, 4-set load ring: 7 chunks (a partial group)
     (900, 320, 0, 128, 8, 64, "f32", 28, None, 4),     # routing, 4-set load ring, readlane form: 10 chunks
-    (64, 2048, 2, 64, 6, 64, "bf16", 29, None, 4),     # decode routing: one wave per token, 64 chunks
-    (128, 4096, 4, 128, 12, 64, "bf16", 30, None, 4),  # decode routing: two waves per token
-    (256, 320, 0, 256, 16, 64, "f32", 31, 1.1, 8),     # decode routing: four waves, fp32 tokens, 10 chunks
-    (33, 64, 1, 130, 5, 64, "bf16", 32, None, 5),      # decode routing: three waves, 2 chunks (< ring depth)
+    (64, 2048, 2, 64, 6, 64, "bf16", 29, None, 4),     # decode routing: one wave per token, 8 stages, 64 chunks
+    (128, 4096, 4, 128, 12, 64, "bf16", 30, None, 4),  # decode routing: two waves per token, 8 stages each
+    (256, 320, 0, 256, 16, 64, "f32", 31, 1.1, 8),     # decode routing: four waves, 4 stages, 10 chunks + 2 past the end
+    (33, 64, 1, 130, 5, 64, "bf16", 32, None, 5),      # decode routing: three waves, 6 stages, 2 chunks (< prefetch depth)
     (3, 8192, 0, 64, 4, 64, "bf16", 33, None, 4),      # decode routing: token row beyond one staging batch
+    (64, 2112, 1, 64, 6, 64, "bf16", 37, 1.1, 4),      # decode routing: 66 chunks, a partial round of 8 stages
+    (5, 8192, 0, 100, 4, 64, "bf16", 38, None, 4),     # decode routing: two waves, 6 stages (d past 8-stage LDS)
+    (2, 16384, 0, 128, 8, 64, "f32", 39, None, 4),     # decode routing: two waves, 4 stages, the largest d
     (1000, 192, 0, 100, 6, 64, "bf16", 35, 1.1, 4),    # matrix-core logits: ragged T, 100 experts (partial 4th block)
     (777, 128, 1, 96, 5, 64, "f32", 36, None, 4),      # matrix-core logits, fp32 tokens: 96 experts, empty 4th block
 ]
