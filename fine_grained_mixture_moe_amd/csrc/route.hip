@@ -854,7 +854,8 @@ __global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int
         }
     };
     // whole rounds of S steps, no branch inside: steps past the last chunk add x = 0 (the zero
-    // chunk after the token row) times a copy of the last centroid chunk, which leaves acc as it is
+    // chunk after the token row) times a copy of the last centroid chunk, which leaves acc as it
+    // is (for finite centroids; acc is never -0, as the chain starts from +0)
     for (int c0 = 0; c0 < nch; c0 += S)
         for_each_step([&](auto jt) { step(jt, c0 + decltype(jt)::value); }, std::make_integer_sequence<int, S>{});
     wait_vmcnt<0>();   // the loads past the last chunk land before the workgroup's LDS is released
