@@ -13,6 +13,9 @@ d=1280, same weights) is timed alongside under "pair" (--no-pair skips it).
 Other workloads: --config.  --accumulate runs moe_expert_ffn in its
 accumulating mode (gate-weighted sum inside the down projection, no y_routed).
 
+"layer_forward" times the same pass as one moe_layer_forward call (decode
+batches: four kernels instead of seven; other batches: the five calls' kernels).
+
 Timing: W warm-up steps, then K steps between two device synchronisations
 (value, ms_per_step); then a separate loop of max(K, 50) steps (200 for
 decode batches) with an event pair around each step gives the median and the
@@ -243,6 +246,29 @@ def run(args) -> dict:
     torch.cuda.synchronize()
     breakdown = {s: round(sum(m[j].elapsed_time(m[j + 1]) for m in marks) / n_b, 4) for j, s in enumerate(stages)}
 
+    # the same pass as one moe_layer_forward call (decode batches: four kernels instead of seven)
+    lf = None
+    if wl.n_routed and not dl.accumulate:
+        for _ in range(3):
+            dl.layer_forward()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dl.layer_forward()
+        torch.cuda.synchronize()
+        lf_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in lev:
+            a.record(stream)
+            dl.layer_forward()
+            b.record(stream)
+        torch.cuda.synchronize()
+        lper = sorted(a.elapsed_time(b) for a, b in lev)
+        dl.check_status()
+        lf = {"ms_per_step": round(lf_ms, 4), "median_ms": round(lper[len(lper) // 2], 4),
+              "min_ms": round(lper[0], 4), "tokens_per_s": round(wl.T / (lf_ms * 1e-3), 1),
+              "layer_hbm_gbs": round(layer_bytes(wl, counts) / (lf_ms * 1e-3) / 1e9, 1)}
+
     if args.copy_probe:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -298,6 +324,7 @@ def run(args) -> dict:
         "active_mfma_frac": round(tflops / mfma_peak, 4),
         "layer_hbm_gbs": round(layer_bytes(wl, counts) / (ms * 1e-3) / 1e9, 1),
         "stage_ms": breakdown,
+        "layer_forward": lf,
         "roofline": roof,
         "device": device_info(),
     }

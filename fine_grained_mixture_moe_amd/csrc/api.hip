@@ -49,6 +49,52 @@ int check_ws(const moe_problem *p, const void *ws, size_t ws_bytes, WsLayout *L)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Argument checks of moe_route_ablate (moe_route: disabled_top = 0).
+int check_route(const moe_problem *p, int32_t disabled_top, const void *x, const float *centroids,
+                const int32_t *idx, const float *gate, const int32_t *counts, const float *prob_sum, const void *ws,
+                size_t ws_bytes, WsLayout *L) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (p->n_routed < 1 || disabled_top < 0) return MOE_ERR_INVALID_ARG;
+    if (disabled_top + p->top_k > p->n_routed) return MOE_ERR_INVALID_ARG;
+    if (p->n_routed > kRouteMaxExperts || disabled_top + p->top_k > kRouteMaxTopK) return MOE_ERR_UNSUPPORTED;
+    if (!centroids || !counts || !prob_sum) return MOE_ERR_INVALID_ARG;
+    if (p->T > 0 && (!x || !idx || !gate)) return MOE_ERR_INVALID_ARG;
+    if ((x && !aligned16(x)) || !aligned16(centroids)) return MOE_ERR_INVALID_ARG;
+    return check_ws(p, ws, ws_bytes, L);
+}
+
+// Argument checks of moe_permute.
+int check_permute(const moe_problem *p, const int32_t *idx, const int32_t *offsets, const int32_t *sorted_token,
+                  const int32_t *slot_of, const void *ws, size_t ws_bytes, WsLayout *L) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (!offsets) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)p->T * p->top_k > 0 && (!idx || !sorted_token || !slot_of)) return MOE_ERR_INVALID_ARG;
+    return check_ws(p, ws, ws_bytes, L);
+}
+
+// Argument checks of moe_combine (with T > 0).
+int check_combine(const moe_problem *p, const void *x, const void *y_routed, const float *y_shared,
+                  const float *gate, const int32_t *slot_of, const void *h) {
+    if (!x || !h) return MOE_ERR_INVALID_ARG;
+    if (p->top_k > 0 && y_routed && (!gate || !slot_of)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(h) || (y_routed && !aligned16(y_routed)) ||
+        (y_shared && !aligned16(y_shared)))
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+// Argument checks of moe_balance_stats.
+int check_stats(const moe_problem *p, int32_t groups, const int32_t *counts, const float *prob_sum, const float *f,
+                const float *P, const float *f_dev, const float *P_dev, const float *exp_bal, const float *dev_bal) {
+    int rc = check_problem(p);
+    if (rc != MOE_OK) return rc;
+    if (p->n_routed < 1 || groups < 1 || p->n_routed % groups != 0) return MOE_ERR_INVALID_ARG;
+    if (!counts || !prob_sum || !f || !P || !f_dev || !P_dev || !exp_bal || !dev_bal) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
 uint8_t *at(void *ws, size_t off) { return (uint8_t *)ws + off; }
 
 }  // namespace
@@ -81,16 +127,9 @@ int moe_workspace_size(const moe_problem *p, size_t *bytes) {
 int moe_route_ablate(const moe_problem *p, int32_t disabled_top, const void *x, const float *centroids,
                      const float *bias, int32_t *idx, float *gate, float *probs, int32_t *counts, float *prob_sum,
                      void *ws, size_t ws_bytes, void *stream) {
-    int rc = check_problem(p);
-    if (rc != MOE_OK) return rc;
-    if (p->n_routed < 1 || disabled_top < 0) return MOE_ERR_INVALID_ARG;
-    if (disabled_top + p->top_k > p->n_routed) return MOE_ERR_INVALID_ARG;
-    if (p->n_routed > kRouteMaxExperts || disabled_top + p->top_k > kRouteMaxTopK) return MOE_ERR_UNSUPPORTED;
-    if (!centroids || !counts || !prob_sum) return MOE_ERR_INVALID_ARG;
-    if (p->T > 0 && (!x || !idx || !gate)) return MOE_ERR_INVALID_ARG;
-    if ((x && !aligned16(x)) || !aligned16(centroids)) return MOE_ERR_INVALID_ARG;
     WsLayout L;
-    if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
+    const int rc = check_route(p, disabled_top, x, centroids, idx, gate, counts, prob_sum, ws, ws_bytes, &L);
+    if (rc != MOE_OK) return rc;
     return hip_status(launch_route(*p, disabled_top, x, centroids, bias, idx, gate, probs,
                                    (int32_t *)at(ws, L.route_counts), (double *)at(ws, L.route_psum), counts,
                                    prob_sum, (hipStream_t)stream));
@@ -130,12 +169,9 @@ int moe_route_hash(const moe_problem *p, const int32_t *token_ids, int32_t *idx,
 
 int moe_permute(const moe_problem *p, const int32_t *idx, int32_t *offsets, int32_t *sorted_token,
                 int32_t *slot_of, void *ws, size_t ws_bytes, void *stream) {
-    int rc = check_problem(p);
-    if (rc != MOE_OK) return rc;
-    if (!offsets) return MOE_ERR_INVALID_ARG;
-    if ((int64_t)p->T * p->top_k > 0 && (!idx || !sorted_token || !slot_of)) return MOE_ERR_INVALID_ARG;
     WsLayout L;
-    if ((rc = check_ws(p, ws, ws_bytes, &L)) != MOE_OK) return rc;
+    const int rc = check_permute(p, idx, offsets, sorted_token, slot_of, ws, ws_bytes, &L);
+    if (rc != MOE_OK) return rc;
     return hip_status(launch_permute(*p, idx, offsets, sorted_token, slot_of, (int32_t *)at(ws, L.perm_hist),
                                      (int32_t *)at(ws, L.perm_base), (hipStream_t)stream));
 }
@@ -282,23 +318,72 @@ int moe_combine(const moe_problem *p, const void *x, const void *y_routed, const
     int rc = check_problem(p);
     if (rc != MOE_OK) return rc;
     if (p->T == 0) return MOE_OK;
-    if (!x || !h) return MOE_ERR_INVALID_ARG;
-    if (p->top_k > 0 && y_routed && (!gate || !slot_of)) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(h) || (y_routed && !aligned16(y_routed)) ||
-        (y_shared && !aligned16(y_shared)))
-        return MOE_ERR_INVALID_ARG;
+    if ((rc = check_combine(p, x, y_routed, y_shared, gate, slot_of, h)) != MOE_OK) return rc;
     return hip_status(launch_combine(*p, x, y_routed, y_shared, gate, slot_of, h, (hipStream_t)stream));
 }
 
 int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *counts, const float *prob_sum,
                       float *f, float *P, float *f_dev, float *P_dev, float *exp_bal, float *dev_bal,
                       void *stream) {
-    int rc = check_problem(p);
+    const int rc = check_stats(p, groups, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, dev_bal);
     if (rc != MOE_OK) return rc;
-    if (p->n_routed < 1 || groups < 1 || p->n_routed % groups != 0) return MOE_ERR_INVALID_ARG;
-    if (!counts || !prob_sum || !f || !P || !f_dev || !P_dev || !exp_bal || !dev_bal) return MOE_ERR_INVALID_ARG;
     return hip_status(launch_balance_stats(*p, groups, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, dev_bal,
                                            (hipStream_t)stream));
+}
+
+int moe_layer_forward(const moe_problem *p, int32_t groups, const moe_layer_io *io, void *ws, size_t ws_bytes,
+                      void *stream) {
+    if (!io) return MOE_ERR_INVALID_ARG;
+    WsLayout L;
+    bool routed = false, shared = false;
+    int rc = check_route(p, 0, io->x, io->centroids, io->idx, io->gate, io->counts, io->prob_sum, ws, ws_bytes, &L);
+    if (rc == MOE_OK)
+        rc = check_permute(p, io->idx, io->offsets, io->sorted_token, io->slot_of, ws, ws_bytes, &L);
+    if (rc == MOE_OK)
+        rc = check_ffn(p, true, true, io->x, io->offsets, io->sorted_token, io->w1_routed, io->w3_routed,
+                       io->w2_routed, io->w1_shared, io->w3_shared, io->w2_shared, io->y_routed, io->y_shared, ws,
+                       ws_bytes, &L, &routed, &shared);
+    if (rc == MOE_OK && p->T > 0)
+        rc = check_combine(p, io->x, io->y_routed, io->y_shared, io->gate, io->slot_of, io->h);
+    if (rc == MOE_OK)
+        rc = check_stats(p, groups, io->counts, io->prob_sum, io->f, io->P, io->f_dev, io->P_dev, io->exp_bal,
+                         io->dev_bal);
+    if (rc != MOE_OK) return rc;
+    // decode batches: routing, the one-workgroup tail (partials summed, statistics, grouping, the
+    // FFN's control words), the fused FFN without its preparation kernel, the combine
+    if (routed && p->T <= kPermuteTokens && route_decode_batch(*p)) {
+        hipStream_t s = (hipStream_t)stream;
+        int32_t *pc = (int32_t *)at(ws, L.route_counts);
+        double *pp = (double *)at(ws, L.route_psum);
+        int32_t *ctl = (int32_t *)at(ws, L.ffn_ctl);
+        const moe_problem q = active_part(*p, routed, shared);
+        hipError_t e = launch_route(*p, 0, io->x, io->centroids, io->bias, io->idx, io->gate, io->probs, pc, pp,
+                                    io->counts, io->prob_sum, s, /*reduce=*/false);
+        if (e == hipSuccess)
+            e = launch_layer_decode_tail(*p, groups, pc, pp, io->counts, io->prob_sum, io->idx, io->offsets,
+                                         io->sorted_token, io->slot_of, io->f, io->P, io->f_dev, io->P_dev,
+                                         io->exp_bal, io->dev_bal, ctl, ffn_ctl_ints(q), s);
+        const FfnArgs a = ffn_args(io->x, io->offsets, io->sorted_token, io->w1_routed, io->w3_routed, io->w2_routed,
+                                   io->w1_shared, io->w3_shared, io->w2_shared, io->y_routed, io->y_shared, ws, L);
+        if (e == hipSuccess) e = launch_expert_ffn(q, a, ctl, s, /*prep=*/false);
+        if (e == hipSuccess)
+            e = launch_combine(*p, io->x, io->y_routed, io->y_shared, io->gate, io->slot_of, io->h, s);
+        return hip_status(e);
+    }
+    // other batches: the five calls (their checks have passed above)
+    if ((rc = moe_route(p, io->x, io->centroids, io->bias, io->idx, io->gate, io->probs, io->counts, io->prob_sum,
+                        ws, ws_bytes, stream)) != MOE_OK)
+        return rc;
+    if ((rc = moe_permute(p, io->idx, io->offsets, io->sorted_token, io->slot_of, ws, ws_bytes, stream)) != MOE_OK)
+        return rc;
+    if ((rc = moe_expert_ffn(p, io->x, io->offsets, io->sorted_token, io->w1_routed, io->w3_routed, io->w2_routed,
+                             io->w1_shared, io->w3_shared, io->w2_shared, io->y_routed, io->y_shared, io->gate,
+                             io->slot_of, ws, ws_bytes, stream)) != MOE_OK)
+        return rc;
+    if ((rc = moe_combine(p, io->x, io->y_routed, io->y_shared, io->gate, io->slot_of, io->h, stream)) != MOE_OK)
+        return rc;
+    return moe_balance_stats(p, groups, io->counts, io->prob_sum, io->f, io->P, io->f_dev, io->P_dev, io->exp_bal,
+                             io->dev_bal, stream);
 }
 
 // ---------------------------------------------------------------------------

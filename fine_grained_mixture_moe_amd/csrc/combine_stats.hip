@@ -96,18 +96,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int K, const
     store8(h + (size_t)t * d + c, acc);
 }
 
-// One workgroup of 256 threads.  f and f' are exact functions of integer
-// counts (fp64 quotient rounded once to fp32); ExpBal and DevBal are fp64
-// sums: strided per-thread sums, a butterfly within each wave, then the four
-// wave sums in order (a fixed order, so deterministic).
-__device__ __forceinline__ double block_sum4(double v, double *s_w) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
-}
-
+// One workgroup of 256 threads (balance_stats_block, moe_internal.h).
 __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K, int D,
                                                             const int32_t *__restrict__ counts,
                                                             const float *__restrict__ prob_sum,
@@ -116,42 +105,7 @@ __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K
                                                             float *__restrict__ P_dev,
                                                             float *__restrict__ exp_bal,
                                                             float *__restrict__ dev_bal) {
-    __shared__ double s_a[4], s_b[4];
-    __shared__ double s_P[kPermuteMaxExperts];
-    __shared__ int s_c[kPermuteMaxExperts];
-    const int gsz = Nr / D;
-    double eb = 0.0, db = 0.0;
-    for (int r = threadIdx.x; r < Nr; r += 256) {
-        const int c = counts[r];
-        const double fr = T > 0 ? ((double)Nr * (double)c) / ((double)K * (double)T) : 0.0;
-        const double pr = T > 0 ? (double)prob_sum[r] / (double)T : 0.0;
-        const float ff = (float)fr, pf = (float)pr;
-        f[r] = ff;
-        P[r] = pf;
-        s_P[r] = pr;
-        s_c[r] = c;
-        eb += (double)ff * (double)pf;
-    }
-    __syncthreads();
-    for (int g = threadIdx.x; g < D; g += 256) {
-        int64_t C = 0;
-        double ps = 0.0;
-        for (int r = g * gsz; r < (g + 1) * gsz; ++r) {
-            C += s_c[r];
-            ps += s_P[r];
-        }
-        const double fg = T > 0 ? ((double)Nr * (double)C) / ((double)K * (double)T * (double)gsz) : 0.0;
-        const float ff = (float)fg, pf = (float)ps;
-        f_dev[g] = ff;
-        P_dev[g] = pf;
-        db += (double)ff * (double)pf;
-    }
-    const double e_all = block_sum4(eb, s_a);
-    const double d_all = block_sum4(db, s_b);
-    if (threadIdx.x == 0) {
-        *exp_bal = (float)e_all;
-        *dev_bal = (float)d_all;
-    }
+    balance_stats_block(T, Nr, K, D, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, dev_bal);
 }
 
 }  // namespace

@@ -1380,8 +1380,8 @@ hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_
     return launch_typed<float, false>(p, a, s);
 }
 
-hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s) {
-    hipError_t e = launch_prep(p, a, ctl, s);
+hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s, bool prep) {
+    hipError_t e = prep ? launch_prep(p, a, ctl, s) : hipSuccess;
     const bool active = p.T > 0 && (p.n_shared > 0 || (p.n_routed > 0 && p.top_k > 0));
     if (e != hipSuccess || !active) return e;
     if (p.dtype == MOE_BF16) return launch_fused(p, a, ctl, s);

@@ -75,12 +75,74 @@ inline WsLayout ws_layout(const moe_problem &p) {
     return L;
 }
 
+// ---- balance statistics of one workgroup (moe_balance_stats, and the decode tail of
+//      moe_layer_forward): "[ACL 2024] DeepSeekMoE: 混合专家语言模型中的极致专家特化",
+//      section "Method details: formulas and load balance" (expert- and device-level balance
+//      losses), with the symbols of "【论文总结】MoE" sections 2.3 and 2.4 ----
+// One workgroup of 256 threads.  f and f' are exact functions of integer
+// counts (fp64 quotient rounded once to fp32); ExpBal and DevBal are fp64
+// sums: strided per-thread sums, a butterfly within each wave, then the four
+// wave sums in order (a fixed order, so deterministic).
+__device__ __forceinline__ double stats_block_sum4(double v, double *s_w) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+}
+
+__device__ inline void balance_stats_block(int T, int Nr, int K, int D, const int32_t *counts,
+                                           const float *prob_sum, float *__restrict__ f,
+                                           float *__restrict__ P, float *__restrict__ f_dev,
+                                           float *__restrict__ P_dev, float *__restrict__ exp_bal,
+                                           float *__restrict__ dev_bal) {
+    __shared__ double s_a[4], s_b[4];
+    __shared__ double s_P[kPermuteMaxExperts];
+    __shared__ int s_c[kPermuteMaxExperts];
+    const int gsz = Nr / D;
+    double eb = 0.0, db = 0.0;
+    for (int r = threadIdx.x; r < Nr; r += 256) {
+        const int c = counts[r];
+        const double fr = T > 0 ? ((double)Nr * (double)c) / ((double)K * (double)T) : 0.0;
+        const double pr = T > 0 ? (double)prob_sum[r] / (double)T : 0.0;
+        const float ff = (float)fr, pf = (float)pr;
+        f[r] = ff;
+        P[r] = pf;
+        s_P[r] = pr;
+        s_c[r] = c;
+        eb += (double)ff * (double)pf;
+    }
+    __syncthreads();
+    for (int g = threadIdx.x; g < D; g += 256) {
+        int64_t C = 0;
+        double ps = 0.0;
+        for (int r = g * gsz; r < (g + 1) * gsz; ++r) {
+            C += s_c[r];
+            ps += s_P[r];
+        }
+        const double fg = T > 0 ? ((double)Nr * (double)C) / ((double)K * (double)T * (double)gsz) : 0.0;
+        const float ff = (float)fg, pf = (float)ps;
+        f_dev[g] = ff;
+        P_dev[g] = pf;
+        db += (double)ff * (double)pf;
+    }
+    const double e_all = stats_block_sum4(eb, s_a);
+    const double d_all = stats_block_sum4(db, s_b);
+    if (threadIdx.x == 0) {
+        *exp_bal = (float)e_all;
+        *dev_bal = (float)d_all;
+    }
+}
+
 // ---- launchers (each returns hipSuccess or the launch error) -------------
 
+// reduce = false leaves the partials unsummed (moe_layer_forward's decode tail sums them)
 hipError_t launch_route(const moe_problem &p, int skip, const void *x, const float *centroids,
                         const float *bias, int32_t *idx, float *gate, float *probs,
                         int32_t *part_counts, double *part_psum,
-                        int32_t *counts, float *prob_sum, hipStream_t s);
+                        int32_t *counts, float *prob_sum, hipStream_t s, bool reduce = true);
+// True when the routing of p takes the decode kernel (one workgroup per token, nblk = T).
+bool route_decode_batch(const moe_problem &p);
 
 // Allocation-free routing: bytes of the static device scratch that holds the
 // routing partials, and its address on the current device (taken once per
@@ -104,6 +166,15 @@ hipError_t launch_route_hash(const moe_problem &p, const int32_t *token_ids, int
 hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *offsets,
                           int32_t *sorted_token, int32_t *slot_of, int32_t *hist,
                           int32_t *base, hipStream_t s);
+// The decode tail of moe_layer_forward (T <= kPermuteTokens, decode routing, T K' > 0): one
+// workgroup sums the routing partials of the T decode workgroups into counts and prob_sum (the
+// order of route_reduce_kernel), runs the balance statistics on them, groups the pairs (the
+// single-block permute) and clears the nctl control words of the fused expert FFN.
+hipError_t launch_layer_decode_tail(const moe_problem &p, int groups, const int32_t *part_counts,
+                                    const double *part_psum, int32_t *counts, float *prob_sum,
+                                    const int32_t *idx, int32_t *offsets, int32_t *sorted_token,
+                                    int32_t *slot_of, float *f, float *P, float *f_dev, float *P_dev,
+                                    float *exp_bal, float *dev_bal, int32_t *ctl, int nctl, hipStream_t s);
 
 struct FfnArgs {
     const void *x;
@@ -133,7 +204,10 @@ hipError_t launch_expert_down(const moe_problem &p, const FfnArgs &a, hipStream_
 // this call only) and, in accumulating mode, zeroes y_acc and writes the
 // gates in grouped order.  p may have no active part (then only the
 // preparation runs).
-hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s);
+// prep = false: the control words are already clear (moe_layer_forward's decode tail cleared
+// them; gather mode only).
+hipError_t launch_expert_ffn(const moe_problem &p, const FfnArgs &a, int32_t *ctl, hipStream_t s,
+                             bool prep = true);
 // name of the kernel (template instantiation) launch_expert_ffn runs for p
 const char *expert_ffn_kernel_name(const moe_problem &p, bool accum);
 // backward: the up projection recomputed, with a = SiLU(p) q written to act_*

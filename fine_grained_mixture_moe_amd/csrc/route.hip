@@ -1240,9 +1240,11 @@ hipError_t route_scratch_ptr(void **ptr) {
     return hipSuccess;
 }
 
+bool route_decode_batch(const moe_problem &p) { return p.T > 0 && route_decode_path(p.T, p.d, p.n_routed); }
+
 hipError_t launch_route(const moe_problem &p, int skip, const void *x, const float *centroids, const float *bias,
                         int32_t *idx, float *gate, float *probs, int32_t *part_counts, double *part_psum,
-                        int32_t *counts, float *prob_sum, hipStream_t s) {
+                        int32_t *counts, float *prob_sum, hipStream_t s, bool reduce) {
     const int nblk = p.T > 0 ? route_blocks(p.T, p.d, p.n_routed) : 0;
     if (nblk > 0) {
         if (route_mfma_path(p.T, p.d, p.n_routed)) {
@@ -1267,6 +1269,7 @@ hipError_t launch_route(const moe_problem &p, int skip, const void *x, const flo
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (!reduce) return hipSuccess;
     route_reduce_kernel<<<p.n_routed, 256, 0, s>>>(nblk, p.n_routed, part_counts, part_psum, counts, prob_sum);
     return hipGetLastError();
 }

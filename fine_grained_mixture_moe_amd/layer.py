@@ -157,6 +157,21 @@ class DeviceLayer:
         if stats and self.prob.n_routed:
             self.balance_stats(stream)
 
+    def layer_io(self) -> dict:
+        """The buffers of this layer as the fields of moe_layer_io."""
+        return dict(x=self.x, centroids=self.centroids, bias=self.bias, w1_routed=self.w1_r, w3_routed=self.w3_r,
+                    w2_routed=self.w2_r, w1_shared=self.w1_s, w3_shared=self.w3_s, w2_shared=self.w2_s,
+                    idx=self.idx, gate=self.gate, probs=self.probs, counts=self.counts, prob_sum=self.prob_sum,
+                    offsets=self.offsets, sorted_token=self.sorted_token, slot_of=self.slot_of,
+                    y_routed=self.y_routed, y_shared=self.y_acc, h=self.h, f=self.f, P=self.P, f_dev=self.f_dev,
+                    P_dev=self.P_dev, exp_bal=self.exp_bal, dev_bal=self.dev_bal)
+
+    def layer_forward(self, stream=None):
+        """The whole layer pass as one moe_layer_forward call (gather mode; needs N' >= 1)."""
+        assert not self.accumulate, "moe_layer_forward runs the gather form of the expert FFN"
+        M.moe_layer_forward(self.prob, self.groups, self.layer_io(), self.ws, self.ws_bytes, stream)
+        self.ffn_called = True
+
     def forward_with_routing(self, idx: np.ndarray, gate: np.ndarray, stream=None):
         """Layer pass with an externally supplied routing (e.g. every expert at gate 1)."""
         torch = _torch()

@@ -40,6 +40,14 @@ class moe_problem(ctypes.Structure):
                 f"top_k={self.top_k}, inter={self.inter}, dtype={self.dtype})")
 
 
+class moe_layer_io(ctypes.Structure):
+    """The pointer struct of moe_layer_forward (include/moe.h), field by field."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "centroids", "bias", "w1_routed", "w3_routed", "w2_routed", "w1_shared", "w3_shared", "w2_shared",
+        "idx", "gate", "probs", "counts", "prob_sum", "offsets", "sorted_token", "slot_of",
+        "y_routed", "y_shared", "h", "f", "P", "f_dev", "P_dev", "exp_bal", "dev_bal")]
+
+
 _lib = None
 _vp = ctypes.c_void_p
 _sz = ctypes.c_size_t
@@ -71,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.moe_balance_stats.argtypes = [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_route_ablate.argtypes = [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_route_hash.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_layer_forward.argtypes = [_pp, ctypes.c_int32, ctypes.POINTER(moe_layer_io), _vp, _sz, _vp]
         L.moe_backward_workspace_size.argtypes = [_pp, ctypes.POINTER(_sz)]
         L.moe_combine_backward.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_expert_ffn_backward.argtypes = [_pp] + [_vp] * 20 + [_sz, _vp]
@@ -79,7 +88,7 @@ def lib() -> ctypes.CDLL:
                    "moe_expert_up",
                    "moe_expert_down", "moe_combine", "moe_balance_stats", "moe_backward_workspace_size",
                    "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward", "moe_route_ablate",
-                   "moe_route_hash"):
+                   "moe_route_hash", "moe_layer_forward"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -222,3 +231,10 @@ def moe_route_backward(p, groups, alpha1, alpha2, x, centroids, probs, idx, dgat
         ctypes.byref(p), int(groups), float(alpha1), float(alpha2), _ptr(x), _ptr(centroids), _ptr(probs),
         _ptr(idx), _ptr(dgate), _ptr(f), _ptr(f_dev), _ptr(dh), _ptr(dx_ffn), _ptr(dx), _ptr(dcentroids),
         _ptr(dbias), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_forward(p, groups, io: dict, ws, ws_bytes, stream=None):
+    """io: the moe_layer_io fields by name (tensors or None)."""
+    s = moe_layer_io(**{k: _ptr(v) for k, v in io.items()})
+    _check("moe_layer_forward", lib().moe_layer_forward(ctypes.byref(p), groups, ctypes.byref(s), _ptr(ws), ws_bytes,
+                                                        _stream(stream)))

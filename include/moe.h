@@ -318,6 +318,56 @@ int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *count
                       const float *prob_sum, float *f, float *P, float *f_dev,
                       float *P_dev, float *exp_bal, float *dev_bal, void *stream);
 
+/*
+ * moe_layer_forward -- one whole layer pass in one call: moe_route,
+ * moe_permute, moe_expert_ffn (gather mode), moe_combine and moe_balance_stats
+ * in that order on `stream`, over one workspace of moe_workspace_size(p).
+ * Source: the five calls above (the layer output of "[ACL 2024] DeepSeekMoE
+ * ..." section "Method details", with its balance terms).
+ *
+ * Every pointer of `io` has the meaning, layout, dtype and ownership it has in
+ * those calls (io->probs may be NULL, io->bias may be NULL; io->y_routed is
+ * required when routed pairs exist, io->y_shared when K_s > 0), and every
+ * output is bitwise the output of the five calls.  All arguments are checked
+ * before anything is enqueued: the first failing check of the five calls is
+ * returned and nothing runs.  Requires N' >= 1 and D = groups as in
+ * moe_balance_stats.
+ *
+ * Decode batches (at most 256 tokens whose routing takes the one-workgroup-
+ * per-token kernel, T K' > 0) run as four kernels instead of seven: routing,
+ * then one workgroup that sums the routing partials, computes the balance
+ * terms, groups the pairs and clears the expert FFN's control words, then the
+ * fused expert FFN and the combine.  Other batches run the five calls' own
+ * kernels.  moe_expert_ffn_status reports on the expert FFN of this call.
+ */
+typedef struct moe_layer_io {
+    /* inputs (moe_route, moe_expert_ffn) */
+    const void *x;
+    const float *centroids;
+    const float *bias;
+    const void *w1_routed, *w3_routed, *w2_routed;
+    const void *w1_shared, *w3_shared, *w2_shared;
+    /* outputs of moe_route */
+    int32_t *idx;
+    float *gate;
+    float *probs;
+    int32_t *counts;
+    float *prob_sum;
+    /* outputs of moe_permute */
+    int32_t *offsets;
+    int32_t *sorted_token;
+    int32_t *slot_of;
+    /* outputs of moe_expert_ffn (y_shared: its y_acc argument) and moe_combine */
+    void *y_routed;
+    float *y_shared;
+    void *h;
+    /* outputs of moe_balance_stats */
+    float *f, *P, *f_dev, *P_dev, *exp_bal, *dev_bal;
+} moe_layer_io;
+
+int moe_layer_forward(const moe_problem *p, int32_t groups, const moe_layer_io *io, void *ws, size_t ws_bytes,
+                      void *stream);
+
 
 /* ========================================================================
  * Backward pass.  Training is the pages' setting ("[ACL 2024] DeepSeekMoE

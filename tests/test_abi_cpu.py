@@ -186,3 +186,31 @@ def test_routing_variants_reject_bad_arguments_before_launch():
     with pytest.raises(M.MoEError) as e:                    # token ids missing
         M.moe_route_hash(h, None, FAKE, FAKE, FAKE, 0)
     assert e.value.status == M.MOE_ERR_INVALID_ARG
+
+
+def test_layer_forward_rejects_bad_arguments_before_launch():
+    """moe_layer_forward runs every check of the five calls before it enqueues anything."""
+    p = M.moe_problem.make(64, 128, 1, 8, 2, 64, "bf16")
+    ws = M.moe_workspace_size(p)
+    names = [n for n, _ in M.moe_layer_io._fields_]
+    full = {n: FAKE for n in names}
+    full["probs"] = None
+    full["bias"] = None
+
+    def status(io, groups=2, ws_bytes=ws, prob=p):
+        with pytest.raises(M.MoEError) as e:
+            M.moe_layer_forward(prob, groups, io, FAKE, ws_bytes, 0)
+        return e.value.status
+
+    with pytest.raises(M.MoEError) as e:   # no pointer struct
+        st = M.lib().moe_layer_forward(ctypes.byref(p), 2, None, FAKE, ws, 0)
+        if st != M.MOE_OK:
+            raise M.MoEError("moe_layer_forward", st)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    for missing in ("x", "centroids", "idx", "gate", "counts", "prob_sum", "offsets", "sorted_token", "slot_of",
+                    "y_routed", "y_shared", "h", "w1_routed", "w2_shared", "f", "dev_bal"):
+        assert status(dict(full, **{missing: None})) == M.MOE_ERR_INVALID_ARG, missing
+    assert status(full, groups=3) == M.MOE_ERR_INVALID_ARG          # D does not divide N'
+    assert status(full, ws_bytes=ws - 1) == M.MOE_ERR_WORKSPACE
+    assert status(dict(full, x=FAKE + 4)) == M.MOE_ERR_INVALID_ARG  # misaligned token rows
+    assert status(full, prob=M.moe_problem.make(64, 128, 1, 0, 0, 64, "bf16")) == M.MOE_ERR_INVALID_ARG   # N' = 0
