@@ -360,7 +360,7 @@ int moe_layer_forward(const moe_problem *p, int32_t groups, const moe_layer_io *
         hipError_t e = launch_route(*p, 0, io->x, io->centroids, io->bias, io->idx, io->gate, io->probs, pc, pp,
                                     io->counts, io->prob_sum, s, /*reduce=*/false);
         if (e == hipSuccess)
-            e = launch_layer_decode_tail(*p, groups, pc, pp, io->counts, io->prob_sum, io->idx, io->offsets,
+            e = launch_layer_decode_tail(*p, groups, pp, io->counts, io->prob_sum, io->idx, io->offsets,
                                          io->sorted_token, io->slot_of, io->f, io->P, io->f_dev, io->P_dev,
                                          io->exp_bal, io->dev_bal, ctl, ffn_ctl_ints(q), s);
         const FfnArgs a = ffn_args(io->x, io->offsets, io->sorted_token, io->w1_routed, io->w3_routed, io->w2_routed,

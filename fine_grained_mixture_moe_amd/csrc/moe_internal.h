@@ -167,11 +167,12 @@ hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *off
                           int32_t *sorted_token, int32_t *slot_of, int32_t *hist,
                           int32_t *base, hipStream_t s);
 // The decode tail of moe_layer_forward (T <= kPermuteTokens, decode routing, T K' > 0): one
-// workgroup sums the routing partials of the T decode workgroups into counts and prob_sum (the
-// order of route_reduce_kernel), runs the balance statistics on them, groups the pairs (the
-// single-block permute) and clears the nctl control words of the fused expert FFN.
-hipError_t launch_layer_decode_tail(const moe_problem &p, int groups, const int32_t *part_counts,
-                                    const double *part_psum, int32_t *counts, float *prob_sum,
+// workgroup groups the pairs (the single-block permute, whose histogram gives counts), sums the
+// affinity partials of the T decode workgroups into prob_sum (the order of
+// route_reduce_kernel), runs the balance statistics on them and clears the nctl control words
+// of the fused expert FFN.
+hipError_t launch_layer_decode_tail(const moe_problem &p, int groups, const double *part_psum,
+                                    int32_t *counts, float *prob_sum,
                                     const int32_t *idx, int32_t *offsets, int32_t *sorted_token,
                                     int32_t *slot_of, float *f, float *P, float *f_dev, float *P_dev,
                                     float *exp_bal, float *dev_bal, int32_t *ctl, int nctl, hipStream_t s);

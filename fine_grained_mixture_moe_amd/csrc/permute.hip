@@ -131,7 +131,10 @@ __device__ int block_exscan_experts(int *tot, int Nr, int *s_w) {
 // precedes it.
 enum { kFromBase = 0, kFromHist = 1, kSelf = 2 };
 // The scatter of block b of nblk (256 threads); the kernel below and the decode tail kernel
-// (layer_decode_tail_kernel) run it.
+// (layer_decode_tail_kernel) run it.  kSelf: the block's entries are read from memory once
+// and kept in LDS for the later passes when they fit (at most kSelfCache), and tot_out (LDS of
+// the caller, or null) receives each expert's count of pairs.
+constexpr int kSelfCache = 4096;
 template <int HM>
 __device__ __forceinline__ void perm_scatter_block(int T, int Nr, int K, int nblk, int b,
                                                    const int32_t *__restrict__ idx,
@@ -139,12 +142,14 @@ __device__ __forceinline__ void perm_scatter_block(int T, int Nr, int K, int nbl
                                                    const int32_t *__restrict__ base,
                                                    int32_t *__restrict__ offsets,
                                                    int32_t *__restrict__ sorted_token,
-                                                   int32_t *__restrict__ slot_of) {
+                                                   int32_t *__restrict__ slot_of, int *tot_out = nullptr) {
     __shared__ unsigned long long mask[4][kPermuteMaxExperts];
     __shared__ int s_first[kPermuteMaxExperts];
     __shared__ int s_tot[kPermuteMaxExperts];
     __shared__ int s_w[4];
+    __shared__ int s_idx[HM == kSelf ? kSelfCache : 1];
     for (int i = threadIdx.x; i < 4 * Nr; i += 256) mask[i / Nr][i % Nr] = 0ull;
+    const bool cached = HM == kSelf && min(kPermuteTokens, T) * K <= kSelfCache;
     if (HM == kSelf) {
         for (int r = threadIdx.x; r < Nr; r += 256) s_tot[r] = 0;
         __syncthreads();
@@ -154,10 +159,14 @@ __device__ __forceinline__ void perm_scatter_block(int T, int Nr, int K, int nbl
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? idx[e + u * 256] : -1;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < kUnroll; ++u) {
                 if ((unsigned)v[u] < (unsigned)Nr) atomicAdd(&s_tot[v[u]], 1);
+                if (cached && e + u * 256 < n) s_idx[e + u * 256] = v[u];
+            }
         }
         __syncthreads();
+        if (tot_out)
+            for (int r = threadIdx.x; r < Nr; r += 256) tot_out[r] = s_tot[r];
         const int all = block_exscan_experts(s_tot, Nr, s_w);
         for (int r = threadIdx.x; r < Nr; r += 256) {
             s_first[r] = s_tot[r];
@@ -200,10 +209,11 @@ __device__ __forceinline__ void perm_scatter_block(int T, int Nr, int K, int nbl
     const int t0 = b * kPermuteTokens;
     const int n = min(kPermuteTokens, T - t0) * K;
     const int32_t *run = idx + (size_t)t0 * K;
+    auto entry = [&](int i) { return cached ? s_idx[i] : run[i]; };
     for (int e = threadIdx.x; e < n; e += kUnroll * 256) {
         int v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? run[e + u * 256] : -1;
+        for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? entry(e + u * 256) : -1;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int tt = (e + u * 256) / K;
@@ -214,7 +224,7 @@ __device__ __forceinline__ void perm_scatter_block(int T, int Nr, int K, int nbl
     for (int e = threadIdx.x; e < n; e += kUnroll * 256) {
         int v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? run[e + u * 256] : -1;
+        for (int u = 0; u < kUnroll; ++u) v[u] = e + u * 256 < n ? entry(e + u * 256) : -1;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int f = e + u * 256;
@@ -253,45 +263,39 @@ __global__ void perm_empty_kernel(int Nr, int32_t *__restrict__ offsets) {
 
 // The decode tail of moe_layer_forward, one workgroup of 256 threads (T <= 256 decode
 // workgroups of routing partials, N' <= 256):
-//   * routing statistics: thread r sums expert r's partials as route_reduce_kernel's tree does
-//     (each group of 64 workgroup rows pairwise at distances 32, 16, ..., 1 -- the butterfly of
-//     its waves -- rows past T adding +0, then the four group sums in order), so counts and
-//     prob_sum are bitwise those of moe_route;
+//   * the single-block grouping (as moe_permute for T <= 256); its histogram of idx gives the
+//     expert counts, the integers moe_route sums from its count partials;
+//   * affinity sums: thread r sums expert r's partials as route_reduce_kernel's tree does (each
+//     group of 64 workgroup rows pairwise at distances 32, 16, ..., 1 -- the butterfly of its
+//     waves -- rows past T adding +0, then the four group sums in order), so prob_sum is bitwise
+//     that of moe_route;
 //   * the balance statistics on them (balance_stats_block, as moe_balance_stats);
-//   * the single-block grouping (as moe_permute for T <= 256);
 //   * the fused expert FFN's control words cleared (as its preparation kernel in gather mode).
 __global__ __launch_bounds__(256) void layer_decode_tail_kernel(
-    int T, int Nr, int K, int D, const int32_t *__restrict__ part_counts, const double *__restrict__ part_psum,
+    int T, int Nr, int K, int D, const double *__restrict__ part_psum,
     int32_t *__restrict__ counts, float *__restrict__ prob_sum, const int32_t *__restrict__ idx,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_token, int32_t *__restrict__ slot_of,
     float *__restrict__ f, float *__restrict__ P, float *__restrict__ f_dev, float *__restrict__ P_dev,
     float *__restrict__ exp_bal, float *__restrict__ dev_bal, int32_t *__restrict__ ctl, int nctl) {
     __shared__ int s_cnt[kRouteMaxExperts];
     __shared__ float s_ps[kRouteMaxExperts];
+    // the grouping first: its histogram of idx is each expert's count of selections, the same
+    // integers as the sum of the routing's count partials
+    perm_scatter_block<kSelf>(T, Nr, K, 1, 0, idx, nullptr, nullptr, offsets, sorted_token, slot_of, s_cnt);
     const int r = threadIdx.x;
     if (r < Nr) {
-        long long c = 0;
         double total = 0.0;
 #pragma nounroll
         for (int w = 0; w < 4; ++w) {
             double g = 0.0;   // a group with no rows sums to +0, as in route_reduce_kernel
             if (64 * w < T) {
-                // the group's 64 rows of both partials are loaded together (rows past T clamped
-                // and replaced by zero), then summed
+                // the group's 64 rows are loaded together (rows past T clamped and replaced by
+                // zero), then summed
                 double a[64];
-                int n[64];
 #pragma unroll
-                for (int i = 0; i < 64; ++i) {
-                    const size_t o = (size_t)min(64 * w + i, T - 1) * Nr + r;
-                    a[i] = part_psum[o];
-                    n[i] = part_counts[o];
-                }
+                for (int i = 0; i < 64; ++i) a[i] = part_psum[(size_t)min(64 * w + i, T - 1) * Nr + r];
 #pragma unroll
-                for (int i = 0; i < 64; ++i) {
-                    const bool in = 64 * w + i < T;
-                    a[i] = 0.0 + (in ? a[i] : 0.0);
-                    c += in ? n[i] : 0;   // integers: any order
-                }
+                for (int i = 0; i < 64; ++i) a[i] = 0.0 + (64 * w + i < T ? a[i] : 0.0);
 #pragma unroll
                 for (int o = 32; o >= 1; o >>= 1)
 #pragma unroll
@@ -301,26 +305,23 @@ __global__ __launch_bounds__(256) void layer_decode_tail_kernel(
             total = w == 0 ? g : total + g;   // ((g0 + g1) + g2) + g3
         }
         const float ps = (float)total;
-        counts[r] = (int32_t)c;
+        counts[r] = s_cnt[r];
         prob_sum[r] = ps;
-        s_cnt[r] = (int32_t)c;
         s_ps[r] = ps;
     }
     __syncthreads();
     balance_stats_block(T, Nr, K, D, s_cnt, s_ps, f, P, f_dev, P_dev, exp_bal, dev_bal);
-    perm_scatter_block<kSelf>(T, Nr, K, 1, 0, idx, nullptr, nullptr, offsets, sorted_token, slot_of);
     for (int i = threadIdx.x; i < nctl; i += 256) ctl[i] = 0;
 }
 
 }  // namespace
 
-hipError_t launch_layer_decode_tail(const moe_problem &p, int groups, const int32_t *part_counts,
-                                    const double *part_psum, int32_t *counts, float *prob_sum,
+hipError_t launch_layer_decode_tail(const moe_problem &p, int groups, const double *part_psum, int32_t *counts, float *prob_sum,
                                     const int32_t *idx, int32_t *offsets, int32_t *sorted_token,
                                     int32_t *slot_of, float *f, float *P, float *f_dev, float *P_dev,
                                     float *exp_bal, float *dev_bal, int32_t *ctl, int nctl, hipStream_t s) {
     if (p.T > kPermuteTokens || p.n_routed > kRouteMaxExperts) return hipErrorInvalidValue;
-    layer_decode_tail_kernel<<<1, 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, part_counts, part_psum, counts,
+    layer_decode_tail_kernel<<<1, 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, part_psum, counts,
                                                prob_sum, idx, offsets, sorted_token, slot_of, f, P, f_dev, P_dev,
                                                exp_bal, dev_bal, ctl, nctl);
     return hipGetLastError();
