@@ -3,7 +3,7 @@
 Its outputs must be bitwise those of moe_route -> moe_permute -> moe_expert_ffn ->
 moe_combine -> moe_balance_stats on the same inputs: on decode batches (one routing
 workgroup per token, at most 256 tokens) it runs its own single-workgroup tail kernel
-(routing sums, statistics, grouping, FFN control words), elsewhere the five calls' kernels.
+(grouping, routing sums, statistics, FFN control words), elsewhere the five calls' kernels.
 """
 import numpy as np
 import pytest
@@ -67,9 +67,25 @@ def test_decode_tail_equals_five_calls(case):
     same_as_five_calls(inp, "decode")
 
 
+PREFILL = [
+    (300, 128, 1, 16, 4, 64, "bf16", 48, None, 4),     # two grouping blocks
+    (3000, 256, 1, 64, 6, 128, "bf16", 49, 1.1, 4),    # 12 grouping blocks
+    (2500, 192, 1, 100, 5, 64, "f32", 52, None, 5),    # fp32 layer, 10 grouping blocks
+    (20000, 64, 0, 256, 8, 64, "bf16", 53, 1.1, 8),    # a histogram large enough for the grouping's scan kernel
+    (9000, 2048, 1, 64, 6, 64, "bf16", 54, None, 4),   # several routing workgroups per reduction thread
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[f"T{c[0]}_d{c[1]}_s{c[2]}_r{c[3]}_k{c[4]}_{c[6]}" for c in PREFILL])
+def test_prefill_batches_equal_five_calls(case):
+    """Batches of several grouping blocks (the five calls' kernels inside one call)."""
+    T, d, Ks, Nr, K, w, dtype, seed, zipf, groups = case
+    inp = W.make_random_case(T, d, Ks, Nr, K, w, dtype=dtype, seed=seed, zipf_s=zipf, groups=groups)
+    same_as_five_calls(inp, "prefill")
+
+
 @pytest.mark.parametrize("case", [
-    (300, 128, 1, 16, 4, 64, "bf16", 48, None, 4),   # beyond 256 tokens: the five calls' kernels
-    (3000, 256, 1, 64, 6, 128, "bf16", 49, 1.1, 4),  # several grouping blocks
+    (300, 128, 1, 64, 4, 64, "bf16", 48, None, 4),   # 64 experts over two grouping blocks
     (0, 128, 1, 16, 4, 64, "bf16", 50, None, 4),     # empty batch
 ])
 def test_other_batches_equal_five_calls(case):
@@ -93,7 +109,11 @@ def test_decode_tail_against_the_oracle():
     PT.check_outputs(g, inp, tokens, ref, "layer_forward")
 
 
-@pytest.mark.parametrize("name", ["c5a", "c5c"])
-def test_decode_configs_full_size(name):
-    """The two decode workloads at full size: moe_layer_forward bitwise equal to the five calls."""
-    same_as_five_calls(W.make_inputs(W.WORKLOADS[name]), name, passes=1)
+@pytest.mark.parametrize("name", ["c5a", "c5c", "c2b", "c5b"])
+def test_configs_full_size(name):
+    """Decode and prefill workloads at full size: moe_layer_forward bitwise equal to the five calls."""
+    if name == "c2b":
+        inp = W.make_c2_fine(independent_centroids=True, coarse=W.make_c2_coarse())
+    else:
+        inp = W.make_inputs(W.WORKLOADS[name])
+    same_as_five_calls(inp, name, passes=1)
