@@ -1132,16 +1132,22 @@ template <int NW, int S, bool XB>
 hipError_t launch_decode_form(const moe_problem &p, int skip, const void *x, const float *E, const float *bias,
                               int32_t *idx, float *gate, float *probs, int32_t *pc, double *pp, hipStream_t s) {
     const size_t lds = decode_lds_bytes(NW, S, p.d);
-    // dynamic LDS beyond 64 KB: raise the kernel's limit (set once per form; the largest d wins)
-    static size_t granted = 0;
+    // dynamic LDS beyond 64 KB: raise the kernel's limit, once per form and device (the largest d
+    // so far wins)
+    constexpr int kDevices = 64;
+    static size_t granted[kDevices] = {};
     static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
     {
         std::lock_guard<std::mutex> lock(mu);
-        if (lds > granted) {
-            const hipError_t e = hipFuncSetAttribute((const void *)route_decode_kernel<NW, S, XB>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (lds > granted[dev]) {
+            e = hipFuncSetAttribute((const void *)route_decode_kernel<NW, S, XB>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
-            granted = lds;
+            granted[dev] = lds;
         }
     }
     route_decode_kernel<NW, S, XB><<<p.T, NW * 64, lds, s>>>(p.T, p.d, p.n_routed, p.top_k, skip, x, E, bias, idx,
