@@ -14,8 +14,11 @@
 namespace moe {
 namespace {
 
+// The combine reads every row once: non-temporal loads (nt), which stream past the caches.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
-    const uint4 q = *(const uint4 *)p;
+    const u32x4_t q = __builtin_nontemporal_load((const u32x4_t *)p);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -24,7 +27,8 @@ __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
     }
 }
 __device__ __forceinline__ void load8(const float *p, float v[8]) {
-    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    const f32x4_t a = __builtin_nontemporal_load((const f32x4_t *)p);
+    const f32x4_t b = __builtin_nontemporal_load((const f32x4_t *)(p + 4));
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
