@@ -14,7 +14,8 @@
 namespace moe {
 namespace {
 
-// The combine reads every row once: non-temporal loads (nt), which stream past the caches.
+// The combine reads and writes every row once: non-temporal accesses (nt), which stream past
+// the caches.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
@@ -42,11 +43,16 @@ __device__ __forceinline__ void store8(uint16_t *p, const float v[8]) {
     q.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
     q.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
     q.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
-    *(uint4 *)p = q;
+    u32x4_t w;
+    w.x = q.x; w.y = q.y; w.z = q.z; w.w = q.w;
+    __builtin_nontemporal_store(w, (u32x4_t *)p);
 }
 __device__ __forceinline__ void store8(float *p, const float v[8]) {
-    *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
-    *(float4 *)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    f32x4_t a, b;
+    a.x = v[0]; a.y = v[1]; a.z = v[2]; a.w = v[3];
+    b.x = v[4]; b.y = v[5]; b.z = v[6]; b.w = v[7];
+    __builtin_nontemporal_store(a, (f32x4_t *)p);
+    __builtin_nontemporal_store(b, (f32x4_t *)(p + 4));
 }
 
 template <typename DT>
