@@ -244,7 +244,9 @@ def run(args) -> dict:
             getattr(dl, s)()
             marks[i][j + 1].record(stream)
     torch.cuda.synchronize()
-    breakdown = {s: round(sum(m[j].elapsed_time(m[j + 1]) for m in marks) / n_b, 4) for j, s in enumerate(stages)}
+    # median per stage: a late host enqueue of one pass shows up as idle time before its first kernel
+    breakdown = {s: round(sorted(m[j].elapsed_time(m[j + 1]) for m in marks)[n_b // 2], 4)
+                 for j, s in enumerate(stages)}
 
     # the same pass as one moe_layer_forward call (decode batches: four kernels instead of seven)
     lf = None
@@ -417,7 +419,7 @@ def run_backward(args) -> dict:
     for m in marks:
         calls(m)
     torch.cuda.synchronize()
-    stages = {k: round(sum(m[j].elapsed_time(m[j + 1]) for m in marks) / len(marks), 4)
+    stages = {k: round(sorted(m[j].elapsed_time(m[j + 1]) for m in marks)[len(marks) // 2], 4)
               for j, k in enumerate(["combine_backward", "expert_ffn_backward", "route_backward"])}
     pairs = wl.T * (wl.top_k + wl.n_shared)
     ffn_flops = 16.0 * wl.d * wl.inter * pairs
