@@ -9,6 +9,8 @@
 //
 // Balance terms, same page and section (expert-level and device-level balance
 // losses) with the symbols of "【论文总结】MoE" sections 2.3 and 2.4.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -118,6 +120,25 @@ __global__ __launch_bounds__(256) void balance_stats_kernel(int T, int Nr, int K
     balance_stats_block(T, Nr, K, D, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, dev_bal);
 }
 
+// Workgroup 0: balance_stats_block; workgroups 1.. clear ctl[0, nctl) (what the fused expert
+// FFN's preparation kernel does in gather mode), so the two share one kernel boundary.
+__global__ __launch_bounds__(256) void layer_stats_ctl_kernel(int T, int Nr, int K, int D,
+                                                              const int32_t *__restrict__ counts,
+                                                              const float *__restrict__ prob_sum,
+                                                              float *__restrict__ f, float *__restrict__ P,
+                                                              float *__restrict__ f_dev,
+                                                              float *__restrict__ P_dev,
+                                                              float *__restrict__ exp_bal,
+                                                              float *__restrict__ dev_bal, int32_t *ctl,
+                                                              int nctl) {
+    if (blockIdx.x == 0) {
+        balance_stats_block(T, Nr, K, D, counts, prob_sum, f, P, f_dev, P_dev, exp_bal, dev_bal);
+        return;
+    }
+    const int stride = (int)(gridDim.x - 1) * 256;
+    for (int i = (int)(blockIdx.x - 1) * 256 + (int)threadIdx.x; i < nctl; i += stride) ctl[i] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const moe_problem &p, const void *x, const void *y_routed,
@@ -143,6 +164,16 @@ hipError_t launch_balance_stats(const moe_problem &p, int groups, const int32_t 
                                 float *exp_bal, float *dev_bal, hipStream_t s) {
     balance_stats_kernel<<<1, 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, counts, prob_sum, f, P, f_dev,
                                            P_dev, exp_bal, dev_bal);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_stats_ctl(const moe_problem &p, int groups, const int32_t *counts,
+                                  const float *prob_sum, float *f, float *P, float *f_dev,
+                                  float *P_dev, float *exp_bal, float *dev_bal, int32_t *ctl, int nctl,
+                                  hipStream_t s) {
+    const int grid = 1 + std::min(std::max((nctl + 255) / 256, 1), 64);
+    layer_stats_ctl_kernel<<<grid, 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, counts, prob_sum, f, P,
+                                                f_dev, P_dev, exp_bal, dev_bal, ctl, nctl);
     return hipGetLastError();
 }
 

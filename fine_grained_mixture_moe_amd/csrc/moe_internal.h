@@ -224,6 +224,13 @@ hipError_t launch_combine(const moe_problem &p, const void *x, const void *y_rou
 hipError_t launch_balance_stats(const moe_problem &p, int groups, const int32_t *counts,
                                 const float *prob_sum, float *f, float *P, float *f_dev,
                                 float *P_dev, float *exp_bal, float *dev_bal, hipStream_t s);
+// The balance statistics and the clearing of the fused expert FFN's nctl control words in one
+// launch (moe_layer_forward beyond decode batches, gather mode): workgroup 0 runs
+// balance_stats_block, the others clear the words. Both only need the routing's counts.
+hipError_t launch_layer_stats_ctl(const moe_problem &p, int groups, const int32_t *counts,
+                                  const float *prob_sum, float *f, float *P, float *f_dev,
+                                  float *P_dev, float *exp_bal, float *dev_bal, int32_t *ctl, int nctl,
+                                  hipStream_t s);
 
 // ---- backward pass (backward.hip) ------------------------------------------
 
