@@ -370,18 +370,23 @@ int moe_layer_forward(const moe_problem *p, int32_t groups, const moe_layer_io *
             e = launch_combine(*p, io->x, io->y_routed, io->y_shared, io->gate, io->slot_of, io->h, s);
         return hip_status(e);
     }
-    // other batches: routing and grouping as moe_route and moe_permute, then one kernel for the
-    // statistics and the FFN's control words, the fused FFN without its preparation kernel, the
-    // combine (their checks have passed above)
-    if ((rc = moe_route(p, io->x, io->centroids, io->bias, io->idx, io->gate, io->probs, io->counts, io->prob_sum,
-                        ws, ws_bytes, stream)) != MOE_OK)
-        return rc;
-    if ((rc = moe_permute(p, io->idx, io->offsets, io->sorted_token, io->slot_of, ws, ws_bytes, stream)) != MOE_OK)
-        return rc;
+    // other batches: the routing; the grouping's histogram with the routing's reduction in one
+    // launch (more than kPermuteTokens tokens with routed pairs; else the two apart, as moe_route
+    // and moe_permute); the grouping; one kernel for the statistics and the FFN's control words;
+    // the fused FFN without its preparation kernel; the combine (their checks have passed above)
     hipStream_t s = (hipStream_t)stream;
+    int32_t *pc = (int32_t *)at(ws, L.route_counts);
+    double *pp = (double *)at(ws, L.route_psum);
+    const bool merge = p->n_routed > 0 && p->top_k > 0 && cdiv(p->T, kPermuteTokens) >= 2;
+    hipError_t e = launch_route(*p, 0, io->x, io->centroids, io->bias, io->idx, io->gate, io->probs, pc, pp,
+                                io->counts, io->prob_sum, s, /*reduce=*/!merge);
+    const RouteReduce rr{p->T > 0 ? route_blocks(p->T, p->d, p->n_routed) : 0, pc, pp, io->counts, io->prob_sum};
+    if (e == hipSuccess)
+        e = launch_permute(*p, io->idx, io->offsets, io->sorted_token, io->slot_of, (int32_t *)at(ws, L.perm_hist),
+                           (int32_t *)at(ws, L.perm_base), s, merge ? &rr : nullptr);
     int32_t *ctl = (int32_t *)at(ws, L.ffn_ctl);
     const moe_problem q = active_part(*p, routed, shared);
-    hipError_t e = launch_layer_stats_ctl(*p, groups, io->counts, io->prob_sum, io->f, io->P, io->f_dev, io->P_dev,
+    if (e == hipSuccess) e = launch_layer_stats_ctl(*p, groups, io->counts, io->prob_sum, io->f, io->P, io->f_dev, io->P_dev,
                                           io->exp_bal, io->dev_bal, ctl, ffn_ctl_ints(q), s);
     const FfnArgs a = ffn_args(io->x, io->offsets, io->sorted_token, io->w1_routed, io->w3_routed, io->w2_routed,
                                io->w1_shared, io->w3_shared, io->w2_shared, io->y_routed, io->y_shared, ws, L);

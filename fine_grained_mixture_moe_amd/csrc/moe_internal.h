@@ -91,6 +91,34 @@ __device__ __forceinline__ double stats_block_sum4(double v, double *s_w) {
     return ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
 }
 
+// One workgroup of 256 threads for expert r: counts[r] = sum_b part_counts[b, r] and
+// prob_sum[r] = sum_b part_psum[b, r] over the nblk routing workgroups, in fp64: strided
+// per-thread sums, a butterfly within each wave, then the 4 wave sums in order (fixed order).
+__device__ inline void route_reduce_block(int r, int nblk, int Nr, const int32_t *__restrict__ part_counts,
+                                          const double *__restrict__ part_psum, int32_t *__restrict__ counts,
+                                          float *__restrict__ prob_sum) {
+    __shared__ double s_p[4];
+    __shared__ long long s_c[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double a = 0.0;
+    long long c = 0;
+    for (int b = threadIdx.x; b < nblk; b += 256) {
+        a += part_psum[(size_t)b * Nr + r];
+        c += part_counts[(size_t)b * Nr + r];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a += __shfl_xor(a, o, 64);
+        c += __shfl_xor(c, o, 64);
+    }
+    if (lane == 0) { s_p[wave] = a; s_c[wave] = c; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        counts[r] = (int32_t)(s_c[0] + s_c[1] + s_c[2] + s_c[3]);
+        prob_sum[r] = (float)(((s_p[0] + s_p[1]) + s_p[2]) + s_p[3]);
+    }
+}
+
 __device__ inline void balance_stats_block(int T, int Nr, int K, int D, const int32_t *counts,
                                            const float *prob_sum, float *__restrict__ f,
                                            float *__restrict__ P, float *__restrict__ f_dev,
@@ -163,9 +191,20 @@ inline size_t route_partial_bytes(const moe_problem &p) {
 hipError_t launch_route_hash(const moe_problem &p, const int32_t *token_ids, int32_t *idx, float *gate,
                              int32_t *counts, hipStream_t s);
 
+// The routing's reduction over its nblk workgroups' partials (route_reduce_block), when
+// launch_permute runs it beside its histogram (moe_layer_forward).
+struct RouteReduce {
+    int nblk;
+    const int32_t *part_counts;
+    const double *part_psum;
+    int32_t *counts;
+    float *prob_sum;
+};
+// rr: also run the routing's reduction, in the histogram's launch; only with more than
+// kPermuteTokens tokens and routed pairs (else hipErrorInvalidValue, nothing launched).
 hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *offsets,
                           int32_t *sorted_token, int32_t *slot_of, int32_t *hist,
-                          int32_t *base, hipStream_t s);
+                          int32_t *base, hipStream_t s, const RouteReduce *rr = nullptr);
 // The decode tail of moe_layer_forward (T <= kPermuteTokens, decode routing, T K' > 0): one
 // workgroup groups the pairs (the single-block permute, whose histogram gives counts), sums the
 // affinity partials of the T decode workgroups into prob_sum (the order of

@@ -32,13 +32,13 @@ namespace {
 // independent loads in flight per thread).
 constexpr int kUnroll = 4;
 
-__global__ __launch_bounds__(256) void perm_hist_kernel(int T, int Nr, int K,
-                                                        const int32_t *__restrict__ idx,
-                                                        int32_t *__restrict__ hist) {
+// Workgroup b of nblk: the expert histogram of tokens [256 b, 256 b + 256) into hist[r, b].
+__device__ inline void perm_hist_block(int T, int Nr, int K, const int32_t *__restrict__ idx,
+                                       int32_t *__restrict__ hist, int b, int nblk) {
     __shared__ int cnt[kPermuteMaxExperts];
     for (int r = threadIdx.x; r < Nr; r += 256) cnt[r] = 0;
     __syncthreads();
-    const int t0 = blockIdx.x * kPermuteTokens;
+    const int t0 = b * kPermuteTokens;
     const int n = min(kPermuteTokens, T - t0) * K;
     const int32_t *run = idx + (size_t)t0 * K;
     for (int e = threadIdx.x; e < n; e += kUnroll * 256) {
@@ -50,7 +50,28 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(int T, int Nr, int K,
             if ((unsigned)v[u] < (unsigned)Nr) atomicAdd(&cnt[v[u]], 1);
     }
     __syncthreads();
-    for (int r = threadIdx.x; r < Nr; r += 256) hist[(size_t)r * gridDim.x + blockIdx.x] = cnt[r];
+    for (int r = threadIdx.x; r < Nr; r += 256) hist[(size_t)r * nblk + b] = cnt[r];
+}
+
+__global__ __launch_bounds__(256) void perm_hist_kernel(int T, int Nr, int K,
+                                                        const int32_t *__restrict__ idx,
+                                                        int32_t *__restrict__ hist) {
+    perm_hist_block(T, Nr, K, idx, hist, blockIdx.x, gridDim.x);
+}
+
+// Workgroups 0 .. nblk-1: perm_hist_block; workgroups nblk .. nblk+Nr-1: the routing's reduction
+// for expert blockIdx.x - nblk (route_reduce_block over rblk partials). Both read only what the
+// routing wrote, so they share one launch (moe_layer_forward).
+__global__ __launch_bounds__(256) void perm_hist_reduce_kernel(int T, int Nr, int K, const int32_t *__restrict__ idx,
+                                                               int32_t *__restrict__ hist, int nblk, int rblk,
+                                                               const int32_t *__restrict__ part_counts,
+                                                               const double *__restrict__ part_psum,
+                                                               int32_t *__restrict__ counts,
+                                                               float *__restrict__ prob_sum) {
+    if ((int)blockIdx.x < nblk)
+        perm_hist_block(T, Nr, K, idx, hist, blockIdx.x, nblk);
+    else
+        route_reduce_block((int)blockIdx.x - nblk, rblk, Nr, part_counts, part_psum, counts, prob_sum);
 }
 
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int nblk, int Nr,
@@ -329,8 +350,9 @@ hipError_t launch_layer_decode_tail(const moe_problem &p, int groups, const doub
 
 hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *offsets,
                           int32_t *sorted_token, int32_t *slot_of, int32_t *hist, int32_t *base,
-                          hipStream_t s) {
+                          hipStream_t s, const RouteReduce *rr) {
     const int nblk = cdiv(p.T, kPermuteTokens);
+    if (rr && (nblk < 2 || p.top_k == 0 || p.n_routed == 0)) return hipErrorInvalidValue;
     if (nblk == 0 || p.top_k == 0 || p.n_routed == 0) {
         perm_empty_kernel<<<1, 256, 0, s>>>(p.n_routed, offsets);
         return hipGetLastError();
@@ -340,7 +362,12 @@ hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *off
                                                      sorted_token, slot_of);
         return hipGetLastError();
     }
-    perm_hist_kernel<<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist);
+    if (rr)
+        perm_hist_reduce_kernel<<<nblk + p.n_routed, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist, nblk,
+                                                                  rr->nblk, rr->part_counts, rr->part_psum,
+                                                                  rr->counts, rr->prob_sum);
+    else
+        perm_hist_kernel<<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist);
     if ((int64_t)nblk * p.n_routed <= kFusedScanMax) {
         perm_scatter_kernel<kFromHist><<<nblk, 256, 0, s>>>(p.T, p.n_routed, p.top_k, idx, hist, nullptr, offsets,
                                                             sorted_token, slot_of);

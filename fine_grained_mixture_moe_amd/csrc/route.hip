@@ -880,32 +880,11 @@ __global__ __launch_bounds__(NW * 64) void route_decode_kernel(int T, int d, int
     }
 }
 
-// One workgroup per expert: counts[r] = sum_b part_counts[b, r],
-// prob_sum[r] = sum_b part_psum[b, r] in fp64: strided per-thread sums, a
-// butterfly within each wave, then the 4 wave sums in order (fixed order).
+// One workgroup per expert (route_reduce_block, moe_internal.h).
 __global__ __launch_bounds__(256) void route_reduce_kernel(
     int nblk, int Nr, const int32_t *__restrict__ part_counts, const double *__restrict__ part_psum,
     int32_t *__restrict__ counts, float *__restrict__ prob_sum) {
-    __shared__ double s_p[4];
-    __shared__ long long s_c[4];
-    const int r = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    double a = 0.0;
-    long long c = 0;
-    for (int b = threadIdx.x; b < nblk; b += 256) {
-        a += part_psum[(size_t)b * Nr + r];
-        c += part_counts[(size_t)b * Nr + r];
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        a += __shfl_xor(a, o, 64);
-        c += __shfl_xor(c, o, 64);
-    }
-    if (lane == 0) { s_p[wave] = a; s_c[wave] = c; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        counts[r] = (int32_t)(s_c[0] + s_c[1] + s_c[2] + s_c[3]);
-        prob_sum[r] = (float)(((s_p[0] + s_p[1]) + s_p[2]) + s_p[3]);
-    }
+    route_reduce_block(blockIdx.x, nblk, Nr, part_counts, part_psum, counts, prob_sum);
 }
 
 // ---------------------------------------------------------------------------

@@ -337,11 +337,12 @@ int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *count
  * per-token kernel, T K' > 0) run as four kernels instead of seven: routing,
  * then one workgroup that groups the pairs, sums the routing partials,
  * computes the balance terms and clears the expert FFN's control words, then
- * the fused expert FFN and the combine.  Other batches run the kernels of
- * moe_route and moe_permute, then one kernel that computes the balance terms
- * and clears the expert FFN's control words (one kernel fewer than the five
- * calls), the expert FFN and the combine.  moe_expert_ffn_status reports on
- * the expert FFN of this call.
+ * the fused expert FFN and the combine.  Other batches run as six kernels
+ * instead of eight: routing; the grouping's histogram with the routing's
+ * reduction in one launch (more than 256 tokens; else the two apart); the
+ * grouping's scatter; one kernel that computes the balance terms and clears
+ * the expert FFN's control words; the expert FFN and the combine.
+ * moe_expert_ffn_status reports on the expert FFN of this call.
  */
 typedef struct moe_layer_io {
     /* inputs (moe_route, moe_expert_ffn) */
