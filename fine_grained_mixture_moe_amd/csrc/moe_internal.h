@@ -205,11 +205,11 @@ struct RouteReduce {
 hipError_t launch_permute(const moe_problem &p, const int32_t *idx, int32_t *offsets,
                           int32_t *sorted_token, int32_t *slot_of, int32_t *hist,
                           int32_t *base, hipStream_t s, const RouteReduce *rr = nullptr);
-// The decode tail of moe_layer_forward (T <= kPermuteTokens, decode routing, T K' > 0): one
-// workgroup groups the pairs (the single-block permute, whose histogram gives counts), sums the
-// affinity partials of the T decode workgroups into prob_sum (the order of
-// route_reduce_kernel), runs the balance statistics on them and clears the nctl control words
-// of the fused expert FFN.
+// The decode tail of moe_layer_forward (T <= kPermuteTokens, decode routing, T K' > 0): two
+// independent workgroups. One groups the pairs (the single-block permute) and clears the nctl
+// control words of the fused expert FFN; the other counts each expert's selections in idx, sums
+// the affinity partials of the T decode workgroups into prob_sum (the order of
+// route_reduce_kernel) and runs the balance statistics on them.
 hipError_t launch_layer_decode_tail(const moe_problem &p, int groups, const double *part_psum,
                                     int32_t *counts, float *prob_sum,
                                     const int32_t *idx, int32_t *offsets, int32_t *sorted_token,

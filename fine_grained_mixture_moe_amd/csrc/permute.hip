@@ -282,16 +282,19 @@ __global__ void perm_empty_kernel(int Nr, int32_t *__restrict__ offsets) {
     for (int r = threadIdx.x; r <= Nr; r += blockDim.x) offsets[r] = 0;
 }
 
-// The decode tail of moe_layer_forward, one workgroup of 256 threads (T <= 256 decode
-// workgroups of routing partials, N' <= 256):
-//   * the single-block grouping (as moe_permute for T <= 256); its histogram of idx gives the
-//     expert counts, the integers moe_route sums from its count partials;
+// The decode tail of moe_layer_forward, two independent workgroups of 256 threads (T <= 256
+// decode workgroups of routing partials, N' <= 256). Workgroup 0 does what the expert FFN after
+// it needs:
+//   * the single-block grouping (as moe_permute for T <= 256);
+//   * the fused expert FFN's control words cleared (as its preparation kernel in gather mode).
+// Workgroup 1, beside it:
+//   * the expert counts as a histogram of idx, the integers moe_route sums from its count
+//     partials;
 //   * affinity sums: thread r sums expert r's partials as route_reduce_kernel's tree does (each
 //     group of 64 workgroup rows pairwise at distances 32, 16, ..., 1 -- the butterfly of its
 //     waves -- rows past T adding +0, then the four group sums in order), so prob_sum is bitwise
 //     that of moe_route;
-//   * the balance statistics on them (balance_stats_block, as moe_balance_stats);
-//   * the fused expert FFN's control words cleared (as its preparation kernel in gather mode).
+//   * the balance statistics on them (balance_stats_block, as moe_balance_stats).
 __global__ __launch_bounds__(256) void layer_decode_tail_kernel(
     int T, int Nr, int K, int D, const double *__restrict__ part_psum,
     int32_t *__restrict__ counts, float *__restrict__ prob_sum, const int32_t *__restrict__ idx,
@@ -300,9 +303,20 @@ __global__ __launch_bounds__(256) void layer_decode_tail_kernel(
     float *__restrict__ exp_bal, float *__restrict__ dev_bal, int32_t *__restrict__ ctl, int nctl) {
     __shared__ int s_cnt[kRouteMaxExperts];
     __shared__ float s_ps[kRouteMaxExperts];
-    // the grouping first: its histogram of idx is each expert's count of selections, the same
-    // integers as the sum of the routing's count partials
-    perm_scatter_block<kSelf>(T, Nr, K, 1, 0, idx, nullptr, nullptr, offsets, sorted_token, slot_of, s_cnt);
+    if (blockIdx.x == 0) {
+        perm_scatter_block<kSelf>(T, Nr, K, 1, 0, idx, nullptr, nullptr, offsets, sorted_token, slot_of);
+        for (int i = threadIdx.x; i < nctl; i += 256) ctl[i] = 0;
+        return;
+    }
+    // each expert's count of selections: the same integers as the sum of the routing's count
+    // partials
+    for (int e = threadIdx.x; e < Nr; e += 256) s_cnt[e] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < T * K; e += 256) {
+        const int v = idx[e];
+        if ((unsigned)v < (unsigned)Nr) atomicAdd(&s_cnt[v], 1);
+    }
+    __syncthreads();
     const int r = threadIdx.x;
     if (r < Nr) {
         double total = 0.0;
@@ -332,7 +346,6 @@ __global__ __launch_bounds__(256) void layer_decode_tail_kernel(
     }
     __syncthreads();
     balance_stats_block(T, Nr, K, D, s_cnt, s_ps, f, P, f_dev, P_dev, exp_bal, dev_bal);
-    for (int i = threadIdx.x; i < nctl; i += 256) ctl[i] = 0;
 }
 
 }  // namespace
@@ -342,7 +355,7 @@ hipError_t launch_layer_decode_tail(const moe_problem &p, int groups, const doub
                                     int32_t *slot_of, float *f, float *P, float *f_dev, float *P_dev,
                                     float *exp_bal, float *dev_bal, int32_t *ctl, int nctl, hipStream_t s) {
     if (p.T > kPermuteTokens || p.n_routed > kRouteMaxExperts) return hipErrorInvalidValue;
-    layer_decode_tail_kernel<<<1, 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, part_psum, counts,
+    layer_decode_tail_kernel<<<2, 256, 0, s>>>(p.T, p.n_routed, p.top_k, groups, part_psum, counts,
                                                prob_sum, idx, offsets, sorted_token, slot_of, f, P, f_dev, P_dev,
                                                exp_bal, dev_bal, ctl, nctl);
     return hipGetLastError();

@@ -335,8 +335,9 @@ int moe_balance_stats(const moe_problem *p, int32_t groups, const int32_t *count
  *
  * Decode batches (at most 256 tokens whose routing takes the one-workgroup-
  * per-token kernel, T K' > 0) run as four kernels instead of seven: routing,
- * then one workgroup that groups the pairs, sums the routing partials,
- * computes the balance terms and clears the expert FFN's control words, then
+ * then one kernel whose two workgroups group the pairs and clear the expert
+ * FFN's control words, and sum the routing partials and compute the balance
+ * terms, then
  * the fused expert FFN and the combine.  Other batches run as six kernels
  * instead of eight: routing; the grouping's histogram with the routing's
  * reduction in one launch (more than 256 tokens; else the two apart); the
